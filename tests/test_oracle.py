@@ -1,0 +1,214 @@
+"""Pins for the oracle's routing, permutation and expert math (CPU)."""
+import itertools
+import math
+
+import numpy as np
+import pytest
+
+from oracle import codecs, formats, moe
+from weight_quantized_moe_amd import synth
+
+
+# ---------------------------------------------------------------- silu
+
+def test_silu_closed_forms():
+    z = np.array([0.0, 1.0, -1.0, 40.0, -40.0, 2.0])
+    s = moe.silu(z)
+    assert s[0] == 0.0
+    assert math.isclose(s[1], 1.0 / (1.0 + math.exp(-1.0)), rel_tol=1e-15)
+    assert math.isclose(s[2], -math.exp(-1.0) / (1.0 + math.exp(-1.0)), rel_tol=1e-15)
+    assert math.isclose(s[3], 40.0, rel_tol=1e-15)
+    assert abs(s[4]) < 1e-15
+    # silu(z) - silu(-z) = z
+    zz = np.linspace(-8, 8, 101)
+    assert np.allclose(moe.silu(zz) - moe.silu(-zz), zz, atol=1e-14)
+
+
+# ---------------------------------------------------------------- routing
+
+def test_route_brute_force_small_e():
+    """For E <= 6 the top-k set is the k-subset with the largest logit sum."""
+    rng = np.random.default_rng(3)
+    for e in range(1, 7):
+        for k in range(1, e + 1):
+            logits = rng.standard_normal((5, e)).astype(np.float32)
+            ids, w = moe.route(logits, k)
+            for t in range(5):
+                best = max(itertools.combinations(range(e), k),
+                           key=lambda s: sum(float(logits[t, j]) for j in s))
+                assert set(ids[t]) == set(best)
+                # descending logit order inside the k
+                sel = logits[t, ids[t]]
+                assert np.all(np.diff(sel) <= 0)
+                # softmax restricted to the chosen set
+                ex = np.array([math.exp(float(logits[t, j])) for j in ids[t]])
+                assert np.allclose(w[t], ex / ex.sum(), rtol=1e-12)
+
+
+def test_route_full_softmax_then_renormalize():
+    """Weights equal a full softmax over E followed by top-k renormalization."""
+    rng = np.random.default_rng(4)
+    logits = rng.standard_normal((16, 32)).astype(np.float32)
+    ids, w = moe.route(logits, 6)
+    p = np.exp(logits.astype(np.float64))
+    p /= p.sum(axis=1, keepdims=True)
+    sel = np.take_along_axis(p, ids.astype(np.int64), 1)
+    assert np.allclose(w, sel / sel.sum(axis=1, keepdims=True), rtol=1e-12)
+
+
+def test_route_ties_prefer_lower_id():
+    logits = np.zeros((3, 8), np.float32)
+    logits[1, [2, 5, 6]] = 1.0
+    logits[2] = [0.5, 1.0, 0.5, 1.0, 0.5, 0.25, 1.0, 0.5]
+    ids, w = moe.route(logits, 4)
+    assert list(ids[0]) == [0, 1, 2, 3]
+    assert list(ids[1]) == [2, 5, 6, 0]
+    assert list(ids[2]) == [1, 3, 6, 0]
+    assert np.allclose(w[0], 0.25)
+
+
+def test_route_invariants_bf16_logits():
+    rng = np.random.default_rng(5)
+    bits = synth.to_bf16_bits(rng.standard_normal((200, 128)).astype(np.float32))
+    logits = moe.bf16_bits_to_f64(bits)              # plenty of exact ties
+    ids, w = moe.route(logits, 8)
+    for t in range(200):
+        assert len(set(ids[t])) == 8
+        thr = logits[t, ids[t, -1]]
+        above = np.nonzero(logits[t] > thr)[0]
+        assert set(above) <= set(ids[t])
+        at = np.nonzero(logits[t] == thr)[0]
+        chosen_at = [j for j in ids[t] if logits[t, j] == thr]
+        assert chosen_at == sorted(at)[:len(chosen_at)]
+    assert np.allclose(w.sum(axis=1), 1.0, atol=1e-12)
+    assert np.all(w > 0)
+
+
+# ---------------------------------------------------------------- permutation
+
+def test_permute_brute_force_and_invariants():
+    rng = np.random.default_rng(6)
+    for (t, e, k) in [(1, 8, 2), (17, 8, 3), (64, 128, 8), (300, 16, 4)]:
+        logits = rng.standard_normal((t, e))
+        ids, _ = moe.route(logits, k)
+        p = moe.permute(ids, e)
+        # brute force: sort (expert, token) pairs
+        pairs = sorted((int(ids[tt, j]), tt, j) for tt in range(t) for j in range(k))
+        assert [x[1] for x in pairs] == list(p.sorted_token_ids)
+        assert [x[1] * k + x[2] for x in pairs] == list(p.sorted_slots)
+        assert p.offsets[0] == 0 and p.offsets[-1] == t * k
+        assert np.all(np.diff(p.offsets) == p.counts)
+        assert np.array_equal(np.sort(p.inv_pos), np.arange(t * k))
+        assert np.array_equal(p.sorted_slots[p.inv_pos], np.arange(t * k))
+        for ee in range(e):
+            toks = p.sorted_token_ids[p.offsets[ee]:p.offsets[ee + 1]]
+            assert np.all(np.diff(toks) > 0)
+
+
+# ---------------------------------------------------------------- expert math
+
+def _exact_weights(fmt, n, k, rng):
+    """Weights exactly representable in ``fmt`` (quantization is lossless)."""
+    if fmt == formats.INT4:
+        q = rng.integers(-7, 8, size=(n, k)).astype(np.float64)
+        q[:, ::128] = 7
+        s = 2.0 ** rng.integers(-7, -3, size=(n, k // 128))
+        return q * np.repeat(s, 128, axis=1)
+    if fmt == formats.FP8:
+        t = codecs.e4m3_decode_table()
+        vals = t[np.isfinite(t)]
+        c = vals[rng.integers(0, len(vals), size=(n, k))]
+        c.reshape(n // 128, 128, k // 128, 128)[:, 0, :, 0] = 448.0
+        s = 2.0 ** rng.integers(-14, -10, size=(n // 128, k // 128))
+        return (c.reshape(n // 128, 128, k // 128, 128) * s[:, None, :, None]).reshape(n, k)
+    # NVFP4: e2m1 codes times a block scale whose code is reproduced by the
+    # quantizer; g = 448*6/amax must make g*amax_b/6 an E4M3 value, so use one
+    # block maximum of 6 everywhere and a global max of 6 * 2**j.
+    e2 = codecs.e2m1_decode_table()
+    c = e2[rng.integers(0, 16, size=(n, k))]
+    c.reshape(n, k // 16, 16)[:, :, 0] = 6.0
+    return c * 2.0 ** -6
+
+
+@pytest.mark.parametrize("fmt", formats.FORMATS)
+def test_dense_equivalence_single_expert(fmt):
+    """E = 1, k = 1: the layer is a dense SwiGLU MLP (textbook form)."""
+    rng = np.random.default_rng(7)
+    h, i, t = 256, 128, 5
+    wg = _exact_weights(fmt, i, h, rng) if fmt != formats.FP8 else None
+    if fmt == formats.FP8:
+        w13_full = _exact_weights(fmt, 2 * i, h, rng)
+        wg, wu = w13_full[:i], w13_full[i:]
+    else:
+        wu = _exact_weights(fmt, i, h, rng)
+    wd = _exact_weights(fmt, h, i, rng)
+    w13 = formats.quantize_stack(fmt, [np.concatenate([wg, wu], axis=0)])
+    w2 = formats.quantize_stack(fmt, [wd])
+    assert np.array_equal(formats.dequantize_expert(w13, 0), np.concatenate([wg, wu]))
+    assert np.array_equal(formats.dequantize_expert(w2, 0), wd)
+    x_bits = synth.to_bf16_bits(rng.standard_normal((t, h)).astype(np.float32))
+    x = moe.bf16_bits_to_f64(x_bits)
+    logits = rng.standard_normal((t, 1)).astype(np.float32)
+    y, ids, w = moe.moe_forward(moe.Layer(w13, w2, 1), logits, x_bits)
+    assert np.all(ids == 0) and np.all(w == 1.0)
+    ref = np.empty((t, h))
+    for r in range(t):
+        g = np.array([sum(wg[a, b] * x[r, b] for b in range(h)) for a in range(i)])
+        u = np.array([sum(wu[a, b] * x[r, b] for b in range(h)) for a in range(i)])
+        act = g / (1.0 + np.exp(-g)) * u
+        ref[r] = [sum(wd[c, a] * act[a] for a in range(i)) for c in range(h)]
+    assert np.allclose(y, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_all_experts_selected_is_full_softmax_mixture():
+    """k = E: y = sum_e softmax(l)_e * MLP_e(x), with no permutation involved."""
+    rng = np.random.default_rng(8)
+    e, h, i, t = 4, 256, 128, 6
+    ws13 = [synth.expert_weight(7, 0, "w13", j, 2 * i, h) for j in range(e)]
+    ws2 = [synth.expert_weight(7, 0, "w2", j, h, i) for j in range(e)]
+    w13 = formats.quantize_stack(formats.INT4, ws13)
+    w2 = formats.quantize_stack(formats.INT4, ws2)
+    x_bits = synth.hidden_bf16(7, 0, t, h)
+    logits = synth.router_logits(7, 0, t, e)
+    y, _, _ = moe.moe_forward(moe.Layer(w13, w2, e), logits, x_bits)
+    x = moe.bf16_bits_to_f64(x_bits)
+    ref = np.zeros((t, h))
+    for r in range(t):
+        p = np.exp(logits[r].astype(np.float64))
+        p /= p.sum()
+        for j in range(e):
+            d13 = formats.dequantize_expert(w13, j)
+            d2 = formats.dequantize_expert(w2, j)
+            g = d13[:i] @ x[r]
+            u = d13[i:] @ x[r]
+            ref[r] += p[j] * (d2 @ (g / (1 + np.exp(-g)) * u))
+    assert np.allclose(y, ref, rtol=1e-11, atol=1e-13)
+
+
+def test_token_subset_matches_full_evaluation():
+    rng = np.random.default_rng(9)
+    e, h, i, t = 8, 256, 128, 32
+    w13 = formats.quantize_stack(formats.NVFP4, [synth.expert_weight(1, 0, "w13", j, 2 * i, h) for j in range(e)])
+    w2 = formats.quantize_stack(formats.NVFP4, [synth.expert_weight(1, 0, "w2", j, h, i) for j in range(e)])
+    layer = moe.Layer(w13, w2, 2)
+    x = synth.hidden_bf16(1, 0, t, h)
+    lg = synth.router_logits(1, 0, t, e)
+    res = synth.residual_bf16(1, 0, t, h)
+    y_full, _, _ = moe.moe_forward(layer, lg, x, res)
+    sub = np.array([0, 5, 31, 17])
+    y_sub, _, _ = moe.moe_forward(layer, lg, x, res, tokens=sub)
+    assert np.allclose(y_full[sub], y_sub, rtol=1e-13, atol=1e-15)
+    y_nores, _, _ = moe.moe_forward(layer, lg, x)
+    assert np.allclose(y_full - y_nores, moe.bf16_bits_to_f64(res), atol=1e-12)
+
+
+def test_workload_logit_skew():
+    """The skewed routing recipes produce the imbalance they are meant to."""
+    lg = synth.router_logits(4, 0, 4096, 128, "zipf")
+    ids, _ = moe.route(lg[:512], 8)
+    counts = np.bincount(ids.ravel(), minlength=128)
+    assert counts.max() > 8 * counts.mean()
+    lg = synth.router_logits(3, 0, 512, 128, "bias")
+    ids, _ = moe.route(lg, 8)
+    counts = np.bincount(ids.ravel(), minlength=128)
+    assert counts.max() > 2 * counts.mean()

@@ -1,0 +1,215 @@
+"""ctypes binding of libmoe_quant.so (argument marshalling only).
+
+Every step of the layer runs in the HIP library; PyTorch supplies device
+memory (tensors' ``data_ptr()``) and the current HIP stream.  If the library is
+missing, constructing a :class:`Layer` raises: there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+ABI_VERSION = 1
+FORMATS = {"int4_g128": 1, "fp8_b128": 2, "nvfp4_g16": 3}
+MQ_F32, MQ_BF16 = 0, 1
+STAGES = ("route", "permute", "gate_up", "down", "combine")
+
+EXPORTED = (
+    "moe_quant_init",
+    "moe_quant_workspace_size",
+    "moe_quant_forward",
+    "moe_quant_check",
+    "moe_quant_dequantize",
+    "moe_quant_destroy",
+    "moe_quant_status_string",
+    "moe_quant_last_error",
+    "moe_quant_abi_version",
+)
+
+
+class MoeQuantError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"moe_quant status {status}: {message}")
+        self.status = status
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [
+        ("abi_version", ctypes.c_uint32),
+        ("num_experts", ctypes.c_int32),
+        ("hidden", ctypes.c_int32),
+        ("intermediate", ctypes.c_int32),
+        ("top_k", ctypes.c_int32),
+        ("format", ctypes.c_int32),
+        ("w13", ctypes.c_void_p),
+        ("w13_scale", ctypes.c_void_p),
+        ("w13_gscale", ctypes.c_void_p),
+        ("w2", ctypes.c_void_p),
+        ("w2_scale", ctypes.c_void_p),
+        ("w2_gscale", ctypes.c_void_p),
+    ]
+
+
+class Probe(ctypes.Structure):
+    _fields_ = [
+        ("topk_ids", ctypes.c_void_p),
+        ("topk_w", ctypes.c_void_p),
+        ("expert_offsets", ctypes.c_void_p),
+        ("sorted_token_ids", ctypes.c_void_p),
+        ("inv_pos", ctypes.c_void_p),
+        ("h", ctypes.c_void_p),
+        ("events", ctypes.c_void_p * (2 * len(STAGES))),
+    ]
+
+
+def library_path() -> str:
+    return os.environ.get("MOE_QUANT_LIB", os.path.join(HERE, "libmoe_quant.so"))
+
+
+_LIB = None
+
+
+def load_library():
+    """Load libmoe_quant.so and declare its signatures (raises if missing)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise MoeQuantError(-1, f"{path} is not built; run weight_quantized_moe_amd.build.build()")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.moe_quant_init.argtypes = [ctypes.POINTER(LayerDesc), ctypes.POINTER(vp)]
+    lib.moe_quant_init.restype = i32
+    lib.moe_quant_workspace_size.argtypes = [vp, i64, ctypes.POINTER(sz)]
+    lib.moe_quant_workspace_size.restype = i32
+    lib.moe_quant_forward.argtypes = [vp, vp, i32, vp, vp, i64, vp, vp, sz,
+                                      ctypes.POINTER(Probe), vp]
+    lib.moe_quant_forward.restype = i32
+    lib.moe_quant_check.argtypes = [vp, vp, vp]
+    lib.moe_quant_check.restype = i32
+    lib.moe_quant_dequantize.argtypes = [vp, i32, i32, vp, vp]
+    lib.moe_quant_dequantize.restype = i32
+    lib.moe_quant_destroy.argtypes = [vp]
+    lib.moe_quant_destroy.restype = None
+    lib.moe_quant_status_string.argtypes = [i32]
+    lib.moe_quant_status_string.restype = ctypes.c_char_p
+    lib.moe_quant_last_error.argtypes = []
+    lib.moe_quant_last_error.restype = ctypes.c_char_p
+    lib.moe_quant_abi_version.argtypes = []
+    lib.moe_quant_abi_version.restype = ctypes.c_uint32
+    if lib.moe_quant_abi_version() != ABI_VERSION:
+        raise MoeQuantError(7, "library ABI version differs from the binding's")
+    _LIB = lib
+    return lib
+
+
+def _check(lib, status: int):
+    if status != 0:
+        raise MoeQuantError(status, lib.moe_quant_last_error().decode())
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+class Layer:
+    """One MoE expert layer over packed weights resident on the GPU.
+
+    ``w13`` [E, 2I, H/2] (4-bit formats) or [E, 2I, H] (FP8) uint8, ``w2``
+    [E, H, I/2] or [E, H, I]; scales and global scales as documented in
+    ``include/moe_quant.h``.  All tensors must live on the GPU and stay alive
+    as long as the layer.
+    """
+
+    def __init__(self, fmt: str, w13, w13_scale, w2, w2_scale, top_k: int,
+                 w13_gscale=None, w2_gscale=None):
+        self._lib = load_library()
+        if fmt not in FORMATS:
+            raise ValueError(f"unknown format {fmt!r}")
+        self.fmt = fmt
+        e, n13, kb = w13.shape
+        e2, h, _ = w2.shape
+        if e2 != e:
+            raise ValueError("w13 and w2 disagree on the number of experts")
+        self.num_experts, self.hidden, self.inter, self.top_k = e, h, n13 // 2, top_k
+        self._keep = (w13, w13_scale, w2, w2_scale, w13_gscale, w2_gscale)
+        d = LayerDesc(ABI_VERSION, e, h, n13 // 2, top_k, FORMATS[fmt],
+                      _ptr(w13), _ptr(w13_scale), _ptr(w13_gscale),
+                      _ptr(w2), _ptr(w2_scale), _ptr(w2_gscale))
+        handle = ctypes.c_void_p()
+        _check(self._lib, self._lib.moe_quant_init(ctypes.byref(d), ctypes.byref(handle)))
+        self._h = handle
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            self._lib.moe_quant_destroy(h)
+            self._h = None
+
+    def workspace_size(self, num_tokens: int) -> int:
+        n = ctypes.c_size_t()
+        _check(self._lib, self._lib.moe_quant_workspace_size(self._h, num_tokens, ctypes.byref(n)))
+        return n.value
+
+    def workspace(self, num_tokens: int, device=None):
+        import torch
+        return torch.empty(max(self.workspace_size(num_tokens), 256), dtype=torch.uint8,
+                           device=device or "cuda")
+
+    def forward(self, logits, hidden, residual=None, out=None, workspace=None,
+                probe: Optional[Dict] = None, events=None, stream=None):
+        """Enqueue one forward; returns ``out`` (bfloat16 [T, H])."""
+        import torch
+        t = hidden.shape[0]
+        if out is None:
+            out = torch.empty((t, self.hidden), dtype=torch.bfloat16, device=hidden.device)
+        if workspace is None:
+            workspace = self.workspace(t, hidden.device)
+        if logits.dtype == torch.float32:
+            ldt = MQ_F32
+        elif logits.dtype == torch.bfloat16:
+            ldt = MQ_BF16
+        else:
+            raise ValueError("router logits must be float32 or bfloat16")
+        pr = None
+        if probe is not None or events is not None:
+            pr = Probe()
+            probe = probe or {}
+            for name in ("topk_ids", "topk_w", "expert_offsets", "sorted_token_ids", "inv_pos", "h"):
+                setattr(pr, name, _ptr(probe.get(name)))
+            if events is not None:
+                for i, ev in enumerate(events):
+                    pr.events[i] = None if ev is None else ev.cuda_event
+        st = self._lib.moe_quant_forward(
+            self._h, _ptr(logits), ldt, _ptr(hidden), _ptr(residual), t, _ptr(out),
+            _ptr(workspace), workspace.numel(), ctypes.byref(pr) if pr is not None else None,
+            _stream(stream))
+        _check(self._lib, st)
+        return out
+
+    def check(self, workspace, stream=None) -> bool:
+        """True if the last forward on ``workspace`` saturated its FP16 intermediate."""
+        st = self._lib.moe_quant_check(self._h, _ptr(workspace), _stream(stream))
+        if st == 9:
+            return True
+        _check(self._lib, st)
+        return False
+
+    def dequantize(self, which: int, expert: int, stream=None):
+        import torch
+        n, k = (2 * self.inter, self.hidden) if which == 0 else (self.hidden, self.inter)
+        out = torch.empty((n, k), dtype=torch.float32, device="cuda")
+        _check(self._lib, self._lib.moe_quant_dequantize(self._h, which, expert, _ptr(out),
+                                                          _stream(stream)))
+        return out
