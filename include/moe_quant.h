@@ -1,0 +1,218 @@
+/*
+ * moe_quant.h - C ABI of libmoe_quant.so: the routed MoE expert layer with
+ * block-quantized expert weights on AMD Instinct MI355X (gfx950).
+ *
+ * What the layer computes.  The model cards describe the thinker's routed
+ * experts kept packed in GPU memory and dequantized per layer "just in time"
+ * for one grouped matmul ("clef-omni-fp8" card, section "How this checkpoint
+ * runs"; "clef-omni-int4" card, section "How this checkpoint runs";
+ * "clef-omni-NVFP4" card, section "How it was made").  For T tokens with
+ * hidden states x[T, H] and router logits l[T, E]:
+ *
+ *   ids[t, 0..k)  = the k largest logits of token t, in descending order, ties
+ *                   to the lower expert id;
+ *   w[t, j]       = softmax over the k selected logits;
+ *   y[t]          = sum_j w[t, j] * W2[e] (silu(G) * U),   e = ids[t, j],
+ *                   [G; U] = W13[e] x[t]  (gate rows first, then up rows),
+ *                   silu(z) = z / (1 + exp(-z));
+ *   out[t]        = bf16(y[t])  or  bf16(residual[t] + y[t]).
+ *
+ * W13[e] is [2I, H], W2[e] is [H, I]; both are stored per expert, stacked over
+ * experts, row major with the input dimension K contiguous, in one of three
+ * packed formats (see mq_wformat).  The router itself is not part of the
+ * library: it stays a BF16 linear layer on every card ("clef-omni-int4" card,
+ * section "Recipe": ignore_layers=mlp.gate); its logits are an input.
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers, owned by the caller, row major
+ *    and contiguous.  The library never allocates device memory, never copies
+ *    weights and keeps no device state: init only borrows the weight pointers
+ *    for the lifetime of the handle.
+ *  - Every entry point returns an mq_status.  Argument checks run on the host
+ *    before anything is enqueued; on failure nothing is enqueued and
+ *    moe_quant_last_error() holds a one-line explanation (thread local).
+ *    Nothing is printed and no exception crosses the ABI.
+ *  - Work is enqueued asynchronously on the caller's HIP stream (a
+ *    hipStream_t, passed as struct ihipStream_t *; NULL is the default stream).
+ *  - A handle is immutable after init: concurrent forward calls on different
+ *    streams are safe as long as each uses its own workspace.
+ */
+#ifndef MOE_QUANT_H
+#define MOE_QUANT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_QUANT_ABI_VERSION 1u
+
+struct ihipStream_t; /* hipStream_t */
+struct ihipEvent_t;  /* hipEvent_t  */
+
+typedef enum {
+  MQ_OK = 0,
+  MQ_E_NULL = 1,      /* a required pointer is NULL                                  */
+  MQ_E_SHAPE = 2,     /* a dimension is out of range or not a multiple of the block  */
+  MQ_E_ALIGN = 3,     /* a pointer is not aligned as required                        */
+  MQ_E_FORMAT = 4,    /* unknown weight format                                       */
+  MQ_E_DTYPE = 5,     /* unknown logits dtype                                        */
+  MQ_E_WORKSPACE = 6, /* workspace NULL or smaller than moe_quant_workspace_size()   */
+  MQ_E_ABI = 7,       /* descriptor built against another MOE_QUANT_ABI_VERSION      */
+  MQ_E_HIP = 8,       /* a HIP launch or runtime call failed                         */
+  MQ_E_OVERFLOW = 9   /* the FP16 SwiGLU intermediate saturated (moe_quant_check)    */
+} mq_status;
+
+/*
+ * Packed weight formats.  N is a projection's output dim and K its input dim
+ * (W13: N = 2I, K = H; W2: N = H, K = I).  4-bit codes are packed two per
+ * byte, the even k in the low nibble.
+ *
+ * MQ_W_INT4_G128  INT4 W4A16, symmetric, one scale per 128 consecutive k of a
+ *                 row ("clef-omni-int4" card, intro and section "What was
+ *                 quantized").
+ *     w      uint8   [E, N, K/2]    nibble c = q + 8 (offset binary)
+ *     scale  float16 [E, N, K/128]
+ *     weight = (c - 8) * scale[n, k/128]
+ *
+ * MQ_W_FP8_B128   FP8 E4M3 (OCP E4M3FN: bias 7, max 448, 0x7F/0xFF NaN) with
+ *                 one FP32 scale per 128x128 block ("clef-omni-fp8" card,
+ *                 sections "What was quantized" and "Recipe"; the stored scale
+ *                 is weight_scale_inv, the dequantization multiplier).
+ *     w      uint8   [E, N, K]      E4M3FN bits
+ *     scale  float32 [E, N/128, K/128]
+ *     weight = e4m3(w) * scale[n/128, k/128]
+ *
+ * MQ_W_NVFP4_G16  NVFP4: FP4 E2M1 values, one E4M3 scale per 16 weights along
+ *                 k, one FP32 global scale per expert matrix
+ *                 ("clef-omni-NVFP4" card, section "How it was made"; gate and
+ *                 up are one concatenated matrix and share its global scale).
+ *     w      uint8   [E, N, K/2]    E2M1 nibbles (bit 3 = sign)
+ *     scale  uint8   [E, N, K/16]   E4M3FN bits
+ *     gscale float32 [E]            global scale g = 448*6/amax
+ *     weight = e2m1(c) * e4m3(scale[n, k/16]) / gscale[e]
+ *
+ * Dimension limits of this version: H and I multiples of 128 for every format
+ * (the NVFP4 format itself only needs 16), 1 <= k <= E <= 512.
+ */
+typedef enum { MQ_W_INT4_G128 = 1, MQ_W_FP8_B128 = 2, MQ_W_NVFP4_G16 = 3 } mq_wformat;
+
+/* Router-logit element type; BF16 logits are widened exactly to FP32. */
+typedef enum { MQ_F32 = 0, MQ_BF16 = 1 } mq_dtype;
+
+typedef struct {
+  uint32_t abi_version; /* must equal MOE_QUANT_ABI_VERSION                      */
+  int32_t num_experts;  /* E                                                      */
+  int32_t hidden;       /* H                                                      */
+  int32_t intermediate; /* I (per expert)                                         */
+  int32_t top_k;        /* k                                                      */
+  int32_t format;       /* mq_wformat                                             */
+  const void *w13;      /* gate_up weights [E, 2I, .], 16-byte aligned            */
+  const void *w13_scale;/* its scales, 16-byte aligned                            */
+  const float *w13_gscale; /* NVFP4 only: [E]; must be NULL for the other formats */
+  const void *w2;       /* down weights [E, H, .], 16-byte aligned                */
+  const void *w2_scale;
+  const float *w2_gscale;
+} mq_layer_desc;
+
+typedef struct mq_layer mq_layer; /* opaque host object */
+
+/* Stages of one forward call, in launch order (for mq_probe.events). */
+enum {
+  MQ_STAGE_ROUTE = 0,   /* top-k + softmax + FP16 staging of the hidden rows */
+  MQ_STAGE_PERMUTE = 1, /* histogram, scan and stable grouping by expert     */
+  MQ_STAGE_GATE_UP = 2, /* grouped gate/up GEMM with SwiGLU epilogue         */
+  MQ_STAGE_DOWN = 3,    /* grouped down GEMM, routing-weighted per slot      */
+  MQ_STAGE_COMBINE = 4, /* slot-ordered sum (+ residual), BF16 rounding      */
+  MQ_NUM_STAGES = 5
+};
+
+/*
+ * Optional extra outputs of a forward call, for tests and profiling.  Every
+ * field may be NULL.  Device arrays are written in stream order:
+ *   topk_ids         int32 [T, k]   selected experts, descending logit
+ *   topk_w           float [T, k]   routing weights
+ *   expert_offsets   int32 [E + 1]  grouped row range of each expert
+ *   sorted_token_ids int32 [T * k]  token of each grouped row (experts
+ *                                   ascending, tokens ascending inside one)
+ *   inv_pos          int32 [T * k]  grouped row of slot t * k + j
+ *   h                uint16 [T*k, I] FP16 bits of the SwiGLU intermediate in
+ *                                   grouped row order
+ * events[2 * s] / events[2 * s + 1] (hipEvent_t) are recorded on the stream
+ * right before / after stage s.
+ */
+typedef struct {
+  int32_t *topk_ids;
+  float *topk_w;
+  int32_t *expert_offsets;
+  int32_t *sorted_token_ids;
+  int32_t *inv_pos;
+  uint16_t *h;
+  struct ihipEvent_t *events[2 * MQ_NUM_STAGES];
+} mq_probe;
+
+/*
+ * Validate a layer descriptor and create a handle.  Host only: no HIP call is
+ * made.  On MQ_OK *out holds a handle to release with moe_quant_destroy.
+ * Errors: MQ_E_NULL (d, out or a weight pointer NULL; gscale NULL for NVFP4),
+ * MQ_E_ABI, MQ_E_FORMAT, MQ_E_SHAPE, MQ_E_ALIGN.
+ */
+mq_status moe_quant_init(const mq_layer_desc *d, mq_layer **out);
+
+/*
+ * Device workspace bytes that one forward call over num_tokens tokens needs
+ * (256-byte aligned start required).  num_tokens >= 0.  Host only.
+ */
+mq_status moe_quant_workspace_size(const mq_layer *L, int64_t num_tokens, size_t *bytes);
+
+/*
+ * Enqueue one layer forward on `stream`.
+ *   router_logits  [T, E] of logits_dtype, 16-byte aligned
+ *   hidden_bf16    [T, H] BF16 bits, 16-byte aligned
+ *   residual_bf16  NULL, or [T, H]: then out = bf16(residual + moe(hidden))
+ *   out_bf16       [T, H] BF16 bits, 16-byte aligned; may alias residual_bf16
+ *   workspace      >= moe_quant_workspace_size(L, T) bytes, 256-byte aligned;
+ *                  its contents on entry do not matter
+ *   probe          NULL, or extra outputs (see mq_probe)
+ * num_tokens == 0 returns MQ_OK without enqueuing anything.  Inputs must not
+ * hold NaN or Inf; results are then unspecified but every access stays in
+ * bounds.  Returns MQ_E_HIP if a launch fails.
+ */
+mq_status moe_quant_forward(const mq_layer *L, const void *router_logits, int32_t logits_dtype,
+                            const uint16_t *hidden_bf16, const uint16_t *residual_bf16,
+                            int64_t num_tokens, uint16_t *out_bf16, void *workspace,
+                            size_t workspace_bytes, const mq_probe *probe,
+                            struct ihipStream_t *stream);
+
+/*
+ * Synchronize `stream` and report whether the last forward that used
+ * `workspace` saturated its FP16 SwiGLU intermediate (|h| > 65504 clamped):
+ * MQ_OK if not, MQ_E_OVERFLOW if it did.  workspace as passed to forward.
+ */
+mq_status moe_quant_check(const mq_layer *L, const void *workspace, struct ihipStream_t *stream);
+
+/*
+ * Test entry: enqueue the dequantization of one expert matrix through the
+ * device unpack paths the GEMMs use, writing float32 [N, K] to `out`
+ * (which: 0 = W13 [2I, H], 1 = W2 [H, I]).  Each value is the format's
+ * definition evaluated in FP32 with at most one rounding: INT4 (c - 8) * s is
+ * exact; FP8 e4m3 * scale is one FP32 multiply; NVFP4 (e2m1 * e4m3) is exact
+ * and is then divided by gscale (one IEEE FP32 division).
+ * Errors: MQ_E_NULL, MQ_E_SHAPE (which or expert out of range), MQ_E_HIP.
+ */
+mq_status moe_quant_dequantize(const mq_layer *L, int32_t which, int32_t expert, float *out,
+                               struct ihipStream_t *stream);
+
+void moe_quant_destroy(mq_layer *L);
+
+/* Static strings; never NULL. */
+const char *moe_quant_status_string(mq_status s);
+const char *moe_quant_last_error(void);
+uint32_t moe_quant_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_QUANT_H */

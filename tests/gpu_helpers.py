@@ -1,0 +1,120 @@
+"""Shared helpers of the GPU parity tests: build packed layers (oracle
+quantizer or directly drawn codes), run the HIP path through the C ABI, and
+compare against the oracle."""
+from __future__ import annotations
+
+import multiprocessing
+import os
+import sys
+from concurrent.futures import ProcessPoolExecutor
+
+import numpy as np
+
+from oracle import formats, moe
+from weight_quantized_moe_amd import synth
+
+RTOL_L2 = 2e-3      # max relative L2 error of a layer output vs the float64 oracle
+ATOL_MAX = 2e-2     # max absolute error
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _quant_one(args):
+    fmt, wid, layer, which, e, n, k = args
+    w = synth.expert_weight(wid, layer, which, e, n, k).astype(np.float64)
+    return formats.quantize_expert(fmt, w)
+
+
+def quantized_layer(fmt, wid, layer, E, H, I, workers=None):
+    """Oracle-quantized N(0, 0.02) weights of one layer (Packed w13, Packed w2)."""
+    out = []
+    for which, n, k in (("w13", 2 * I, H), ("w2", H, I)):
+        p = formats.empty_packed(fmt, E, n, k)
+        jobs = [(fmt, wid, layer, which, e, n, k) for e in range(E)]
+        if E * n * k > 4_000_000:
+            nproc = workers or min(16, len(os.sched_getaffinity(0)))
+            ctx = multiprocessing.get_context("spawn")
+            with ProcessPoolExecutor(nproc, mp_context=ctx) as ex:
+                res = list(ex.map(_quant_one, jobs, chunksize=4))
+        else:
+            res = [_quant_one(j) for j in jobs]
+        for e, (pw, s, g) in enumerate(res):
+            p.w[e] = pw
+            p.scale[e] = s
+            if g is not None:
+                p.gscale[e] = g
+        out.append(p)
+    return out[0], out[1]
+
+
+def random_layer(fmt, seed, E, H, I):
+    """Packed weights drawn directly (uniform codes, realistic scales)."""
+    w, s, g = synth.random_packed(fmt, E, 2 * I, H, seed)
+    p13 = formats.Packed(fmt, w, s, g, 2 * I, H)
+    w, s, g = synth.random_packed(fmt, E, H, I, seed + 1)
+    p2 = formats.Packed(fmt, w, s, g, H, I)
+    return p13, p2
+
+
+def dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+class GpuLayer:
+    def __init__(self, p13, p2, top_k):
+        from weight_quantized_moe_amd import Layer
+        self.p13, self.p2, self.top_k = p13, p2, top_k
+        self.t = [dev(p13.w), dev(p13.scale), dev(p2.w), dev(p2.scale)]
+        g13 = dev(p13.gscale) if p13.gscale is not None else None
+        g2 = dev(p2.gscale) if p2.gscale is not None else None
+        self.t += [g13, g2]
+        self.layer = Layer(p13.fmt, self.t[0], self.t[1], self.t[2], self.t[3], top_k,
+                           w13_gscale=g13, w2_gscale=g2)
+        self.oracle = moe.Layer(p13, p2, top_k)
+
+    def run(self, logits, x_bits, res_bits=None, probe=False, logits_bf16=False):
+        import torch
+        T = x_bits.shape[0]
+        E, k, I = self.layer.num_experts, self.top_k, self.layer.inter
+        lg = dev(logits)
+        if logits_bf16:
+            lg = lg.view(torch.bfloat16)
+        x = dev(x_bits.view(np.int16)).view(torch.bfloat16)
+        res = dev(res_bits.view(np.int16)).view(torch.bfloat16) if res_bits is not None else None
+        pr = None
+        if probe:
+            pr = dict(topk_ids=torch.empty((T, k), dtype=torch.int32, device="cuda"),
+                      topk_w=torch.empty((T, k), dtype=torch.float32, device="cuda"),
+                      expert_offsets=torch.empty(E + 1, dtype=torch.int32, device="cuda"),
+                      sorted_token_ids=torch.empty(T * k, dtype=torch.int32, device="cuda"),
+                      inv_pos=torch.empty(T * k, dtype=torch.int32, device="cuda"),
+                      h=torch.empty((T * k, I), dtype=torch.float16, device="cuda"))
+        ws = self.layer.workspace(T)
+        out = self.layer.forward(lg, x, residual=res, workspace=ws, probe=pr)
+        torch.cuda.synchronize()
+        out_np = out.view(torch.int16).cpu().numpy().view(np.uint16)
+        pr_np = {k_: v.cpu().numpy() for k_, v in pr.items()} if pr else None
+        overflow = self.layer.check(ws)
+        return out_np, pr_np, overflow
+
+
+def errors(out_bits, y_ref):
+    y = moe.bf16_bits_to_f64(out_bits)
+    rel = float(np.linalg.norm(y - y_ref) / max(np.linalg.norm(y_ref), 1e-300))
+    mx = float(np.abs(y - y_ref).max()) if y.size else 0.0
+    return rel, mx
+
+
+def check_routing(pr, logits, k, E):
+    """Bit-exact routing and grouping against the oracle."""
+    ids, w = moe.route(logits, k)
+    assert np.array_equal(pr["topk_ids"], ids), "top-k ids differ"
+    assert np.allclose(pr["topk_w"], w, rtol=2e-6, atol=1e-7), "routing weights differ"
+    p = moe.permute(ids, E)
+    assert np.array_equal(pr["expert_offsets"], p.offsets), "expert offsets differ"
+    assert np.array_equal(pr["sorted_token_ids"], p.sorted_token_ids), "grouped token order differs"
+    assert np.array_equal(pr["inv_pos"], p.inv_pos), "inverse positions differ"

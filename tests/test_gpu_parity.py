@@ -1,0 +1,176 @@
+"""Parity of the HIP path (through the C ABI) with the float64 oracle.
+
+Routing, grouping and dequantized weights are compared bit-exactly; layer
+outputs within relative L2 2e-3 and max abs 2e-2 of the oracle.
+"""
+import numpy as np
+import pytest
+
+from oracle import codecs, formats, moe
+from weight_quantized_moe_amd import synth
+
+from gpu_helpers import (ATOL_MAX, RTOL_L2, GpuLayer, check_routing, errors, log,
+                         quantized_layer, random_layer)
+
+pytestmark = pytest.mark.gpu
+
+FMTS = formats.FORMATS
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from weight_quantized_moe_amd import load_library
+    load_library()      # fails loudly if the HIP library is missing
+
+
+# ------------------------------------------------------------ dequantization
+
+def _special_layer(fmt, rng):
+    """Small layer whose codes cover every code value of the format."""
+    E, H, I = 2, 256, 128
+    p13, p2 = quantized_layer(fmt, 11, 0, E, H, I)
+    for p in (p13, p2):
+        flat = p.w.reshape(-1)
+        if fmt == formats.FP8:
+            codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+        else:
+            codes = np.arange(256, dtype=np.uint8)        # all nibble pairs
+        flat[:len(codes)] = codes
+        if fmt == formats.NVFP4:
+            sflat = p.scale.reshape(-1)
+            sc = np.array([c for c in range(128) if c != 0x7F], np.uint8)
+            sflat[:len(sc)] = sc
+    return p13, p2
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_dequantize_bit_exact(fmt):
+    log(f"[dequant] fmt={fmt}")
+    p13, p2 = _special_layer(fmt, np.random.default_rng(0))
+    g = GpuLayer(p13, p2, 2)
+    for which, p in ((0, p13), (1, p2)):
+        for e in range(p.num_experts):
+            got = g.layer.dequantize(which, e).cpu().numpy()
+            ref = formats.dequantize_expert(p, e)
+            if fmt == formats.NVFP4:
+                # the device divides the exact FP32 product by gscale once
+                vals = codecs.decode_e2m1(codecs.unpack_nibbles(p.w[e])).reshape(p.n, p.k // 16, 16)
+                s = codecs.decode_e4m3(p.scale[e])[:, :, None]
+                ref32 = (vals * s).astype(np.float32).reshape(p.n, p.k) / np.float32(p.gscale[e])
+            else:
+                ref32 = ref.astype(np.float32)   # INT4 exact; FP8 one rounding
+            assert np.array_equal(got, ref32), f"{fmt} which={which} e={e}"
+
+
+# ------------------------------------------------------------ routing
+
+@pytest.mark.parametrize("logit_kind", ["f32", "bf16_ties"])
+@pytest.mark.parametrize("T", [1, 37, 300, 2500])
+def test_routing_and_grouping_bit_exact(T, logit_kind):
+    log(f"[routing] T={T} logits={logit_kind}")
+    E, H, I, k = 128, 256, 128, 8
+    p13, p2 = random_layer(formats.INT4, 5, E, H, I)
+    g = GpuLayer(p13, p2, k)
+    rng = np.random.default_rng(T)
+    x = synth.hidden_bf16(6, 0, T, H)
+    if logit_kind == "f32":
+        lg = synth.router_logits(6, 0, T, E)
+        out, pr, _ = g.run(lg, x, probe=True)
+        check_routing(pr, lg, k, E)
+    else:
+        # coarse BF16 logits: many exact ties
+        lgf = np.round(rng.standard_normal((T, E)) * 4) / 4
+        bits = synth.to_bf16_bits(lgf.astype(np.float32))
+        out, pr, _ = g.run(bits, x, probe=True, logits_bf16=True)
+        check_routing(pr, moe.bf16_bits_to_f64(bits), k, E)
+
+
+# ------------------------------------------------------------ layer outputs
+
+def _check_layer(g, lg, x, res=None, tokens=None, tag=""):
+    out, pr, ovf = g.run(lg, x, res, probe=True)
+    check_routing(pr, lg, g.top_k, g.layer.num_experts) if tokens is None else None
+    assert not ovf
+    y, _, _ = moe.moe_forward(g.oracle, lg, x, res, tokens=tokens)
+    got = out if tokens is None else out[tokens]
+    rel, mx = errors(got, y)
+    log(f"    {tag} rel_l2={rel:.3e} max_abs={mx:.3e}")
+    assert rel <= RTOL_L2 and mx <= ATOL_MAX, (tag, rel, mx)
+    return out, pr
+
+
+def test_tiny_config_int4():
+    """Tiny layer: H 256, I 128, 8 experts, top-2, 64 tokens, INT4 g128."""
+    w = synth.WORKLOADS["tiny"]
+    log("[tiny]")
+    p13, p2 = quantized_layer(w.fmt, w.wid, 0, w.experts, w.hidden, w.inter)
+    g = GpuLayer(p13, p2, w.top_k)
+    lg = synth.router_logits(w.wid, 0, 64, w.experts)
+    x = synth.hidden_bf16(w.wid, 0, 64, w.hidden)
+    _check_layer(g, lg, x, tag="tiny")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("T,k", [(1, 4), (5, 4), (64, 4), (300, 4), (1000, 2), (777, 16)])
+def test_small_layers(fmt, T, k):
+    """E 16, H 512, I 384: decode (T*k <= 16 E) and prefill paths, ragged tiles."""
+    log(f"[small] fmt={fmt} T={T} k={k}")
+    E, H, I = 16, 512, 384
+    p13, p2 = quantized_layer(fmt, 12, k, E, H, I)
+    g = GpuLayer(p13, p2, k)
+    lg = synth.router_logits(12, T, T, E, "bias")
+    x = synth.hidden_bf16(12, T, T, H)
+    _check_layer(g, lg, x, tag=f"{fmt} T={T} k={k}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_residual_and_determinism(fmt):
+    log(f"[residual] fmt={fmt}")
+    E, H, I, k, T = 16, 256, 256, 4, 200
+    p13, p2 = quantized_layer(fmt, 13, 0, E, H, I)
+    g = GpuLayer(p13, p2, k)
+    lg = synth.router_logits(13, 0, T, E)
+    x = synth.hidden_bf16(13, 0, T, H)
+    res = synth.residual_bf16(13, 0, T, H)
+    out1, _ = _check_layer(g, lg, x, res, tag="residual")
+    out2, _, _ = g.run(lg, x, res)
+    assert np.array_equal(out1, out2), "repeat runs differ"
+
+
+def test_edge_cases():
+    log("[edge] k=1, k=E, single expert, empty experts")
+    H, I = 256, 128
+    for (E, k, T) in [(8, 1, 50), (8, 8, 20), (1, 1, 9), (64, 2, 3)]:
+        p13, p2 = quantized_layer(formats.INT4, 14, E, E, H, I)
+        g = GpuLayer(p13, p2, k)
+        lg = synth.router_logits(14, E, T, E)
+        x = synth.hidden_bf16(14, E, T, H)
+        _check_layer(g, lg, x, tag=f"E={E} k={k} T={T}")
+
+
+def test_zero_tokens_is_a_noop():
+    import torch
+    E, H, I = 8, 256, 128
+    p13, p2 = random_layer(formats.FP8, 3, E, H, I)
+    g = GpuLayer(p13, p2, 2)
+    out = torch.full((0, H), 7, dtype=torch.bfloat16, device="cuda")
+    g.layer.forward(torch.empty((0, E), device="cuda"), torch.empty((0, H), dtype=torch.bfloat16,
+                    device="cuda"), out=out, workspace=torch.empty(256, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+
+
+def test_fp16_intermediate_overflow_flag():
+    """Saturating the FP16 SwiGLU intermediate sets the flag and clamps."""
+    log("[overflow]")
+    E, H, I, k, T = 4, 256, 128, 2, 16
+    p13, p2 = quantized_layer(formats.INT4, 15, 0, E, H, I)
+    p13.scale[:] = np.float16(60000.0)
+    g = GpuLayer(p13, p2, k)
+    lg = synth.router_logits(15, 0, T, E)
+    x = synth.hidden_bf16(15, 0, T, H)
+    _, pr, ovf = g.run(lg, x, probe=True)
+    assert ovf
+    assert np.nanmax(np.abs(pr["h"].astype(np.float32))) <= 65504.0

@@ -1,0 +1,64 @@
+// Internal declarations shared by the host ABI and the kernel launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mq {
+
+constexpr int kMaxExperts = 512;
+constexpr int kPrefillBM = 128;  // token rows per prefill M-tile
+
+// Workspace carve-up for one forward call over T tokens (offsets in bytes).
+struct Workspace {
+  size_t topk_ids, topk_w;     // int32 [R], float [R]            (R = T*k)
+  size_t offsets;              // int32 [E+1]
+  size_t active;               // int32 [1 + E]: count, then active expert ids
+  size_t mtile;                // int32 [E+1]: prefix of ceil(n_e / kPrefillBM)
+  size_t sorted_slots;         // int32 [R]: slot t*k+j of each grouped row
+  size_t inv_pos;              // int32 [R]
+  size_t x16;                  // fp16 [T, H]: hidden rows scaled by 2^-s_t
+  size_t rowscale;             // float [T]: 2^s_t
+  size_t h;                    // fp16 [R, I]
+  size_t partial;              // float [R, H]: routing-weighted expert outputs per slot
+  size_t flags;                // uint32 [4] at offset 0: bit 0 = FP16 intermediate saturated
+  size_t total;
+};
+
+Workspace workspace_layout(int64_t T, int E, int H, int I, int k);
+
+struct LayerDims {
+  int E, H, I, k, fmt;
+  const uint8_t *w13, *w2;
+  const void *s13, *s2;
+  const float *g13, *g2;
+};
+
+struct FwdPtrs {
+  const void *logits;
+  int logits_bf16;
+  const uint16_t *hidden;
+  const uint16_t *residual;
+  uint16_t *out;
+  char *ws;
+  int T;
+  // probe outputs (may be null)
+  int32_t *p_ids, *p_offsets, *p_sorted_tok, *p_inv;
+  float *p_w;
+  uint16_t *p_h;
+};
+
+// launchers (return hipGetLastError() after the launch)
+hipError_t launch_route(const LayerDims &L, const FwdPtrs &P, const Workspace &W, hipStream_t s);
+hipError_t launch_permute(const LayerDims &L, const FwdPtrs &P, const Workspace &W, hipStream_t s);
+hipError_t launch_gate_up(const LayerDims &L, const FwdPtrs &P, const Workspace &W, bool decode,
+                          hipStream_t s);
+hipError_t launch_down(const LayerDims &L, const FwdPtrs &P, const Workspace &W, bool decode,
+                       hipStream_t s);
+hipError_t launch_combine(const LayerDims &L, const FwdPtrs &P, const Workspace &W, hipStream_t s);
+hipError_t launch_dequantize(const LayerDims &L, int which, int expert, float *out, hipStream_t s);
+
+// Rows per expert at or below which the decode (weight-streaming) GEMMs run.
+bool use_decode_path(int64_t T, int E, int k);
+
+}  // namespace mq

@@ -1,0 +1,259 @@
+// Host side of the C ABI declared in include/moe_quant.h: argument checks,
+// workspace carve-up and the stream-ordered launch sequence of one forward.
+#include "../../include/moe_quant.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <new>
+
+#include "internal.h"
+
+struct mq_layer {
+  mq_layer_desc d;
+};
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+mq_status fail(mq_status s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+constexpr int64_t kMaxTokens = 1 << 22;
+
+}  // namespace
+
+namespace mq {
+
+Workspace workspace_layout(int64_t T, int E, int H, int I, int k) {
+  Workspace w{};
+  const size_t R = (size_t)T * k;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = up256(o + bytes);
+    return at;
+  };
+  w.flags = take(16);  // first, so its offset (0) does not depend on T
+  w.topk_ids = take(R * 4);
+  w.topk_w = take(R * 4);
+  w.offsets = take((size_t)(E + 1) * 4);
+  w.active = take((size_t)(E + 1) * 4);
+  w.mtile = take((size_t)(E + 1) * 4);
+  w.sorted_slots = take(R * 4);
+  w.inv_pos = take(R * 4);
+  w.x16 = take((size_t)T * H * 2);
+  w.rowscale = take((size_t)T * 4);
+  w.h = take(R * (size_t)I * 2);
+  w.partial = take(R * (size_t)H * 4);
+  w.total = o;
+  return w;
+}
+
+}  // namespace mq
+
+extern "C" {
+
+uint32_t moe_quant_abi_version(void) { return MOE_QUANT_ABI_VERSION; }
+
+const char *moe_quant_last_error(void) { return g_err; }
+
+const char *moe_quant_status_string(mq_status s) {
+  switch (s) {
+    case MQ_OK: return "MQ_OK: success";
+    case MQ_E_NULL: return "MQ_E_NULL: a required pointer is NULL";
+    case MQ_E_SHAPE: return "MQ_E_SHAPE: dimension out of range or not a block multiple";
+    case MQ_E_ALIGN: return "MQ_E_ALIGN: pointer not aligned as required";
+    case MQ_E_FORMAT: return "MQ_E_FORMAT: unknown weight format";
+    case MQ_E_DTYPE: return "MQ_E_DTYPE: unknown logits dtype";
+    case MQ_E_WORKSPACE: return "MQ_E_WORKSPACE: workspace missing or too small";
+    case MQ_E_ABI: return "MQ_E_ABI: descriptor ABI version mismatch";
+    case MQ_E_HIP: return "MQ_E_HIP: HIP runtime or launch failure";
+    case MQ_E_OVERFLOW: return "MQ_E_OVERFLOW: FP16 SwiGLU intermediate saturated";
+  }
+  return "unknown mq_status";
+}
+
+mq_status moe_quant_init(const mq_layer_desc *d, mq_layer **out) {
+  if (!d || !out) return fail(MQ_E_NULL, "init: desc and out must be non-NULL");
+  *out = nullptr;
+  if (d->abi_version != MOE_QUANT_ABI_VERSION)
+    return fail(MQ_E_ABI, "init: descriptor abi_version %u, library %u", d->abi_version,
+                MOE_QUANT_ABI_VERSION);
+  if (d->format != MQ_W_INT4_G128 && d->format != MQ_W_FP8_B128 && d->format != MQ_W_NVFP4_G16)
+    return fail(MQ_E_FORMAT, "init: unknown weight format %d", d->format);
+  const int E = d->num_experts, H = d->hidden, I = d->intermediate, k = d->top_k;
+  if (E < 1 || E > mq::kMaxExperts)
+    return fail(MQ_E_SHAPE, "init: num_experts %d outside [1, %d]", E, mq::kMaxExperts);
+  if (k < 1 || k > E || k > 64) return fail(MQ_E_SHAPE, "init: top_k %d outside [1, min(E, 64)]", k);
+  if (H < 128 || I < 128 || H % 128 || I % 128)
+    return fail(MQ_E_SHAPE,
+                "init: hidden %d and intermediate %d must be positive multiples of 128 "
+                "(block sizes of INT4 g128 / FP8 128x128; this version's tiles for NVFP4)",
+                H, I);
+  if ((int64_t)H > 65536 || (int64_t)I > 65536)
+    return fail(MQ_E_SHAPE, "init: hidden/intermediate above 65536");
+  if (!d->w13 || !d->w13_scale || !d->w2 || !d->w2_scale)
+    return fail(MQ_E_NULL, "init: weight and scale pointers must be non-NULL");
+  if (d->format == MQ_W_NVFP4_G16 && (!d->w13_gscale || !d->w2_gscale))
+    return fail(MQ_E_NULL, "init: NVFP4 needs w13_gscale and w2_gscale");
+  if (d->format != MQ_W_NVFP4_G16 && (d->w13_gscale || d->w2_gscale))
+    return fail(MQ_E_NULL, "init: gscale pointers must be NULL for INT4 and FP8");
+  const void *al16[4] = {d->w13, d->w13_scale, d->w2, d->w2_scale};
+  for (const void *p : al16)
+    if (!aligned(p, 16)) return fail(MQ_E_ALIGN, "init: weight/scale pointer %p not 16-byte aligned", p);
+  if ((d->w13_gscale && !aligned(d->w13_gscale, 4)) || (d->w2_gscale && !aligned(d->w2_gscale, 4)))
+    return fail(MQ_E_ALIGN, "init: gscale pointers must be 4-byte aligned");
+  mq_layer *L = new (std::nothrow) mq_layer;
+  if (!L) return fail(MQ_E_NULL, "init: host allocation failed");
+  L->d = *d;
+  *out = L;
+  g_err[0] = 0;
+  return MQ_OK;
+}
+
+void moe_quant_destroy(mq_layer *L) { delete L; }
+
+mq_status moe_quant_workspace_size(const mq_layer *L, int64_t num_tokens, size_t *bytes) {
+  if (!L || !bytes) return fail(MQ_E_NULL, "workspace_size: NULL argument");
+  if (num_tokens < 0 || num_tokens > kMaxTokens)
+    return fail(MQ_E_SHAPE, "workspace_size: num_tokens %lld outside [0, %lld]",
+                (long long)num_tokens, (long long)kMaxTokens);
+  const mq_layer_desc &d = L->d;
+  *bytes = mq::workspace_layout(num_tokens, d.num_experts, d.hidden, d.intermediate, d.top_k).total;
+  return MQ_OK;
+}
+
+static mq::LayerDims dims_of(const mq_layer *L) {
+  const mq_layer_desc &d = L->d;
+  mq::LayerDims D;
+  D.E = d.num_experts; D.H = d.hidden; D.I = d.intermediate; D.k = d.top_k; D.fmt = d.format;
+  D.w13 = (const uint8_t *)d.w13; D.w2 = (const uint8_t *)d.w2;
+  D.s13 = d.w13_scale; D.s2 = d.w2_scale;
+  D.g13 = d.w13_gscale; D.g2 = d.w2_gscale;
+  return D;
+}
+
+mq_status moe_quant_forward(const mq_layer *L, const void *router_logits, int32_t logits_dtype,
+                            const uint16_t *hidden_bf16, const uint16_t *residual_bf16,
+                            int64_t num_tokens, uint16_t *out_bf16, void *workspace,
+                            size_t workspace_bytes, const mq_probe *probe,
+                            struct ihipStream_t *stream) {
+  if (!L) return fail(MQ_E_NULL, "forward: NULL layer handle");
+  if (num_tokens < 0 || num_tokens > kMaxTokens)
+    return fail(MQ_E_SHAPE, "forward: num_tokens %lld outside [0, %lld]", (long long)num_tokens,
+                (long long)kMaxTokens);
+  if (logits_dtype != MQ_F32 && logits_dtype != MQ_BF16)
+    return fail(MQ_E_DTYPE, "forward: unknown logits dtype %d", logits_dtype);
+  if (num_tokens == 0) {
+    g_err[0] = 0;
+    return MQ_OK;
+  }
+  if (!router_logits || !hidden_bf16 || !out_bf16)
+    return fail(MQ_E_NULL, "forward: logits, hidden and out must be non-NULL");
+  if (!aligned(router_logits, 16) || !aligned(hidden_bf16, 16) || !aligned(out_bf16, 16) ||
+      (residual_bf16 && !aligned(residual_bf16, 16)))
+    return fail(MQ_E_ALIGN, "forward: logits/hidden/residual/out must be 16-byte aligned");
+  const mq::LayerDims D = dims_of(L);
+  const mq::Workspace W = mq::workspace_layout(num_tokens, D.E, D.H, D.I, D.k);
+  if (!workspace) return fail(MQ_E_WORKSPACE, "forward: workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(MQ_E_ALIGN, "forward: workspace not 256-byte aligned");
+  if (workspace_bytes < W.total)
+    return fail(MQ_E_WORKSPACE, "forward: workspace %zu bytes, need %zu", workspace_bytes, W.total);
+  if (probe) {
+    const void *pp[6] = {probe->topk_ids, probe->topk_w, probe->expert_offsets,
+                         probe->sorted_token_ids, probe->inv_pos, probe->h};
+    for (const void *p : pp)
+      if (p && !aligned(p, 4)) return fail(MQ_E_ALIGN, "forward: probe arrays must be 4-byte aligned");
+  }
+
+  mq::FwdPtrs P{};
+  P.logits = router_logits;
+  P.logits_bf16 = logits_dtype == MQ_BF16;
+  P.hidden = hidden_bf16;
+  P.residual = residual_bf16;
+  P.out = out_bf16;
+  P.ws = (char *)workspace;
+  P.T = (int)num_tokens;
+  if (probe) {
+    P.p_ids = probe->topk_ids;
+    P.p_w = probe->topk_w;
+    P.p_offsets = probe->expert_offsets;
+    P.p_sorted_tok = probe->sorted_token_ids;
+    P.p_inv = probe->inv_pos;
+    P.p_h = probe->h;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  const bool decode = mq::use_decode_path(num_tokens, D.E, D.k);
+  auto ev = [&](int stage, int after) {
+    if (probe && probe->events[2 * stage + after])
+      (void)hipEventRecord((hipEvent_t)probe->events[2 * stage + after], s);
+  };
+  hipError_t e;
+  ev(MQ_STAGE_ROUTE, 0);
+  if ((e = mq::launch_route(D, P, W, s)) != hipSuccess)
+    return fail(MQ_E_HIP, "forward: route launch: %s", hipGetErrorString(e));
+  ev(MQ_STAGE_ROUTE, 1);
+  ev(MQ_STAGE_PERMUTE, 0);
+  if ((e = mq::launch_permute(D, P, W, s)) != hipSuccess)
+    return fail(MQ_E_HIP, "forward: permute launch: %s", hipGetErrorString(e));
+  ev(MQ_STAGE_PERMUTE, 1);
+  ev(MQ_STAGE_GATE_UP, 0);
+  if ((e = mq::launch_gate_up(D, P, W, decode, s)) != hipSuccess)
+    return fail(MQ_E_HIP, "forward: gate_up launch: %s", hipGetErrorString(e));
+  ev(MQ_STAGE_GATE_UP, 1);
+  if (P.p_h) {
+    e = hipMemcpyAsync(P.p_h, P.ws + W.h, (size_t)num_tokens * D.k * D.I * 2,
+                       hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return fail(MQ_E_HIP, "forward: probe copy: %s", hipGetErrorString(e));
+  }
+  ev(MQ_STAGE_DOWN, 0);
+  if ((e = mq::launch_down(D, P, W, decode, s)) != hipSuccess)
+    return fail(MQ_E_HIP, "forward: down launch: %s", hipGetErrorString(e));
+  ev(MQ_STAGE_DOWN, 1);
+  ev(MQ_STAGE_COMBINE, 0);
+  if ((e = mq::launch_combine(D, P, W, s)) != hipSuccess)
+    return fail(MQ_E_HIP, "forward: combine launch: %s", hipGetErrorString(e));
+  ev(MQ_STAGE_COMBINE, 1);
+  g_err[0] = 0;
+  return MQ_OK;
+}
+
+mq_status moe_quant_check(const mq_layer *L, const void *workspace, struct ihipStream_t *stream) {
+  if (!L || !workspace) return fail(MQ_E_NULL, "check: NULL argument");
+  // the flags word is the first field of every workspace layout (offset 0)
+  hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return fail(MQ_E_HIP, "check: %s", hipGetErrorString(e));
+  uint32_t flag = 0;
+  e = hipMemcpy(&flag, workspace, sizeof(flag), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(MQ_E_HIP, "check: %s", hipGetErrorString(e));
+  if (flag) return fail(MQ_E_OVERFLOW, "check: FP16 SwiGLU intermediate saturated");
+  g_err[0] = 0;
+  return MQ_OK;
+}
+
+mq_status moe_quant_dequantize(const mq_layer *L, int32_t which, int32_t expert, float *out,
+                               struct ihipStream_t *stream) {
+  if (!L || !out) return fail(MQ_E_NULL, "dequantize: NULL argument");
+  if (which != 0 && which != 1) return fail(MQ_E_SHAPE, "dequantize: which must be 0 or 1");
+  if (expert < 0 || expert >= L->d.num_experts)
+    return fail(MQ_E_SHAPE, "dequantize: expert %d outside [0, %d)", expert, L->d.num_experts);
+  if (!aligned(out, 16)) return fail(MQ_E_ALIGN, "dequantize: out must be 16-byte aligned");
+  hipError_t e = mq::launch_dequantize(dims_of(L), which, expert, out, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(MQ_E_HIP, "dequantize: %s", hipGetErrorString(e));
+  g_err[0] = 0;
+  return MQ_OK;
+}
+
+}  // extern "C"
