@@ -122,12 +122,11 @@ def main():
     n_layers = max(2, math.ceil(1.5 * 2 ** 30 / layer_bytes))
     layers, np_layers = [], []
     for li in range(n_layers):
-        w, s, g = synth.random_packed(fmt, E, 2 * I, H, 1000 + 2 * li)
-        w_, s_, g_ = synth.random_packed(fmt, E, H, I, 1001 + 2 * li)
-        if li == 0:
-            np_layers = (w, s, g, w_, s_, g_)
-        to = lambda a: None if a is None else torch.from_numpy(a).to(dev)  # noqa: E731
-        t13, ts13, tg13, t2, ts2, tg2 = map(to, (w, s, g, w_, s_, g_))
+        t13, ts13, tg13 = synth.random_packed_torch(fmt, E, 2 * I, H, 1000 + 2 * li, dev)
+        t2, ts2, tg2 = synth.random_packed_torch(fmt, E, H, I, 1001 + 2 * li, dev)
+        if li == 0 and not args.no_cpu_baseline:
+            to_np = lambda a: None if a is None else a.cpu().numpy()  # noqa: E731
+            np_layers = tuple(map(to_np, (t13, ts13, tg13, t2, ts2, tg2)))
         layers.append(Layer(fmt, t13, ts13, t2, ts2, k, w13_gscale=tg13, w2_gscale=tg2))
 
     def run_config(T, steps, warmup):

@@ -51,7 +51,8 @@ def quantized_layer(fmt, wid, layer, E, H, I, workers=None):
 
 
 def random_layer(fmt, seed, E, H, I):
-    """Packed weights drawn directly (uniform codes, realistic scales)."""
+    """Packed weights drawn directly (codes and scales with the spread of
+    quantized N(0, 0.02) weights)."""
     w, s, g = synth.random_packed(fmt, E, 2 * I, H, seed)
     p13 = formats.Packed(fmt, w, s, g, 2 * I, H)
     w, s, g = synth.random_packed(fmt, E, H, I, seed + 1)
@@ -106,6 +107,12 @@ def errors(out_bits, y_ref):
     y = moe.bf16_bits_to_f64(out_bits)
     rel = float(np.linalg.norm(y - y_ref) / max(np.linalg.norm(y_ref), 1e-300))
     mx = float(np.abs(y - y_ref).max()) if y.size else 0.0
+    if y.size and mx > ATOL_MAX:
+        i = np.unravel_index(np.argmax(np.abs(y - y_ref)), y.shape)
+        ulp = 2.0 ** (np.floor(np.log2(max(abs(y_ref[i]), 2.0 ** -126))) - 7)
+        log(f"    worst element {tuple(int(v) for v in i)}: got {y[i]!r} oracle {y_ref[i]!r} "
+            f"(= {abs(y[i] - y_ref[i]) / ulp:.2f} bf16 ulp); output rms "
+            f"{float(np.sqrt(np.mean(y_ref ** 2))):.4g}, max {float(np.abs(y_ref).max()):.4g}")
     return rel, mx
 
 

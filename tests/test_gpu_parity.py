@@ -68,10 +68,12 @@ def test_dequantize_bit_exact(fmt):
 # ------------------------------------------------------------ routing
 
 @pytest.mark.parametrize("logit_kind", ["f32", "bf16_ties"])
-@pytest.mark.parametrize("T", [1, 37, 300, 2500])
-def test_routing_and_grouping_bit_exact(T, logit_kind):
-    log(f"[routing] T={T} logits={logit_kind}")
-    E, H, I, k = 128, 256, 128, 8
+@pytest.mark.parametrize("T,E,k", [(1, 128, 8), (37, 128, 8), (64, 128, 8), (65, 128, 8),
+                                   (300, 128, 8), (2500, 128, 8), (37, 200, 20), (300, 200, 6),
+                                   (50, 512, 64), (700, 512, 3)])
+def test_routing_and_grouping_bit_exact(T, E, k, logit_kind):
+    log(f"[routing] T={T} E={E} k={k} logits={logit_kind}")
+    H, I = 256, 128
     p13, p2 = random_layer(formats.INT4, 5, E, H, I)
     g = GpuLayer(p13, p2, k)
     rng = np.random.default_rng(T)

@@ -32,17 +32,34 @@ __device__ __forceinline__ u4 as_u4(h8 x) { return __builtin_bit_cast(u4, x); }
 
 // ---------------------------------------------------------------- INT4
 // One 32-bit word holds the 8 nibbles of k = 0..7 (k even in the low nibble of
-// each byte, so nibble i sits at bits 4i).  Masking bits {4i, 16+4i} and OR-ing
-// the FP16 pattern of 1024.0 yields the pair (1024 + c_i, 1024 + c_{i+4});
-// subtracting 1032 gives (c - 8) exactly.  The operand order is therefore
-// k = {0,4,1,5,2,6,3,7}; the activation operand is permuted to match
-// (perm_0415 below).
+// each byte, so nibble i sits at bits 4i).  OR-ing a masked nibble into the
+// FP16 pattern of 1024.0 gives an exact FP16 integer:
+//   (w      & 0x000F000F) | 0x6400 6400 -> (1024 + c0,    1024 + c4)
+//   (w      & 0x00F000F0) | 0x6400 6400 -> (1024 + 16 c1, 1024 + 16 c5)
+//   (w >> 8 & 0x000F000F) | ...          -> (1024 + c2,    1024 + c6)
+//   (w >> 8 & 0x00F000F0) | ...          -> (1024 + 16 c3, 1024 + 16 c7)
+// (1024 + 16 c <= 1264 keeps the exponent of 1024, ulp 1).  Then
+// x - 1032 = c - 8 and x / 16 - 72 = c - 8, both exact in one packed op.
+// The operand order is therefore k = {0,4,1,5,2,6,3,7}; the activation
+// operand is stored or permuted to match (perm_0415 below).  9 VALU ops per
+// 8 weights: 1 shift, 4 and-or, 4 packed FP16 add/fma.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t bits) {
+  uint32_t r;
+  // VOP3 on gfx9 takes no literal constants: keep mask and bits in registers
+  // so this stays one instruction instead of v_and + v_or.
+  asm volatile("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(mask), "v"(bits));
+  return r;
+}
 __device__ __forceinline__ h8 unpack_int4(uint32_t w) {
-  const h2 off = {(_Float16)1032.0f, (_Float16)1032.0f};
-  h2 p0 = as_h2((w & 0x000F000Fu) | 0x64006400u) - off;
-  h2 p1 = as_h2(((w >> 4) & 0x000F000Fu) | 0x64006400u) - off;
-  h2 p2 = as_h2(((w >> 8) & 0x000F000Fu) | 0x64006400u) - off;
-  h2 p3 = as_h2(((w >> 12) & 0x000F000Fu) | 0x64006400u) - off;
+  const uint32_t m_lo = 0x000F000Fu, m_hi = 0x00F000F0u, magic = 0x64006400u;
+  const h2 off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+  const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const h2 off16 = {(_Float16)-72.0f, (_Float16)-72.0f};
+  const uint32_t v = w >> 8;
+  const h2 p0 = as_h2(and_or(w, m_lo, magic)) + off;
+  const h2 p1 = __builtin_elementwise_fma(as_h2(and_or(w, m_hi, magic)), sixteenth, off16);
+  const h2 p2 = as_h2(and_or(v, m_lo, magic)) + off;
+  const h2 p3 = __builtin_elementwise_fma(as_h2(and_or(v, m_hi, magic)), sixteenth, off16);
   u4 r = {as_u32(p0), as_u32(p1), as_u32(p2), as_u32(p3)};
   return as_h8(r);
 }
@@ -107,6 +124,38 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 }
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) {
   return __builtin_bit_cast(float, b << 16);
+}
+
+// Power-of-two row scaling of BF16 activations into FP16: the shift s puts
+// max|x| * 2^-s into [2^14, 2^15) (clamped to [-120, 120] so 2^+-s stay normal
+// FP32 numbers); then every BF16 value above max * 2^-31 is exact in FP16.
+__device__ __forceinline__ int row_shift(float m) {
+  if (!(m > 0.f)) return 0;
+  const int ex = (int)((__builtin_bit_cast(uint32_t, m) >> 23) & 0xFF) - 127;
+  const int sh = ex - 14;
+  return sh < -120 ? -120 : (sh > 120 ? 120 : sh);
+}
+__device__ __forceinline__ float pow2f(int s) {
+  return __builtin_bit_cast(float, (uint32_t)(127 + s) << 23);
+}
+// 8 BF16 values (bits) times a power of two -> 8 FP16 values.
+__device__ __forceinline__ u4 bf16x8_to_f16x8(u4 v, float scale) {
+  u4 o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    h2 hh = {(_Float16)(bf16_to_f32(v[q] & 0xFFFFu) * scale),
+             (_Float16)(bf16_to_f32(v[q] >> 16) * scale)};
+    o[q] = as_u32(hh);
+  }
+  return o;
+}
+__device__ __forceinline__ float absmax_bf16x8(u4 v, float m) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    m = fmaxf(m, fabsf(bf16_to_f32(v[q] & 0xFFFFu)));
+    m = fmaxf(m, fabsf(bf16_to_f32(v[q] >> 16)));
+  }
+  return m;
 }
 
 template <typename T>

@@ -14,6 +14,8 @@
 // grouped tokens), the B operand is weights (columns = output features).  A
 // lane therefore owns one output column, so a per-column scale is one scalar
 // per lane.
+#include <algorithm>
+
 #include "device.h"
 #include "internal.h"
 
@@ -35,8 +37,6 @@ struct GemmArgs {
   int tiles;              // decode: column tiles per expert; prefill: N tiles
 };
 
-constexpr int kDecodeKC = 2048;  // k chunk of the activation rows kept in LDS
-
 __device__ __forceinline__ void store_h(const GemmArgs &a, int r, int col, float g, float u) {
   float hv = silu(g) * u;
   if (fabsf(hv) > 65504.f) {
@@ -47,117 +47,148 @@ __device__ __forceinline__ void store_h(const GemmArgs &a, int r, int col, float
 }
 
 // ===========================================================================
-// Decode path: few rows per expert.  The weights are streamed once from HBM
-// straight into MFMA B-operand registers (no LDS round trip); the <= 16 rows
-// of one expert sit in LDS and feed the A operand of 16x16x32 MFMAs.
-//   lane l: output column n = l % 16, k slice q = l / 16.
-//   group g (128 k): lane reads 32 consecutive k of its weight row,
-//   k = 128 g + 32 q + [0, 32), and MFMA j in 0..3 consumes k + 8 j + [0, 8).
-// Each wave owns two 16-column tiles (gate + matching up columns, or two
-// adjacent down columns); KSPLIT waves split the k groups of one tile pair.
+// Decode path: few rows per expert.  Weights are streamed once from HBM
+// straight into MFMA B-operand registers, kD groups ahead of their use; the
+// <= 16 activation rows of the expert (FP16, prepared by the routing kernel)
+// are copied once per unit into LDS and feed the A operand.
+//   16x16x32 MFMA, lane l: output column n = l % 16, k slice q = l / 16, and
+//   A row m = l % 16 (a grouped row of the expert; rows >= nrows are never
+//   written to LDS and never stored: an MFMA output row depends only on its
+//   own A row).  Group g (128 k): lane holds k = 128 g + 32 q + [0, 32); MFMA
+//   j in 0..3 consumes k + 8 j + [0, 8).
+// A block has kDecodeWaves waves: CG column-tile pairs x KSPLIT k-splits.  Each
+// wave owns two 16-column tiles (gate + matching up columns, or two adjacent
+// down columns); KSPLIT waves reduce their partial sums through LDS.  The grid
+// is persistent: resident blocks loop over (expert, tile group) units.
 // ===========================================================================
+constexpr int kDecodeWaves = 8;
+#ifndef MQ_DECODE_DEPTH
+#define MQ_DECODE_DEPTH 4
+#endif
+constexpr int kD = MQ_DECODE_DEPTH;  // weight groups in flight per wave (even)
+static_assert(kD % 2 == 0, "groups are prefetched in pairs");
+
+// Registers of one group in flight.  Scales stay raw until use: a conversion
+// at load time would make the compiler wait for that load, and loads retire in
+// order, so it would drain every older prefetch as well.
 template <int FMT>
 struct DecodeFrag {
   u4 w[2];
   u4 w2[2];
-  float s[2];
-  uint32_t sb[2];
+  float s[2];       // FP8 block scale
+  uint32_t sb[2];   // INT4: FP16 group-scale bits; NVFP4: two E4M3 block-scale bytes
 };
 
-template <int FMT, int STAGE>
-__device__ __forceinline__ void stage_rows(_Float16 *As, int lda, const GemmArgs &a, int rbeg,
-                                           int nrows, int kc, int kcn) {
-  const int cpr = kcn >> 3;
-  for (int idx = threadIdx.x; idx < 16 * cpr; idx += 256) {
-    const int m = idx / cpr, c = idx - m * cpr;
-    u4 v = {0u, 0u, 0u, 0u};
-    if (m < nrows) {
-      const _Float16 *src;
-      if (STAGE == 0)
-        src = a.a_src + (size_t)(a.sorted_slots[rbeg + m] / a.k) * a.K + kc + c * 8;
-      else
-        src = a.a_src + (size_t)(rbeg + m) * a.K + kc + c * 8;
-      v = *(const u4 *)src;
-      if (FMT == FMT_INT4) v = perm_0415(v);
-    }
-    *(u4 *)(As + m * lda + c * 8) = v;
-  }
-}
-
-template <int FMT, int STAGE, int KSPLIT>
-__global__ __launch_bounds__(256) void gemm_decode(GemmArgs a) {
+template <int FMT, int STAGE, int KSPLIT, int GCT>
+__global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode(GemmArgs a) {
+  // GCT > 0: the k groups per row (K / 128) known at compile time; the group
+  // loop is then fully unrolled, so every wait on a prefetch is an exact
+  // count instead of the conservative merge LLVM makes at a loop header.
+  constexpr int CG = kDecodeWaves / KSPLIT;
+  constexpr int NGCT = GCT > 0 && GCT % KSPLIT == 0 ? GCT / KSPLIT : 0;
   extern __shared__ __align__(16) unsigned char smem[];
-  constexpr int CG = 4 / KSPLIT;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int cg = wave / KSPLIT, kp = wave % KSPLIT;
-  const int slot_idx = blockIdx.x / a.tiles, tile = blockIdx.x % a.tiles;
-  if (slot_idx >= a.active[0]) return;
-  const int e = a.active[1 + slot_idx];
-  const int r0 = a.offsets[e], ne = a.offsets[e + 1] - r0;
-  const int K = a.K, N = a.N, G = K / 128;
-  const int KC = K < kDecodeKC ? K : kDecodeKC;
-  const int lda = KC + 8;
-  _Float16 *As = (_Float16 *)smem;
-  float *red = (float *)(smem + (size_t)16 * lda * 2);
   const int q = lane >> 4, nl = lane & 15;
-
-  int row[2];
-  if (STAGE == 0) {
-    const int n0 = (tile * CG + cg) * 16;
-    row[0] = n0 + nl;
-    row[1] = a.I + n0 + nl;
-  } else {
-    const int n0 = (tile * CG + cg) * 32;
-    row[0] = n0 + nl;
-    row[1] = n0 + 16 + nl;
-  }
+  const int K = GCT > 0 ? GCT * 128 : a.K, N = a.N, G = K / 128;
+  const int lda = K + 8;                                          // halves
+  _Float16 *As = (_Float16 *)smem;                                // [16][lda]
+  float *red = (float *)(smem + (size_t)16 * lda * 2);            // [KSPLIT-1][CG][512]
   const size_t rowbytes = FMT == FMT_FP8 ? (size_t)K : (size_t)K / 2;
-  const uint8_t *wrow[2];
-  const void *srow[2];
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    wrow[t] = a.w + ((size_t)e * N + row[t]) * rowbytes;
-    if (FMT == FMT_INT4)
-      srow[t] = (const _Float16 *)a.scale + ((size_t)e * N + row[t]) * G;
-    else if (FMT == FMT_FP8)
-      srow[t] = (const float *)a.scale + ((size_t)e * (N / 128) + row[t] / 128) * G;
-    else
-      srow[t] = (const uint8_t *)a.scale + ((size_t)e * N + row[t]) * (K / 16);
-  }
+  const int gb = (kp * G) / KSPLIT;                               // groups [gb, gb + ng)
+  const int ng = NGCT > 0 ? NGCT : ((kp + 1) * G) / KSPLIT - gb;
+  const int n_units = a.active[0] * a.tiles;
 
-  auto load = [&](DecodeFrag<FMT> &f, int g) {
+  for (int unit = blockIdx.x; unit < n_units; unit += gridDim.x) {
+    const int slot_idx = unit / a.tiles, tile = unit - slot_idx * a.tiles;
+    const int e = a.active[1 + slot_idx];
+    const int r0 = a.offsets[e], ne = a.offsets[e + 1] - r0;
+    int row[2];
+    if (STAGE == 0) {
+      const int n0 = (tile * CG + cg) * 16;
+      row[0] = n0 + nl;
+      row[1] = a.I + n0 + nl;
+    } else {
+      const int n0 = (tile * CG + cg) * 32;
+      row[0] = n0 + nl;
+      row[1] = n0 + 16 + nl;
+    }
+    const uint8_t *wrow[2];
+    const void *srow[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      if (FMT == FMT_FP8) {
-        const u4 *p = (const u4 *)(wrow[t] + (size_t)g * 128 + q * 32);
-        f.w[t] = ld_nt(p);
-        f.w2[t] = ld_nt(p + 1);
-        f.s[t] = ((const float *)srow[t])[g];
-      } else {
-        f.w[t] = ld_nt((const u4 *)(wrow[t] + (size_t)g * 64 + q * 16));
-        if (FMT == FMT_INT4)
-          f.s[t] = (float)((const _Float16 *)srow[t])[g];
-        else
-          f.sb[t] = *(const uint16_t *)((const uint8_t *)srow[t] + 8 * g + 2 * q);
-      }
+      wrow[t] = a.w + ((size_t)e * N + row[t]) * rowbytes;
+      if (FMT == FMT_INT4)
+        srow[t] = (const _Float16 *)a.scale + ((size_t)e * N + row[t]) * G;
+      else if (FMT == FMT_FP8)
+        srow[t] = (const float *)a.scale + ((size_t)e * (N / 128) + row[t] / 128) * G;
+      else
+        srow[t] = (const uint8_t *)a.scale + ((size_t)e * N + row[t]) * (K / 16);
     }
-  };
 
-  for (int mc = 0; mc < ne; mc += 16) {
-    f4 acc[2];
-    acc[0] = f4{0.f, 0.f, 0.f, 0.f};
-    acc[1] = acc[0];
-    for (int kc = 0; kc < K; kc += KC) {
-      const int kcn = (K - kc) < KC ? (K - kc) : KC;
-      const int gb = kc / 128 + kp, ge = (kc + kcn) / 128;
-      DecodeFrag<FMT> cur, nxt;
-      if (gb < ge) load(cur, gb);
+    // Groups g and g + 1 (if `two`), issued tile by tile so the two halves of
+    // every 128-byte line of a 4-bit row are requested back to back.
+    auto load_pair = [&](DecodeFrag<FMT> &fa, DecodeFrag<FMT> &fb, int g, bool two) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        if (FMT == FMT_FP8) {
+          const u4 *p = (const u4 *)(wrow[t] + (size_t)g * 128 + q * 32);
+          fa.w[t] = ld_nt(p);
+          fa.w2[t] = ld_nt(p + 1);
+          if (two) {
+            fb.w[t] = ld_nt(p + 8);
+            fb.w2[t] = ld_nt(p + 9);
+          }
+        } else {
+          const u4 *p = (const u4 *)(wrow[t] + (size_t)g * 64 + q * 16);
+          fa.w[t] = ld_nt(p);
+          if (two) fb.w[t] = ld_nt(p + 4);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        if (FMT == FMT_FP8) {
+          fa.s[t] = ((const float *)srow[t])[g];
+          if (two) fb.s[t] = ((const float *)srow[t])[g + 1];
+        } else if (FMT == FMT_INT4) {
+          fa.sb[t] = ((const uint16_t *)srow[t])[g];
+          if (two) fb.sb[t] = ((const uint16_t *)srow[t])[g + 1];
+        } else {
+          fa.sb[t] = *(const uint16_t *)((const uint8_t *)srow[t] + 8 * g + 2 * q);
+          if (two) fb.sb[t] = *(const uint16_t *)((const uint8_t *)srow[t] + 8 * (g + 1) + 2 * q);
+        }
+      }
+    };
+
+    for (int mc = 0; mc < ne; mc += 16) {
+      const int nrows = (ne - mc) < 16 ? (ne - mc) : 16;
+      DecodeFrag<FMT> f[kD];
+#pragma unroll
+      for (int d = 0; d < kD; d += 2)
+        if (d < ng) load_pair(f[d], f[d + 1], gb + d, d + 1 < ng);
+
+      // ---- rows of this expert -> LDS (one pass; gate/up rows arrive in the
+      // INT4 k order already, down rows are permuted here)
       __syncthreads();
-      stage_rows<FMT, STAGE>(As, lda, a, r0 + mc, (ne - mc) < 16 ? (ne - mc) : 16, kc, kcn);
+      {
+        const int cpr = K >> 3;
+        for (int idx = threadIdx.x; idx < nrows * cpr; idx += 64 * kDecodeWaves) {
+          const int m = idx / cpr, c = idx - m * cpr;
+          const int r = r0 + mc + m;
+          const size_t src_row = STAGE == 0 ? (size_t)(a.sorted_slots[r] / a.k) : (size_t)r;
+          u4 v = *(const u4 *)(a.a_src + src_row * K + c * 8);
+          if (FMT == FMT_INT4 && STAGE == 1) v = perm_0415(v);
+          *(u4 *)(As + m * lda + c * 8) = v;
+        }
+      }
       __syncthreads();
-      for (int g = gb; g < ge; g += KSPLIT) {
-        if (g + KSPLIT < ge) load(nxt, g + KSPLIT);
-        const _Float16 *ap = As + nl * lda + (g * 128 - kc) + 32 * q;
+
+      f4 acc[2];
+      acc[0] = f4{0.f, 0.f, 0.f, 0.f};
+      acc[1] = acc[0];
+      const _Float16 *abase = As + nl * lda + 32 * q;
+      auto compute = [&](const DecodeFrag<FMT> &fr, int g) {
+        const _Float16 *ap = abase + g * 128;
         f4 tmp[2];
         tmp[0] = f4{0.f, 0.f, 0.f, 0.f};
         tmp[1] = tmp[0];
@@ -168,12 +199,12 @@ __global__ __launch_bounds__(256) void gemm_decode(GemmArgs a) {
           for (int t = 0; t < 2; ++t) {
             h8 bv;
             if (FMT == FMT_INT4) {
-              bv = unpack_int4(cur.w[t][j]);
+              bv = unpack_int4(fr.w[t][j]);
             } else if (FMT == FMT_FP8) {
-              bv = j < 2 ? unpack_fp8(cur.w[t][2 * j], cur.w[t][2 * j + 1])
-                         : unpack_fp8(cur.w2[t][2 * j - 4], cur.w2[t][2 * j - 3]);
+              bv = j < 2 ? unpack_fp8(fr.w[t][2 * j], fr.w[t][2 * j + 1])
+                         : unpack_fp8(fr.w2[t][2 * j - 4], fr.w2[t][2 * j - 3]);
             } else {
-              bv = unpack_nvfp4(cur.w[t][j], e4m3_to_f16((cur.sb[t] >> (8 * (j >> 1))) & 0xFFu));
+              bv = unpack_nvfp4(fr.w[t][j], e4m3_to_f16((fr.sb[t] >> (8 * (j >> 1))) & 0xFFu));
             }
             if (FMT == FMT_NVFP4)
               acc[t] = mfma16(av, bv, acc[t]);
@@ -181,47 +212,89 @@ __global__ __launch_bounds__(256) void gemm_decode(GemmArgs a) {
               tmp[t] = mfma16(av, bv, tmp[t]);
           }
         }
-        if (FMT != FMT_NVFP4) {
+        if (FMT == FMT_INT4) {
 #pragma unroll
-          for (int t = 0; t < 2; ++t) acc[t] += tmp[t] * cur.s[t];
+          for (int t = 0; t < 2; ++t)
+            acc[t] += tmp[t] * (float)__builtin_bit_cast(_Float16, (uint16_t)fr.sb[t]);
+        } else if (FMT == FMT_FP8) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t) acc[t] += tmp[t] * fr.s[t];
         }
-        cur = nxt;
-      }
-    }
-    if (KSPLIT > 1) {
-      if (kp > 0) {
-        float *rb = red + (size_t)((kp - 1) * CG + cg) * 512;
+      };
+
+      if constexpr (NGCT > 0) {
+        // fully unrolled ring of kD groups
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int i = 0; i < NGCT; i += 2) {
+          compute(f[i % kD], gb + i);
+          if (i + 1 < NGCT) compute(f[(i + 1) % kD], gb + i + 1);
+          if (i + kD < NGCT) {
+            load_pair(f[i % kD], f[(i + 1) % kD], gb + i + kD, i + kD + 1 < NGCT);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      } else {
+        // steady state: every computed pair of groups is replaced by the pair
+        // kD ahead (unconditional: no register merge waits on a load)
+        int i = 0;
+        for (; i + 2 * kD <= ng; i += kD) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) rb[(t * 4 + i) * 64 + lane] = acc[t][i];
+          for (int d = 0; d < kD; d += 2) {
+            compute(f[d], gb + i + d);
+            compute(f[d + 1], gb + i + d + 1);
+            load_pair(f[d], f[d + 1], gb + i + d + kD, true);
+            // keep the prefetch here: sunk to the loop end, it would become
+            // the youngest load and the next wait would drain the window
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        // tail: fewer than 2 kD groups left
+#pragma unroll
+        for (int d = 0; d < kD; d += 2) {
+          if (i + d < ng) compute(f[d], gb + i + d);
+          if (i + d + 1 < ng) compute(f[d + 1], gb + i + d + 1);
+          if (i + d + kD < ng) load_pair(f[d], f[d + 1], gb + i + d + kD, i + d + kD + 1 < ng);
+        }
+#pragma unroll
+        for (int d = 0; d < kD; ++d)
+          if (i + kD + d < ng) compute(f[d], gb + i + kD + d);
       }
-      __syncthreads();
-      if (kp == 0) {
-        for (int p = 1; p < KSPLIT; ++p) {
-          const float *rb = red + (size_t)((p - 1) * CG + cg) * 512;
+
+      if (KSPLIT > 1) {
+        if (kp > 0) {
+          float *rb = red + (size_t)((kp - 1) * CG + cg) * 512;
 #pragma unroll
           for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[t][i] += rb[(t * 4 + i) * 64 + lane];
+            for (int ii = 0; ii < 4; ++ii) rb[(t * 4 + ii) * 64 + lane] = acc[t][ii];
+        }
+        __syncthreads();
+        if (kp == 0) {
+          for (int p = 1; p < KSPLIT; ++p) {
+            const float *rb = red + (size_t)((p - 1) * CG + cg) * 512;
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+              for (int ii = 0; ii < 4; ++ii) acc[t][ii] += rb[(t * 4 + ii) * 64 + lane];
+          }
         }
       }
-    }
-    if (kp == 0) {
-      const float ginv = FMT == FMT_NVFP4 ? 1.0f / a.gscale[e] : 1.0f;
+      if (kp == 0) {
+        const float ginv = FMT == FMT_NVFP4 ? 1.0f / a.gscale[e] : 1.0f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = mc + 4 * q + i;
-        if (m >= ne) continue;
-        const int r = r0 + m;
-        const int slot = a.sorted_slots[r];
-        if (STAGE == 0) {
-          const float rs = a.rowscale[slot / a.k] * ginv;
-          store_h(a, r, row[0], acc[0][i] * rs, acc[1][i] * rs);
-        } else {
-          const float wt = a.topk_w[slot] * ginv;
-          a.partial[(size_t)slot * a.H + row[0]] = acc[0][i] * wt;
-          a.partial[(size_t)slot * a.H + row[1]] = acc[1][i] * wt;
+        for (int ii = 0; ii < 4; ++ii) {
+          const int m = 4 * q + ii;
+          if (m >= nrows) continue;
+          const int r = r0 + mc + m;
+          const int slot = a.sorted_slots[r];
+          if (STAGE == 0) {
+            const float sc = a.rowscale[slot / a.k] * ginv;
+            store_h(a, r, row[0], acc[0][ii] * sc, acc[1][ii] * sc);
+          } else {
+            const float wt = a.topk_w[slot] * ginv;
+            a.partial[(size_t)slot * a.H + row[0]] = acc[0][ii] * wt;
+            a.partial[(size_t)slot * a.H + row[1]] = acc[1][ii] * wt;
+          }
         }
       }
     }
@@ -320,7 +393,7 @@ __global__ __launch_bounds__(256, 2) void gemm_prefill(GemmArgs a) {
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
       u4 v = areg[p];
-      if (FMT == FMT_INT4) v = perm_0415(v);
+      if (FMT == FMT_INT4 && STAGE == 1) v = perm_0415(v);  // gate/up rows come INT4-ordered
       *(u4 *)(As + (p * 16 + (tid >> 4)) * kLD + (tid & 15) * 8) = v;
     }
     _Float16 *bdst = Bs + brow * kLD + bhalf * 64;
@@ -336,7 +409,7 @@ __global__ __launch_bounds__(256, 2) void gemm_prefill(GemmArgs a) {
       *(h8 *)(bdst + c * 8) = v;
     }
     __syncthreads();
-    if (ks + 1 < nK) gload(ks + 1);
+    // scales of this k step first: the prefetch below retires after them
     float sc[2] = {1.f, 1.f};
     if (FMT == FMT_INT4) {
 #pragma unroll
@@ -347,6 +420,7 @@ __global__ __launch_bounds__(256, 2) void gemm_prefill(GemmArgs a) {
       for (int tn = 0; tn < 2; ++tn)
         sc[tn] = ((const float *)a.scale)[((size_t)e * (N / 128) + lrow[tn] / 128) * G + ks];
     }
+    if (ks + 1 < nK) gload(ks + 1);
     f16v tmp[2][2];
     if (FMT != FMT_NVFP4) {
 #pragma unroll
@@ -510,34 +584,80 @@ static GemmArgs make_args(const LayerDims &L, const FwdPtrs &P, const Workspace 
   return a;
 }
 
+static int g_num_cus = 0;
+
+static int num_cus() {
+  if (g_num_cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      g_num_cus = n;
+    else
+      g_num_cus = 256;
+  }
+  return g_num_cus;
+}
+
+template <int FMT, int STAGE, int KSPLIT, int GCT>
+static hipError_t run_decode_g(GemmArgs a, int slots, hipStream_t s) {
+  constexpr int CG = kDecodeWaves / KSPLIT;
+  a.tiles = STAGE == 0 ? a.I / (16 * CG) : a.H / (32 * CG);
+  const size_t lds = (size_t)16 * (a.K + 8) * 2 + (size_t)(KSPLIT - 1) * CG * 512 * 4;
+  // persistent grid: as many blocks as are resident at once (from the
+  // kernel's registers and LDS), never more than the number of units
+  static int per_cu = 0;
+  static size_t per_cu_lds = 0;
+  if (per_cu == 0 || per_cu_lds != lds) {
+    (void)hipFuncSetAttribute((const void *)gemm_decode<FMT, STAGE, KSPLIT, GCT>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_decode<FMT, STAGE, KSPLIT, GCT>,
+                                                     64 * kDecodeWaves, lds) != hipSuccess || n < 1)
+      n = 1;
+    per_cu = n;
+    per_cu_lds = lds;
+  }
+  const long units = (long)slots * a.tiles;
+  const long grid = std::min<long>(units, (long)num_cus() * per_cu);
+  hipLaunchKernelGGL((gemm_decode<FMT, STAGE, KSPLIT, GCT>), dim3((unsigned)grid),
+                     dim3(64 * kDecodeWaves), lds, s, a);
+  return hipGetLastError();
+}
+
 template <int FMT, int STAGE, int KSPLIT>
 static hipError_t run_decode(GemmArgs a, int slots, hipStream_t s) {
-  constexpr int CG = 4 / KSPLIT;
-  a.tiles = STAGE == 0 ? a.I / (16 * CG) : a.H / (32 * CG);
-  const int KC = a.K < kDecodeKC ? a.K : kDecodeKC;
-  const size_t lds = (size_t)16 * (KC + 8) * 2 + (size_t)(KSPLIT - 1) * CG * 512 * 4;
-  static bool attr_set = false;
-  if (!attr_set) {
-    (void)hipFuncSetAttribute((const void *)gemm_decode<FMT, STAGE, KSPLIT>,
-                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    attr_set = true;
+  switch (a.K / 128) {  // k groups per row; unrolled variants for common sizes
+    case 4: return run_decode_g<FMT, STAGE, KSPLIT, 4>(a, slots, s);
+    case 6: return run_decode_g<FMT, STAGE, KSPLIT, 6>(a, slots, s);
+    case 8: return run_decode_g<FMT, STAGE, KSPLIT, 8>(a, slots, s);
+    case 12: return run_decode_g<FMT, STAGE, KSPLIT, 12>(a, slots, s);
+    case 16: return run_decode_g<FMT, STAGE, KSPLIT, 16>(a, slots, s);
+    case 32: return run_decode_g<FMT, STAGE, KSPLIT, 32>(a, slots, s);
+    default: return run_decode_g<FMT, STAGE, KSPLIT, 0>(a, slots, s);
   }
-  hipLaunchKernelGGL((gemm_decode<FMT, STAGE, KSPLIT>), dim3(slots * a.tiles), dim3(256), lds, s, a);
-  return hipGetLastError();
 }
 
 template <int FMT, int STAGE>
 static hipError_t run_decode_ks(GemmArgs a, int slots, hipStream_t s) {
-  // split k across the waves of a block when there are too few column tiles
-  // to give every SIMD work
-  const long cols = STAGE == 0 ? (long)a.I / 16 : (long)a.H / 32;
-  const long waves = (long)slots * cols;
-  const int groups = a.K / 128;
-  if (waves < 1024 && groups >= 4)
-    return run_decode<FMT, STAGE, 4>(a, slots, s);
-  if (waves < 2048 && groups >= 2)
-    return run_decode<FMT, STAGE, 2>(a, slots, s);
-  return run_decode<FMT, STAGE, 1>(a, slots, s);
+  // Smallest k split whose column groups tile the expert exactly and whose
+  // wave-tasks (tile pair x k split) cover the resident waves about twice.
+  const int cols = STAGE == 0 ? a.I / 16 : a.H / 32;  // tile pairs per expert
+  const long waves = (long)num_cus() * 16;
+  const int ksplits[4] = {1, 2, 4, 8};
+  int pick = 8;
+  for (int ks : ksplits) {
+    if (cols % (kDecodeWaves / ks) != 0) continue;
+    if ((long)slots * cols * ks >= 2 * waves) {
+      pick = ks;
+      break;
+    }
+  }
+  switch (pick) {
+    case 1: return run_decode<FMT, STAGE, 1>(a, slots, s);
+    case 2: return run_decode<FMT, STAGE, 2>(a, slots, s);
+    case 4: return run_decode<FMT, STAGE, 4>(a, slots, s);
+    default: return run_decode<FMT, STAGE, 8>(a, slots, s);
+  }
 }
 
 template <int FMT, int STAGE>
@@ -608,8 +728,10 @@ hipError_t launch_dequantize(const LayerDims &L, int which, int expert, float *o
   return hipGetLastError();
 }
 
-bool use_decode_path(int64_t T, int E, int k) {
+bool use_decode_path(int64_t T, int E, int k, int H, int I) {
   // mean rows per expert <= 16: one 16-row MFMA block per expert on average
+  (void)H;
+  (void)I;
   return T * k <= (int64_t)16 * E;
 }
 

@@ -17,7 +17,7 @@ struct Workspace {
   size_t mtile;                // int32 [E+1]: prefix of ceil(n_e / kPrefillBM)
   size_t sorted_slots;         // int32 [R]: slot t*k+j of each grouped row
   size_t inv_pos;              // int32 [R]
-  size_t x16;                  // fp16 [T, H]: hidden rows scaled by 2^-s_t
+  size_t x16;                  // fp16 [T, H]: hidden rows scaled by 2^-s_t (INT4: k order of the unpack)
   size_t rowscale;             // float [T]: 2^s_t
   size_t h;                    // fp16 [R, I]
   size_t partial;              // float [R, H]: routing-weighted expert outputs per slot
@@ -59,6 +59,6 @@ hipError_t launch_combine(const LayerDims &L, const FwdPtrs &P, const Workspace 
 hipError_t launch_dequantize(const LayerDims &L, int which, int expert, float *out, hipStream_t s);
 
 // Rows per expert at or below which the decode (weight-streaming) GEMMs run.
-bool use_decode_path(int64_t T, int E, int k);
+bool use_decode_path(int64_t T, int E, int k, int H, int I);
 
 }  // namespace mq

@@ -195,7 +195,7 @@ mq_status moe_quant_forward(const mq_layer *L, const void *router_logits, int32_
     P.p_h = probe->h;
   }
   hipStream_t s = (hipStream_t)stream;
-  const bool decode = mq::use_decode_path(num_tokens, D.E, D.k);
+  const bool decode = mq::use_decode_path(num_tokens, D.E, D.k, D.H, D.I);
   auto ev = [&](int stage, int after) {
     if (probe && probe->events[2 * stage + after])
       (void)hipEventRecord((hipEvent_t)probe->events[2 * stage + after], s);

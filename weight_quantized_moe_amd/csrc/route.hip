@@ -6,6 +6,10 @@
 // over the selected k.  The router stays an unquantized BF16 layer on the
 // model cards ("clef-omni-int4" card, section "Recipe": ignore_layers =
 // mlp.gate); its logits arrive as an input.
+//
+// Top-k runs on a group of 16 lanes per token (4 tokens per wave): every lane
+// holds E/16 keys, and each of the k rounds is a local maximum plus a 4-step
+// DPP all-reduce inside the 16-lane row.
 #include "device.h"
 #include "internal.h"
 
@@ -22,37 +26,59 @@ __device__ __forceinline__ float from_ordered_key(uint32_t o) {
   return __builtin_bit_cast(float, b);
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  uint32_t lo = __shfl_xor((uint32_t)v, m, 64);
-  uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
-  return ((uint64_t)hi << 32) | lo;
+// DPP lane moves inside a 16-lane row (every lane has a valid source).
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kCtrl, 0xF, 0xF, false);
+}
+constexpr int kXor1 = 0xB1, kXor2 = 0x4E, kHalfMirror = 0x141, kMirror = 0x140;
+
+template <int kCtrl>
+__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+  return ((uint64_t)dpp<kCtrl>((uint32_t)(v >> 32)) << 32) | dpp<kCtrl>((uint32_t)v);
+}
+__device__ __forceinline__ uint64_t max16_u64(uint64_t v) {
+  uint64_t o;
+  o = dpp64<kXor1>(v); v = o > v ? o : v;
+  o = dpp64<kXor2>(v); v = o > v ? o : v;
+  o = dpp64<kHalfMirror>(v); v = o > v ? o : v;
+  o = dpp64<kMirror>(v); v = o > v ? o : v;
+  return v;
+}
+template <int kCtrl>
+__device__ __forceinline__ float dppf(float v) {
+  return __builtin_bit_cast(float, dpp<kCtrl>(__builtin_bit_cast(uint32_t, v)));
+}
+__device__ __forceinline__ float sum16(float v) {
+  v += dppf<kXor1>(v);
+  v += dppf<kXor2>(v);
+  v += dppf<kHalfMirror>(v);
+  v += dppf<kMirror>(v);
+  return v;
+}
+__device__ __forceinline__ float max16f(float v) {
+  v = fmaxf(v, dppf<kXor1>(v));
+  v = fmaxf(v, dppf<kXor2>(v));
+  v = fmaxf(v, dppf<kHalfMirror>(v));
+  v = fmaxf(v, dppf<kMirror>(v));
+  return v;
 }
 
-// One wave per token.  Keys pack (ordered logit, ~expert id) so that the wave
-// maximum is the largest logit with the lowest id; a selected key is replaced
-// by 0, below every real key (the id half of a real key is never 0 because
-// E <= 512), so the k winners are always k distinct valid experts.
-template <bool kBf16Logits>
-__global__ __launch_bounds__(256) void route_kernel(const void *__restrict__ logits,
-                                                    const uint16_t *__restrict__ hidden, int T,
-                                                    int E, int H, int k, int32_t *__restrict__ ids,
-                                                    float *__restrict__ wts,
-                                                    _Float16 *__restrict__ x16,
-                                                    float *__restrict__ rowscale,
-                                                    uint32_t *__restrict__ flags,
-                                                    int32_t *__restrict__ p_ids,
-                                                    float *__restrict__ p_w) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + wave;
-  if (blockIdx.x == 0 && threadIdx.x == 0) flags[0] = 0u;
-  if (t >= T) return;
-
-  // ---- top-k over the E logits of token t
-  constexpr int kPer = kMaxExperts / 64;
+// Top-k + softmax of token t on the 16 lanes of one DPP row (li = lane % 16).
+// Keys pack (ordered logit, ~expert id): the row maximum is the largest logit
+// with the lowest id.  A selected key becomes 0, below every real key (the id
+// half of a real key is never 0 since E <= 512), so the k winners are always k
+// distinct valid experts.  Results go to ids/wts (global) and, if given, to
+// sm_ids (shared, [k]).
+template <int kPer, bool kBf16Logits>
+__device__ __forceinline__ void topk16(const void *__restrict__ logits, int t, int E, int k, int li,
+                                       int32_t *__restrict__ ids, float *__restrict__ wts,
+                                       int32_t *__restrict__ p_ids, float *__restrict__ p_w,
+                                       int32_t *sm_ids) {
   uint64_t key[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    const int e = lane + 64 * i;
+    const int e = li + 16 * i;
     key[i] = 0;
     if (e < E) {
       float v;
@@ -63,86 +89,225 @@ __global__ __launch_bounds__(256) void route_kernel(const void *__restrict__ log
       key[i] = ((uint64_t)ordered_key(v) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
     }
   }
-  float my_v = 0.f;
-  int my_id = 0;
-  float v_max = 0.f;
-  for (int j = 0; j < k; ++j) {   // k <= 64: lane j keeps slot j
-    uint64_t best = 0;
+  float sv[4] = {0.f, 0.f, 0.f, 0.f};  // slot j = li + 16 s held by this lane
+  int si[4] = {0, 0, 0, 0};
+  float vmax = 0.f;
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = key[0];
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) best = key[i] > best ? key[i] : best;
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      const uint64_t o = shfl_xor_u64(best, m);
-      best = o > best ? o : best;
-    }
+    for (int i = 1; i < kPer; ++i) best = key[i] > best ? key[i] : best;
+    best = max16_u64(best);
     const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
     const float v = from_ordered_key((uint32_t)(best >> 32));
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
-      if (lane + 64 * i == e) key[i] = 0;
-    if (j == 0) v_max = v;
-    if (lane == j) {
-      my_v = v;
-      my_id = e;
+      if (li + 16 * i == e) key[i] = 0;
+    if (j == 0) vmax = v;
+    if ((j & 15) == li) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        if ((j >> 4) == s) { sv[s] = v; si[s] = e; }
     }
   }
-  // softmax over the k selected logits
-  const float p = lane < k ? expf(my_v - v_max) : 0.f;
-  float sum = p;
+  float p[4], sum = 0.f;
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, 64);
-  if (lane < k) {
-    const float w = p / sum;
-    ids[(size_t)t * k + lane] = my_id;
-    wts[(size_t)t * k + lane] = w;
-    if (p_ids) p_ids[(size_t)t * k + lane] = my_id;
-    if (p_w) p_w[(size_t)t * k + lane] = w;
+  for (int s = 0; s < 4; ++s) {
+    p[s] = (li + 16 * s < k) ? expf(sv[s] - vmax) : 0.f;
+    sum += p[s];
   }
+  sum = sum16(sum);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int j = li + 16 * s;
+    if (j < k) {
+      const float w = p[s] / sum;
+      ids[(size_t)t * k + j] = si[s];
+      wts[(size_t)t * k + j] = w;
+      if (p_ids) p_ids[(size_t)t * k + j] = si[s];
+      if (p_w) p_w[(size_t)t * k + j] = w;
+      if (sm_ids) sm_ids[j] = si[s];
+    }
+  }
+}
 
-  // ---- hidden row -> FP16 scaled by a power of two.  With max|x| mapped into
-  // [2^14, 2^15) every BF16 value of the row above max * 2^-31 converts to FP16
-  // exactly (BF16 has 8 significant bits, FP16 11, and the FP16 subnormal step
-  // there is 2^-24); smaller entries round with an absolute error below
-  // max * 2^-39.  The GEMM multiplies its result rows back by 2^s.
-  const uint16_t *xr = hidden + (size_t)t * H;
-  float m = 0.f;
-  for (int c = lane * 8; c < H; c += 512) {
-    const u4 v = *(const u4 *)(xr + c);
+// Hidden row of token t -> FP16 scaled by a power of two, on one 16-lane row.
+// With kPermInt4 every 8 consecutive values are stored in the k order of the
+// INT4 unpack ({0,4,1,5,2,6,3,7}, see unpack_int4), so INT4 GEMMs use the rows
+// as they are.
+// With max|x| mapped into [2^14, 2^15), every BF16 value of the row above
+// max * 2^-31 converts to FP16 exactly (BF16 has 8 significant bits, FP16 11,
+// and the FP16 subnormal step there is 2^-24); smaller entries round with an
+// absolute error below max * 2^-39.  The GEMM multiplies its rows back by 2^s.
+// Hidden rows of the wave's 4 tokens -> FP16 scaled by a power of two each,
+// using all 64 lanes per row.  With max|x| mapped into [2^14, 2^15), every BF16
+// value of the row above max * 2^-31 converts to FP16 exactly (BF16 has 8
+// significant bits, FP16 11, and the FP16 subnormal step there is 2^-24);
+// smaller entries round with an absolute error below max * 2^-39.  The GEMMs
+// multiply their result rows back by 2^s.  With kPermInt4 every 8 consecutive
+// values are stored in the k order of the INT4 unpack ({0,4,1,5,2,6,3,7}, see
+// unpack_int4), so INT4 GEMMs use the rows as they are.  Loads of the 4 rows
+// are issued together (kChunk per row per round trip).
+template <bool kPermInt4>
+__device__ __forceinline__ void rows_to_f16(const uint16_t *__restrict__ hidden, int t0, int T,
+                                            int H, int lane, _Float16 *__restrict__ x16,
+                                            float *__restrict__ rowscale) {
+  constexpr int kChunk = 4;  // u4 per lane per row per round trip (2048 values)
+  float m[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int c0 = lane * 8; c0 < H; c0 += 512 * kChunk) {
+    u4 v[4][kChunk];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      m = fmaxf(m, fabsf(bf16_to_f32(v[q] & 0xFFFFu)));
-      m = fmaxf(m, fabsf(bf16_to_f32(v[q] >> 16)));
-    }
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u)
+        if (t0 + r < T && c0 + 512 * u < H)
+          v[r][u] = *(const u4 *)(hidden + (size_t)(t0 + r) * H + c0 + 512 * u);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u)
+        if (t0 + r < T && c0 + 512 * u < H) m[r] = absmax_bf16x8(v[r][u], m[r]);
   }
 #pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
-  int sh = 0;
-  if (m > 0.f) {
-    const int ex = (int)((__builtin_bit_cast(uint32_t, m) >> 23) & 0xFF) - 127;
-    sh = ex - 14;
-    sh = sh < -120 ? -120 : (sh > 120 ? 120 : sh);
+  for (int r = 0; r < 4; ++r) {
+    m[r] = max16f(m[r]);
+    m[r] = fmaxf(m[r], __shfl_xor(m[r], 16, 64));
+    m[r] = fmaxf(m[r], __shfl_xor(m[r], 32, 64));
   }
-  const float down = __builtin_bit_cast(float, (uint32_t)(127 - sh) << 23);
-  if (lane == 0) rowscale[t] = __builtin_bit_cast(float, (uint32_t)(127 + sh) << 23);
-  _Float16 *xo = x16 + (size_t)t * H;
-  for (int c = lane * 8; c < H; c += 512) {
-    const u4 v = *(const u4 *)(xr + c);
-    u4 o;
+  float down[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      h2 hh = {(_Float16)(bf16_to_f32(v[q] & 0xFFFFu) * down),
-               (_Float16)(bf16_to_f32(v[q] >> 16) * down)};
-      o[q] = as_u32(hh);
+  for (int r = 0; r < 4; ++r) {
+    const int sh = row_shift(m[r]);
+    down[r] = pow2f(-sh);
+    if (lane == 0 && t0 + r < T) rowscale[t0 + r] = pow2f(sh);
+  }
+  for (int c0 = lane * 8; c0 < H; c0 += 512 * kChunk) {
+    u4 v[4][kChunk];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u)
+        if (t0 + r < T && c0 + 512 * u < H)
+          v[r][u] = *(const u4 *)(hidden + (size_t)(t0 + r) * H + c0 + 512 * u);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u)
+        if (t0 + r < T && c0 + 512 * u < H) {
+          const u4 o = bf16x8_to_f16x8(v[r][u], down[r]);
+          *(u4 *)(x16 + (size_t)(t0 + r) * H + c0 + 512 * u) = kPermInt4 ? perm_0415(o) : o;
+        }
+  }
+}
+
+// General-T routing: 16 tokens per block of 256 threads.  Also zeroes the
+// flags word and, for the prefill path, stages the hidden rows in FP16.
+template <int kPer, bool kBf16Logits, bool kPermInt4>
+__global__ __launch_bounds__(256) void route_kernel(const void *__restrict__ logits,
+                                                    const uint16_t *__restrict__ hidden, int T,
+                                                    int E, int H, int k, int32_t *__restrict__ ids,
+                                                    float *__restrict__ wts,
+                                                    _Float16 *__restrict__ x16,
+                                                    float *__restrict__ rowscale,
+                                                    uint32_t *__restrict__ flags,
+                                                    int32_t *__restrict__ p_ids,
+                                                    float *__restrict__ p_w) {
+  const int lane = threadIdx.x & 63, li = lane & 15;
+  const int t = blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int t0 = blockIdx.x * 16 + (threadIdx.x >> 6) * 4;  // first token of this wave
+  if (blockIdx.x == 0 && threadIdx.x == 0) flags[0] = 0u;
+  if (t0 >= T) return;
+  if (t < T) topk16<kPer, kBf16Logits>(logits, t, E, k, li, ids, wts, p_ids, p_w, nullptr);
+  rows_to_f16<kPermInt4>(hidden, t0, T, H, lane, x16, rowscale);
+}
+
+// ---------------------------------------------------------------------------
+// Exclusive scan of cnt[0..E) (E <= 512) by one wave; also the prefill
+// M-tile counts and the active-expert list.  Writes offsets[E+1], mtile[E+1],
+// active[1+E] and, if given, p_offsets.  Lanes hold 8 consecutive experts.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void scan_experts_wave(const int32_t *cnt, int E, int lane,
+                                                  int32_t *__restrict__ offsets,
+                                                  int32_t *__restrict__ mtile,
+                                                  int32_t *__restrict__ active,
+                                                  int32_t *__restrict__ p_offsets,
+                                                  int32_t *cursor) {
+  int c[8], s0 = 0, s1 = 0, s2 = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int e = lane * 8 + i;
+    c[i] = e < E ? cnt[e] : 0;
+    s0 += c[i];
+    s1 += (c[i] + kPrefillBM - 1) / kPrefillBM;
+    s2 += c[i] > 0;
+  }
+  int i0 = s0, i1 = s1, i2 = s2;  // inclusive wave scans
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int a0 = __shfl_up(i0, d, 64), a1 = __shfl_up(i1, d, 64), a2 = __shfl_up(i2, d, 64);
+    if (lane >= d) { i0 += a0; i1 += a1; i2 += a2; }
+  }
+  int r0 = i0 - s0, r1 = i1 - s1, r2 = i2 - s2;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int e = lane * 8 + i;
+    if (e < E) {
+      offsets[e] = r0;
+      if (p_offsets) p_offsets[e] = r0;
+      if (cursor) cursor[e] = r0;
+      mtile[e] = r1;
+      if (c[i] > 0) active[1 + r2] = e;
     }
-    *(u4 *)(xo + c) = o;
+    r0 += c[i];
+    r1 += (c[i] + kPrefillBM - 1) / kPrefillBM;
+    r2 += c[i] > 0;
+  }
+  if (lane == 63) {
+    offsets[E] = i0;
+    if (p_offsets) p_offsets[E] = i0;
+    mtile[E] = i1;
+    active[0] = i2;
   }
 }
 
 // ---------------------------------------------------------------------------
-// Stable grouping by expert, one workgroup of 1024 threads.
-//   1. per-expert counts (LDS atomics);
-//   2. exclusive scans: row offsets, prefill M-tile offsets, active experts;
-//   3. tokens in chunks of 1024 (16 waves x 64): each wave records, per expert,
+// T <= 64: grouping in one workgroup.  One 64-bit token mask per expert gives
+// the counts (popcount) and the stable rank of every token inside its expert
+// (popcount of the mask bits below it).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void permute_small_kernel(
+    const int32_t *__restrict__ ids, int T, int E, int k, int32_t *__restrict__ offsets,
+    int32_t *__restrict__ mtile, int32_t *__restrict__ active, int32_t *__restrict__ sorted_slots,
+    int32_t *__restrict__ inv_pos, int32_t *__restrict__ p_offsets,
+    int32_t *__restrict__ p_sorted_tok, int32_t *__restrict__ p_inv) {
+  __shared__ int32_t sm_ids[64 * 64];
+  __shared__ uint64_t mask[kMaxExperts];
+  __shared__ int32_t cnt[kMaxExperts];
+  __shared__ int32_t off[kMaxExperts];
+  const int tid = threadIdx.x, lane = tid & 63;
+  for (int e = tid; e < E; e += 1024) mask[e] = 0ull;
+  for (int i = tid; i < T * k; i += 1024) sm_ids[i] = ids[i];
+  __syncthreads();
+  for (int i = tid; i < T * k; i += 1024) atomicOr(&mask[sm_ids[i]], 1ull << (i / k));
+  __syncthreads();
+  for (int e = tid; e < E; e += 1024) cnt[e] = __popcll(mask[e]);
+  __syncthreads();
+  if (tid < 64) scan_experts_wave(cnt, E, lane, offsets, mtile, active, p_offsets, off);
+  __syncthreads();
+  for (int i = tid; i < T * k; i += 1024) {
+    const int tt = i / k, e = sm_ids[i];
+    const uint64_t below = tt == 0 ? 0ull : (~0ull >> (64 - tt));
+    const int pos = off[e] + __popcll(mask[e] & below);
+    sorted_slots[pos] = i;
+    inv_pos[i] = pos;
+    if (p_sorted_tok) p_sorted_tok[pos] = tt;
+    if (p_inv) p_inv[i] = pos;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Stable grouping by expert for any T, one workgroup of 1024 threads.
+//   1. per-expert counts (LDS atomics) and the exclusive scans;
+//   2. tokens in chunks of 1024 (16 waves x 64): each wave records, per expert,
 //      the 64-bit mask of its lanes routed there; ranks inside the chunk are
 //      (rows of earlier waves) + popcount(mask & lanes below me), which keeps
 //      token order inside every expert.
@@ -157,7 +322,6 @@ __global__ __launch_bounds__(1024) void permute_kernel(
   int32_t *base = (int32_t *)(mask + 16 * E);              // [16][E]
   int32_t *cnt = base + 16 * E;                            // [E]
   int32_t *cursor = cnt + E;                               // [E]
-  int32_t *scan = cursor + E;                              // [3][1024] scratch
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int R = T * k;
@@ -165,41 +329,7 @@ __global__ __launch_bounds__(1024) void permute_kernel(
   __syncthreads();
   for (int i = tid; i < R; i += 1024) atomicAdd(&cnt[ids[i]], 1);
   __syncthreads();
-
-  // inclusive Hillis-Steele scans of (count, m-tiles, active flag); E <= 1024
-  int v0 = 0, v1 = 0, v2 = 0;
-  if (tid < E) {
-    v0 = cnt[tid];
-    v1 = (v0 + kPrefillBM - 1) / kPrefillBM;
-    v2 = v0 > 0 ? 1 : 0;
-  }
-  for (int d = 1; d < 1024; d <<= 1) {
-    scan[tid] = v0;
-    scan[1024 + tid] = v1;
-    scan[2048 + tid] = v2;
-    __syncthreads();
-    if (tid >= d) {
-      v0 += scan[tid - d];
-      v1 += scan[1024 + tid - d];
-      v2 += scan[2048 + tid - d];
-    }
-    __syncthreads();
-  }
-  if (tid < E) {
-    const int c = cnt[tid];
-    const int ex0 = v0 - c;
-    offsets[tid] = ex0;
-    if (p_offsets) p_offsets[tid] = ex0;
-    mtile[tid] = v1 - (c + kPrefillBM - 1) / kPrefillBM;
-    if (c > 0) active[1 + (v2 - 1)] = tid;
-    cursor[tid] = ex0;
-    if (tid == E - 1) {
-      offsets[E] = v0;
-      if (p_offsets) p_offsets[E] = v0;
-      mtile[E] = v1;
-      active[0] = v2;
-    }
-  }
+  if (tid < 64) scan_experts_wave(cnt, E, lane, offsets, mtile, active, p_offsets, cursor);
   __syncthreads();
 
   for (int c0 = 0; c0 < T; c0 += 1024) {
@@ -235,25 +365,52 @@ __global__ __launch_bounds__(1024) void permute_kernel(
   }
 }
 
-hipError_t launch_route(const LayerDims &L, const FwdPtrs &P, const Workspace &W, hipStream_t s) {
+// ---------------------------------------------------------------------------
+template <int kPer, bool kBf16, bool kPerm>
+static hipError_t route_dispatch(const LayerDims &L, const FwdPtrs &P, const Workspace &W,
+                                 hipStream_t s) {
   char *ws = P.ws;
-  dim3 grid((P.T + 3) / 4), block(256);
-  if (P.logits_bf16)
-    hipLaunchKernelGGL(route_kernel<true>, grid, block, 0, s, P.logits, P.hidden, P.T, L.E, L.H,
-                       L.k, (int32_t *)(ws + W.topk_ids), (float *)(ws + W.topk_w),
-                       (_Float16 *)(ws + W.x16), (float *)(ws + W.rowscale),
-                       (uint32_t *)(ws + W.flags), P.p_ids, P.p_w);
-  else
-    hipLaunchKernelGGL(route_kernel<false>, grid, block, 0, s, P.logits, P.hidden, P.T, L.E, L.H,
-                       L.k, (int32_t *)(ws + W.topk_ids), (float *)(ws + W.topk_w),
-                       (_Float16 *)(ws + W.x16), (float *)(ws + W.rowscale),
-                       (uint32_t *)(ws + W.flags), P.p_ids, P.p_w);
+  hipLaunchKernelGGL((route_kernel<kPer, kBf16, kPerm>), dim3((P.T + 15) / 16), dim3(256), 0, s,
+                     P.logits, P.hidden, P.T, L.E, L.H, L.k, (int32_t *)(ws + W.topk_ids),
+                     (float *)(ws + W.topk_w), (_Float16 *)(ws + W.x16), (float *)(ws + W.rowscale),
+                     (uint32_t *)(ws + W.flags), P.p_ids, P.p_w);
   return hipGetLastError();
+}
+
+template <int kPer>
+static hipError_t route_dispatch2(const LayerDims &L, const FwdPtrs &P, const Workspace &W,
+                                  hipStream_t s) {
+  const bool perm = L.fmt == FMT_INT4;
+  if (P.logits_bf16)
+    return perm ? route_dispatch<kPer, true, true>(L, P, W, s)
+                : route_dispatch<kPer, true, false>(L, P, W, s);
+  return perm ? route_dispatch<kPer, false, true>(L, P, W, s)
+              : route_dispatch<kPer, false, false>(L, P, W, s);
+}
+
+hipError_t launch_route(const LayerDims &L, const FwdPtrs &P, const Workspace &W, hipStream_t s) {
+  if (L.E <= 128) return route_dispatch2<8>(L, P, W, s);
+  if (L.E <= 256) return route_dispatch2<16>(L, P, W, s);
+  return route_dispatch2<32>(L, P, W, s);
 }
 
 hipError_t launch_permute(const LayerDims &L, const FwdPtrs &P, const Workspace &W, hipStream_t s) {
   char *ws = P.ws;
-  const size_t lds = (size_t)16 * L.E * 8 + (size_t)16 * L.E * 4 + 2 * (size_t)L.E * 4 + 3 * 1024 * 4;
+  if (P.T <= 64) {
+    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(1024), 0, s,
+                       (const int32_t *)(ws + W.topk_ids), P.T, L.E, L.k,
+                       (int32_t *)(ws + W.offsets), (int32_t *)(ws + W.mtile),
+                       (int32_t *)(ws + W.active), (int32_t *)(ws + W.sorted_slots),
+                       (int32_t *)(ws + W.inv_pos), P.p_offsets, P.p_sorted_tok, P.p_inv);
+    return hipGetLastError();
+  }
+  const size_t lds = (size_t)16 * L.E * 8 + (size_t)16 * L.E * 4 + 2 * (size_t)L.E * 4;
+  static bool attr_set = false;
+  if (!attr_set) {
+    (void)hipFuncSetAttribute((const void *)permute_kernel,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    attr_set = true;
+  }
   hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), lds, s, (const int32_t *)(ws + W.topk_ids),
                      P.T, L.E, L.k, (int32_t *)(ws + W.offsets), (int32_t *)(ws + W.mtile),
                      (int32_t *)(ws + W.active), (int32_t *)(ws + W.sorted_slots),

@@ -112,14 +112,23 @@ def router_logits(wid: int, layer: int, tokens: int, experts: int,
     return x.astype(np.float32)
 
 
+# INT4 codes are drawn from a rounded normal of this standard deviation: the
+# code spread of N(0, 0.02) weights under a per-128 max-abs / 7 scale.
+INT4_CODE_STD = 2.6
+
+
 def random_packed(fmt: str, experts: int, n: int, k: int, seed: int):
-    """Packed weights drawn directly: uniform codes and scales of the magnitude
-    N(0, 0.02) weights quantize to.  Returns (w, scale, gscale-or-None) numpy
-    arrays in the library's layouts (see the header ``moe_quant.h``)."""
+    """Packed weights drawn directly, with the spread of quantized N(0, 0.02)
+    weights: INT4 codes from a rounded normal, FP8 and E2M1 codes uniform, and
+    scales of the magnitude such weights produce.  Returns (w, scale,
+    gscale-or-None) numpy arrays in the library's layouts (see the header
+    ``moe_quant.h``)."""
     g = np.random.default_rng(np.random.SeedSequence([seed, n, k]))
     if fmt == "int4_g128":
-        w = g.integers(0, 256, size=(experts, n, k // 2), dtype=np.uint8)
-        s = (0.02 * g.uniform(2.5, 3.5, size=(experts, n, k // 128)) / 7).astype(np.float16)
+        q = np.clip(np.rint(g.standard_normal((experts, n, k), dtype=np.float32) * INT4_CODE_STD),
+                    -8, 7).astype(np.uint8) + 8
+        w = q[..., 0::2] | (q[..., 1::2] << 4)
+        s = (0.02 * g.uniform(2.4, 3.4, size=(experts, n, k // 128)) / 7).astype(np.float16)
         return w, s, None
     if fmt == "fp8_b128":
         w = g.integers(0, 256, size=(experts, n, k), dtype=np.uint8)
@@ -131,5 +140,37 @@ def random_packed(fmt: str, experts: int, n: int, k: int, seed: int):
         w = g.integers(0, 256, size=(experts, n, k // 2), dtype=np.uint8)
         s = g.integers(0x60, 0x7F, size=(experts, n, k // 16), dtype=np.uint8)
         gs = (448.0 * 6.0 / (0.02 * g.uniform(4.5, 5.5, size=experts))).astype(np.float32)
+        return w, s, gs
+    raise ValueError(fmt)
+
+
+def random_packed_torch(fmt: str, experts: int, n: int, k: int, seed: int, device="cuda"):
+    """Same recipe as :func:`random_packed`, drawn on the GPU with a seeded
+    torch generator (for multi-layer stacks, where host generation is slow)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(np.random.SeedSequence([seed, n, k]).generate_state(1)[0]))
+    u8 = dict(dtype=torch.uint8, device=device, generator=g)
+    if fmt == "int4_g128":
+        w = torch.empty((experts, n, k // 2), dtype=torch.uint8, device=device)
+        for e in range(experts):        # one expert at a time bounds the float temporaries
+            q = (torch.randn((n, k), device=device, generator=g) * INT4_CODE_STD).round_() \
+                .clamp_(-8, 7).to(torch.int16) + 8
+            w[e] = (q[:, 0::2] | (q[:, 1::2] << 4)).to(torch.uint8)
+        s = (0.02 * (2.4 + torch.rand((experts, n, k // 128), device=device, generator=g)) / 7
+             ).to(torch.float16)
+        return w, s, None
+    if fmt == "fp8_b128":
+        w = torch.randint(0, 256, (experts, n, k), **u8)
+        nan = (w & 0x7F) == 0x7F
+        w[nan] = w[nan] & 0xF7
+        s = (0.02 * (4.0 + 0.6 * torch.rand((experts, n // 128, k // 128), device=device,
+                                             generator=g)) / 448).to(torch.float32)
+        return w, s, None
+    if fmt == "nvfp4_g16":
+        w = torch.randint(0, 256, (experts, n, k // 2), **u8)
+        s = torch.randint(0x60, 0x7F, (experts, n, k // 16), **u8)
+        gs = (448.0 * 6.0 / (0.02 * (4.5 + torch.rand(experts, device=device, generator=g)))
+              ).to(torch.float32)
         return w, s, gs
     raise ValueError(fmt)
