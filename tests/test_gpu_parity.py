@@ -129,6 +129,19 @@ def test_small_layers(fmt, T, k):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("T", [20, 700])
+def test_hidden_not_multiple_of_256(fmt, T):
+    """H = 384: the prefill down projection's last 256-column tile is half full."""
+    log(f"[h384] fmt={fmt} T={T}")
+    E, H, I, k = 8, 384, 256, 2
+    p13, p2 = quantized_layer(fmt, 16, T, E, H, I)
+    g = GpuLayer(p13, p2, k)
+    lg = synth.router_logits(16, T, T, E)
+    x = synth.hidden_bf16(16, T, T, H)
+    _check_layer(g, lg, x, tag=f"{fmt} H=384 T={T}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 def test_residual_and_determinism(fmt):
     log(f"[residual] fmt={fmt}")
     E, H, I, k, T = 16, 256, 256, 4, 200

@@ -113,7 +113,9 @@ __device__ __forceinline__ h8 unpack_nvfp4(uint32_t w, _Float16 s) {
 }
 
 // ---------------------------------------------------------------- misc
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+// silu(z) = z / (1 + e^-z); the reciprocal is the hardware one (1 ulp), which
+// is far below the FP16 rounding of the SwiGLU intermediate it feeds.
+__device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // float -> bfloat16 bits, round to nearest even (NaN stays NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {

@@ -302,23 +302,73 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode(GemmArgs a) {
 }
 
 // ===========================================================================
-// Prefill path: tiles of 128 grouped rows x 128 weight columns x 128 k.  The
-// weight tile is unpacked once into LDS and shared by the 4 waves (2 x 2, each
-// 64 x 64 = 2 x 2 MFMA 32x32x16 tiles).  For the gate/up projection the block
-// covers 64 gate columns and the same 64 up columns, so every lane holds the
-// gate and up value of one column and SwiGLU runs in registers.
+// Prefill path: tiles of 128 grouped rows x 256 weight columns, stepping k by
+// 64.  The weight tile is dequantized once per block into LDS as FP16 and
+// shared by the 4 waves; the waves form a 2 x 2 grid and each owns 64 rows x
+// 128 columns (2 x 4 MFMA 32x32x16 tiles), so every 16-k step reads 6 operand
+// fragments from LDS for 8 MFMAs.
+//
+// Dequantization into the tile: INT4 (c - 8) * s and FP8 e4m3 * sinv carry
+// their group / block scale, multiplied by a power of two 2^p per weight row
+// chosen from the row's largest scale so the values sit high in FP16 range;
+// the product is rounded once to FP16 (relative error <= 2^-11) and the
+// accumulator of that column is multiplied by 2^-p at the end.  NVFP4
+// e2m1 * e4m3 products are exact in FP16; its global scale divides the
+// finished sum.
+//
+// For the gate/up projection a block covers 128 gate columns and the same 128
+// up columns; wave (wm, wn) holds gate columns 64 wn + [0, 64) in tiles 0-1
+// and the matching up columns in tiles 2-3, so SwiGLU runs in registers.
+//
+// Two pipelines (NSTAGE):
+//  2: double-buffered LDS, one block (4 waves) per CU; the HBM loads of k step
+//     s are issued two steps ahead into one of two register sets, written to
+//     LDS one step ahead; one barrier per step.
+//  1: one LDS buffer, two blocks per CU; loads one step ahead.
+// Tiles are numbered (M-tile, N-tile) with N fastest and dealt to the 8 XCDs
+// in contiguous ranges (blocks are dispatched to XCDs round robin), so tiles
+// that share activation rows or an expert's weights run on the same L2.
 // ===========================================================================
-constexpr int kBM = kPrefillBM, kBN = 128, kBK = 128, kLD = kBK + 8;
+#ifndef MQ_PREFILL_NSTAGE
+#define MQ_PREFILL_NSTAGE 1
+#endif
+constexpr int kBM = kPrefillBM, kBN = 256, kBK = 64, kLD = kBK + 8;  // kLD in halves
+constexpr size_t kPrefillStage = (size_t)(kBM + kBN) * kLD * 2;        // bytes per LDS stage
 
-template <int FMT, int STAGE>
-__global__ __launch_bounds__(256, 2) void gemm_prefill(GemmArgs a) {
+// Power of two that maps a row's largest weight magnitude `m` to [2^14, 2^15).
+__device__ __forceinline__ float row_pow2(float m, float *inv) {
+  const int sh = -row_shift(m);  // row_shift maps m * 2^-s into [2^14, 2^15)
+  *inv = pow2f(-sh);
+  return pow2f(sh);
+}
+
+// Raw HBM data of one k step for one thread.  B rows are taken 4 lanes to a
+// row (rows 64 i + tid / 4, i = 0..3; 16 consecutive k each, chunk tid % 4), so
+// one wave load touches 16 weight rows with contiguous bytes per row.
+template <int FMT>
+struct PrefillRegs {
+  u4 a[4];
+  uint32_t b[4][FMT == FMT_FP8 ? 4 : 2];  // 16 codes of row i
+  uint32_t s[4];  // INT4: FP16 scale bits; FP8: FP32 scale bits; NVFP4: E4M3 scale byte
+};
+
+template <int FMT, int STAGE, int NSTAGE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NSTAGE == 2 ? 1 : 2, NSTAGE == 2 ? 1 : 2)))
+void gemm_prefill(GemmArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  _Float16 *As = (_Float16 *)smem;  // [kBM][kLD]
-  _Float16 *Bs = As + kBM * kLD;    // [kBN][kLD]
+  float *colinv = (float *)(smem + NSTAGE * kPrefillStage);  // [kBN]: 2^-p of each B row
+  float *rowfs = colinv + kBN;                                // [kBN]: 2^p of each B row
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
-  const int mt = blockIdx.x / a.tiles, nt = blockIdx.x % a.tiles;
-  if (mt >= a.mtile[a.E]) return;
+  // ---- tile of this block
+  const int NT = a.tiles;
+  const int n_tiles = a.mtile[a.E] * NT;
+  const int per_xcd = (n_tiles + 7) >> 3;
+  const int xslot = blockIdx.x >> 3;
+  if (xslot >= per_xcd) return;
+  const int L = (blockIdx.x & 7) * per_xcd + xslot;
+  if (L >= n_tiles) return;
+  const int mt = L / NT, nt = L - mt * NT;
   int lo = 0, hi = a.E - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -330,153 +380,255 @@ __global__ __launch_bounds__(256, 2) void gemm_prefill(GemmArgs a) {
   const int K = a.K, N = a.N, G = K / 128, nK = K / kBK;
   const size_t rowbytes = FMT == FMT_FP8 ? (size_t)K : (size_t)K / 2;
 
-  // ---- staging assignments
-  const int brow = tid >> 1, bhalf = tid & 1;
-  const int nb = STAGE == 0 ? nt * 64 : nt * 128;
-  const int wrow_g = STAGE == 0 ? (brow < 64 ? nb + brow : a.I + nb + brow - 64) : nb + brow;
-  const uint8_t *wsrc = a.w + ((size_t)e * N + wrow_g) * rowbytes;
-  const uint8_t *ssrc = FMT == FMT_NVFP4
-                            ? (const uint8_t *)a.scale + ((size_t)e * N + wrow_g) * (K / 16)
-                            : nullptr;
-  const _Float16 *asrc[8];
+  // ---- A staging: row (tid >> 3) + 32 p, 16-byte chunk tid & 7
+  const _Float16 *asrc[4];
 #pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    const int rr = p * 16 + (tid >> 4);
+  for (int p = 0; p < 4; ++p) {
+    const int rr = (tid >> 3) + 32 * p;
     const int r = rbeg + (rr < nrows ? rr : nrows - 1);
     const size_t arow = STAGE == 0 ? (size_t)(a.sorted_slots[r] / a.k) : (size_t)r;
-    asrc[p] = a.a_src + arow * K + (tid & 15) * 8;
+    asrc[p] = a.a_src + arow * K + (tid & 7) * 8;
   }
-  // ---- this lane's output columns (one per 32-wide tile)
-  const int j = lane & 31;
-  int lrow[2], bbase[2];
+  const int nb = nt * (STAGE == 0 ? kBN / 2 : kBN);
+  // global weight row of local B row lr.  (down: H need only be a multiple of
+  // 128, so the last N tile may be half empty; its missing rows re-read row
+  // H-1 and are never stored)
+  auto grow = [&](int lr) {
+    return STAGE == 0 ? (lr < kBN / 2 ? nb + lr : a.I + nb + lr - kBN / 2) : min(nb + lr, N - 1);
+  };
+  // ---- power of two of B row tid (from its largest scale), shared via LDS
+  if (FMT != FMT_NVFP4) {
+    const int gr = grow(tid);
+    float m = 0.f;
+    for (int g = 0; g < G; ++g) {
+      const float sv = FMT == FMT_INT4
+                           ? (float)((const _Float16 *)a.scale)[((size_t)e * N + gr) * G + g]
+                           : ((const float *)a.scale)[((size_t)e * (N / 128) + gr / 128) * G + g];
+      m = fmaxf(m, fabsf(sv));
+    }
+    float inv;
+    rowfs[tid] = row_pow2(m * (FMT == FMT_INT4 ? 8.f : 448.f), &inv);
+    colinv[tid] = inv;
+  } else {
+    colinv[tid] = 1.f;
+  }
+  // ---- B staging: rows 64 i + (tid >> 2), chunk c = tid & 3 (k 16 c .. 16 c + 16)
+  const int bc = tid & 3;
+  const uint8_t *wsrc[4];
+  const void *ssrc[4];
 #pragma unroll
-  for (int tn = 0; tn < 2; ++tn) {
+  for (int i = 0; i < 4; ++i) {
+    const int gr = grow(64 * i + (tid >> 2));
+    wsrc[i] = a.w + ((size_t)e * N + gr) * rowbytes + (FMT == FMT_FP8 ? 16 : 8) * bc;
+    if (FMT == FMT_INT4)
+      ssrc[i] = (const _Float16 *)a.scale + ((size_t)e * N + gr) * G;
+    else if (FMT == FMT_FP8)
+      ssrc[i] = (const float *)a.scale + ((size_t)e * (N / 128) + gr / 128) * G;
+    else
+      ssrc[i] = (const uint8_t *)a.scale + ((size_t)e * N + gr) * (K / 16) + bc;
+  }
+
+  // ---- the wave's four 32-wide column tiles: B row of this lane in each
+  // (MFMA A operand) and the tile's first global weight row
+  const int j = lane & 31;
+  int tcol[4], bl[4];
+#pragma unroll
+  for (int tn = 0; tn < 4; ++tn) {
     if (STAGE == 0) {
-      bbase[tn] = tn * 64 + wn * 32;
-      lrow[tn] = (tn == 0 ? nb : a.I + nb) + wn * 32 + j;
+      const int c = wn * 64 + (tn & 1) * 32;
+      bl[tn] = (tn < 2 ? 0 : kBN / 2) + c + j;
+      tcol[tn] = (tn < 2 ? nb : a.I + nb) + c;
     } else {
-      bbase[tn] = wn * 64 + tn * 32;
-      lrow[tn] = nb + wn * 64 + tn * 32 + j;
+      bl[tn] = wn * 128 + tn * 32 + j;
+      tcol[tn] = nb + wn * 128 + tn * 32;  // may reach past H in a half tile
     }
   }
 
-  u4 areg[8], breg[4];
-  uint32_t sreg = 0;
-  auto gload = [&](int ks) {
+  auto gload = [&](PrefillRegs<FMT> &R, int ks) {
     const int kb = ks * kBK;
 #pragma unroll
-    for (int p = 0; p < 8; ++p) areg[p] = *(const u4 *)(asrc[p] + kb);
-    if (FMT == FMT_FP8) {
-      const u4 *pw = (const u4 *)(wsrc + kb + bhalf * 64);
+    for (int p = 0; p < 4; ++p) R.a[p] = *(const u4 *)(asrc[p] + kb);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) breg[c] = ld_nt(pw + c);
-    } else {
-      const u4 *pw = (const u4 *)(wsrc + kb / 2 + bhalf * 32);
-      breg[0] = ld_nt(pw);
-      breg[1] = ld_nt(pw + 1);
-      if (FMT == FMT_NVFP4) sreg = *(const uint32_t *)(ssrc + kb / 16 + 4 * bhalf);
+    for (int i = 0; i < 4; ++i) {
+      if (FMT == FMT_FP8) {
+        const u4 v = ld_nt((const u4 *)(wsrc[i] + kb));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) R.b[i][q] = v[q];
+      } else {
+        typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+        const u2 v = ld_nt((const u2 *)(wsrc[i] + kb / 2));
+        R.b[i][0] = v[0];
+        R.b[i][1] = v[1];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (FMT == FMT_INT4)
+        R.s[i] = ((const uint16_t *)ssrc[i])[kb >> 7];
+      else if (FMT == FMT_FP8)
+        R.s[i] = __builtin_bit_cast(uint32_t, ((const float *)ssrc[i])[kb >> 7]);
+      else
+        R.s[i] = ((const uint8_t *)ssrc[i])[kb / 16];
     }
   };
+  float rowf[4] = {1.f, 1.f, 1.f, 1.f};
+  auto stage = [&](const PrefillRegs<FMT> &R, int buf) {
+    _Float16 *As = (_Float16 *)(smem + buf * kPrefillStage);
+    _Float16 *Bs = As + kBM * kLD;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      u4 v = R.a[p];
+      if (FMT == FMT_INT4 && STAGE == 1) v = perm_0415(v);  // gate/up rows come INT4-ordered
+      *(u4 *)(As + ((tid >> 3) + 32 * p) * kLD + (tid & 7) * 8) = v;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      h8 v[2];
+      if (FMT == FMT_INT4) {
+        v[0] = unpack_int4(R.b[i][0]);
+        v[1] = unpack_int4(R.b[i][1]);
+      } else if (FMT == FMT_FP8) {
+        v[0] = unpack_fp8(R.b[i][0], R.b[i][1]);
+        v[1] = unpack_fp8(R.b[i][2], R.b[i][3]);
+      } else {
+        const _Float16 sb = e4m3_to_f16(R.s[i]);
+        v[0] = unpack_nvfp4(R.b[i][0], sb);
+        v[1] = unpack_nvfp4(R.b[i][1], sb);
+      }
+      if (FMT != FMT_NVFP4) {
+        const float sv = FMT == FMT_INT4 ? (float)__builtin_bit_cast(_Float16, (uint16_t)R.s[i])
+                                         : __builtin_bit_cast(float, R.s[i]);
+        const _Float16 s16 = (_Float16)(sv * rowf[i]);
+        const h2 sc = {s16, s16};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          u4 w = as_u4(v[h]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) w[q] = as_u32(as_h2(w[q]) * sc);
+          v[h] = as_h8(w);
+        }
+      }
+      _Float16 *bdst = Bs + (64 * i + (tid >> 2)) * kLD + 16 * bc;
+      *(h8 *)bdst = v[0];
+      *(h8 *)(bdst + 8) = v[1];
+    }
+  };
+  __syncthreads();  // rowfs / colinv
+  if (FMT != FMT_NVFP4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rowf[i] = rowfs[64 * i + (tid >> 2)];
+  }
 
-  f16v acc[2][2];
+  f16v acc[2][4];
 #pragma unroll
   for (int tm = 0; tm < 2; ++tm)
 #pragma unroll
-    for (int tn = 0; tn < 2; ++tn)
+    for (int tn = 0; tn < 4; ++tn)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[tm][tn][i] = 0.f;
 
-  gload(0);
-  for (int ks = 0; ks < nK; ++ks) {
-    __syncthreads();
-    // registers -> LDS (A permuted for INT4, B unpacked to FP16 codes)
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      u4 v = areg[p];
-      if (FMT == FMT_INT4 && STAGE == 1) v = perm_0415(v);  // gate/up rows come INT4-ordered
-      *(u4 *)(As + (p * 16 + (tid >> 4)) * kLD + (tid & 15) * 8) = v;
-    }
-    _Float16 *bdst = Bs + brow * kLD + bhalf * 64;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      h8 v;
-      if (FMT == FMT_INT4)
-        v = unpack_int4(breg[c >> 2][c & 3]);
-      else if (FMT == FMT_FP8)
-        v = unpack_fp8(breg[c >> 1][(c & 1) * 2], breg[c >> 1][(c & 1) * 2 + 1]);
-      else
-        v = unpack_nvfp4(breg[c >> 2][c & 3], e4m3_to_f16((sreg >> (8 * (c >> 1))) & 0xFFu));
-      *(h8 *)(bdst + c * 8) = v;
-    }
-    __syncthreads();
-    // scales of this k step first: the prefetch below retires after them
-    float sc[2] = {1.f, 1.f};
-    if (FMT == FMT_INT4) {
-#pragma unroll
-      for (int tn = 0; tn < 2; ++tn)
-        sc[tn] = (float)((const _Float16 *)a.scale)[((size_t)e * N + lrow[tn]) * G + ks];
-    } else if (FMT == FMT_FP8) {
-#pragma unroll
-      for (int tn = 0; tn < 2; ++tn)
-        sc[tn] = ((const float *)a.scale)[((size_t)e * (N / 128) + lrow[tn] / 128) * G + ks];
-    }
-    if (ks + 1 < nK) gload(ks + 1);
-    f16v tmp[2][2];
-    if (FMT != FMT_NVFP4) {
-#pragma unroll
-      for (int tm = 0; tm < 2; ++tm)
-#pragma unroll
-        for (int tn = 0; tn < 2; ++tn)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) tmp[tm][tn][i] = 0.f;
-    }
+  auto compute = [&](int buf) {
+    const _Float16 *As = (const _Float16 *)(smem + buf * kPrefillStage);
+    const _Float16 *Bs = As + kBM * kLD;
 #pragma unroll
     for (int s = 0; s < kBK / 16; ++s) {
       const int kk = s * 16 + 8 * (lane >> 5);
-      h8 av[2], bv[2];
+      h8 av[2], bv[4];
 #pragma unroll
       for (int tm = 0; tm < 2; ++tm) av[tm] = *(const h8 *)(As + (wm * 64 + tm * 32 + j) * kLD + kk);
 #pragma unroll
-      for (int tn = 0; tn < 2; ++tn) bv[tn] = *(const h8 *)(Bs + (bbase[tn] + j) * kLD + kk);
+      for (int tn = 0; tn < 4; ++tn) bv[tn] = *(const h8 *)(Bs + bl[tn] * kLD + kk);
 #pragma unroll
       for (int tm = 0; tm < 2; ++tm)
 #pragma unroll
-        for (int tn = 0; tn < 2; ++tn) {
-          if (FMT == FMT_NVFP4)
-            acc[tm][tn] = mfma32(av[tm], bv[tn], acc[tm][tn]);
-          else
-            tmp[tm][tn] = mfma32(av[tm], bv[tn], tmp[tm][tn]);
-        }
+        for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = mfma32(bv[tn], av[tm], acc[tm][tn]);
     }
-    if (FMT != FMT_NVFP4) {
-#pragma unroll
-      for (int tm = 0; tm < 2; ++tm)
-#pragma unroll
-        for (int tn = 0; tn < 2; ++tn) acc[tm][tn] += tmp[tm][tn] * sc[tn];
+  };
+
+  if constexpr (NSTAGE == 2) {
+    PrefillRegs<FMT> R0, R1;
+    gload(R0, 0);
+    gload(R1, 1);
+    stage(R0, 0);
+    if (2 < nK) gload(R0, 2);
+    __syncthreads();
+    // nK is even (K is a multiple of 128): iterations in pairs keep the
+    // register-set index static
+    for (int ks = 0; ks < nK; ks += 2) {
+      // even step ks: buffer 0 computes, step ks+1 (set R1) goes to buffer 1
+      stage(R1, 1);
+      if (ks + 3 < nK) gload(R1, ks + 3);
+      compute(0);
+      __syncthreads();
+      // odd step ks+1: buffer 1 computes, step ks+2 (set R0) goes to buffer 0
+      if (ks + 2 < nK) {
+        stage(R0, 0);
+        if (ks + 4 < nK) gload(R0, ks + 4);
+      }
+      compute(1);
+      __syncthreads();
+    }
+  } else {
+    PrefillRegs<FMT> R;
+    gload(R, 0);
+    for (int ks = 0; ks < nK; ++ks) {
+      __syncthreads();
+      stage(R, 0);
+      __syncthreads();
+      if (ks + 1 < nK) gload(R, ks + 1);
+      compute(0);
     }
   }
 
-  // ---- epilogue.  32x32 accumulator layout: register v of lane l holds
-  // row 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32.
+  // ---- epilogue.  The MFMA ran as C[n][m] (weights as its A operand), so
+  // lane l holds grouped row m = l % 32 of each M tile and, in register v,
+  // column 8 (v / 4) + 4 (l / 32) + v % 4 of the tile: four consecutive
+  // columns per group of four registers.
   const float ginv = FMT == FMT_NVFP4 ? 1.0f / a.gscale[e] : 1.0f;
+  const int cl = 4 * (lane >> 5);
+  uint32_t sat = 0u;
 #pragma unroll
   for (int tm = 0; tm < 2; ++tm) {
+    const int row = wm * 64 + tm * 32 + j;
+    if (row >= nrows) continue;
+    const int r = rbeg + row;
+    const int slot = a.sorted_slots[r];
+    const float rsc = (STAGE == 0 ? a.rowscale[slot / a.k] : a.topk_w[slot]) * ginv;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int row = wm * 64 + tm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      if (row >= nrows) continue;
-      const int r = rbeg + row;
-      const int slot = a.sorted_slots[r];
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int c4 = 8 * g4 + cl;  // first of this lane's 4 columns in the tile
       if (STAGE == 0) {
-        const float rs = a.rowscale[slot / a.k] * ginv;
-        store_h(a, r, lrow[0], acc[tm][0][v] * rs, acc[tm][1][v] * rs);
+#pragma unroll
+        for (int tn = 0; tn < 2; ++tn) {
+          const f4 ig = *(const f4 *)(colinv + bl[tn] - j + c4);
+          const f4 iu = *(const f4 *)(colinv + bl[tn + 2] - j + c4);
+          h2 o[2];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float gv = acc[tm][tn][4 * g4 + i] * (rsc * ig[i]);
+            const float uv = acc[tm][tn + 2][4 * g4 + i] * (rsc * iu[i]);
+            float hv = silu(gv) * uv;
+            const float hc = fminf(fmaxf(hv, -65504.f), 65504.f);
+            sat |= hc != hv;
+            o[i >> 1][i & 1] = (_Float16)hc;
+          }
+          typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+          *(u2 *)(a.h_out + (size_t)r * a.I + tcol[tn] + c4) = u2{as_u32(o[0]), as_u32(o[1])};
+        }
       } else {
-        const float wt = a.topk_w[slot] * ginv;
-        a.partial[(size_t)slot * a.H + lrow[0]] = acc[tm][0][v] * wt;
-        a.partial[(size_t)slot * a.H + lrow[1]] = acc[tm][1][v] * wt;
+#pragma unroll
+        for (int tn = 0; tn < 4; ++tn) {
+          if (tcol[tn] >= N) continue;
+          const f4 ic = *(const f4 *)(colinv + bl[tn] - j + c4);
+          f4 o;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[i] = acc[tm][tn][4 * g4 + i] * (rsc * ic[i]);
+          *(f4 *)(a.partial + (size_t)slot * a.H + tcol[tn] + c4) = o;
+        }
       }
     }
   }
+  if (STAGE == 0 && __builtin_amdgcn_ballot_w64(sat != 0u) != 0ull && lane == 0) atomicOr(a.flags, 1u);
 }
 
 // ===========================================================================
@@ -662,17 +814,19 @@ static hipError_t run_decode_ks(GemmArgs a, int slots, hipStream_t s) {
 
 template <int FMT, int STAGE>
 static hipError_t run_prefill(GemmArgs a, int64_t R, hipStream_t s) {
-  a.tiles = STAGE == 0 ? a.I / 64 : a.H / 128;
+  constexpr int NS = MQ_PREFILL_NSTAGE;
+  // gate/up: I is a multiple of 128, so kBN / 2 = 128 columns tile it exactly
+  a.tiles = STAGE == 0 ? a.I / (kBN / 2) : (a.H + kBN - 1) / kBN;
   const int64_t max_mt = R / kBM + a.E;  // >= sum_e ceil(n_e / kBM)
-  const size_t lds = (size_t)(kBM + kBN) * kLD * 2;
+  const int64_t grid = 8 * ((max_mt * a.tiles + 7) / 8);
+  const size_t lds = NS * kPrefillStage + 2 * kBN * sizeof(float);
   static bool attr_set = false;
   if (!attr_set) {
-    (void)hipFuncSetAttribute((const void *)gemm_prefill<FMT, STAGE>,
-                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    (void)hipFuncSetAttribute((const void *)gemm_prefill<FMT, STAGE, NS>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     attr_set = true;
   }
-  hipLaunchKernelGGL((gemm_prefill<FMT, STAGE>), dim3((unsigned)(max_mt * a.tiles)), dim3(256), lds,
-                     s, a);
+  hipLaunchKernelGGL((gemm_prefill<FMT, STAGE, NS>), dim3((unsigned)grid), dim3(256), lds, s, a);
   return hipGetLastError();
 }
 
