@@ -8,6 +8,18 @@ namespace mq {
 
 constexpr int kMaxExperts = 512;
 constexpr int kPrefillBM = 128;  // token rows per prefill M-tile
+constexpr int kMaxChunks = 256;  // token chunks of the grouping for T > 64
+
+// Chunks of the grouping: at most kMaxChunks, each a multiple of 256 tokens.
+inline void permute_chunks(int64_t T, int *nc, int *chunk) {
+  int64_t n = (T + 255) / 256;
+  if (n > kMaxChunks) n = kMaxChunks;
+  if (n < 1) n = 1;
+  int64_t c = (T + n - 1) / n;
+  c = (c + 255) / 256 * 256;
+  *chunk = (int)c;
+  *nc = (int)((T + c - 1) / c);
+}
 
 // Workspace carve-up for one forward call over T tokens (offsets in bytes).
 struct Workspace {
@@ -21,6 +33,7 @@ struct Workspace {
   size_t rowscale;             // float [T]: 2^s_t
   size_t h;                    // fp16 [R, I]
   size_t partial;              // float [R, H]: routing-weighted expert outputs per slot
+  size_t chunks;               // int32 [kMaxChunks, E]: per-chunk expert counts, then bases
   size_t flags;                // uint32 [4] at offset 0: bit 0 = FP16 intermediate saturated
   size_t total;
 };

@@ -53,6 +53,7 @@ Workspace workspace_layout(int64_t T, int E, int H, int I, int k) {
   w.mtile = take((size_t)(E + 1) * 4);
   w.sorted_slots = take(R * 4);
   w.inv_pos = take(R * 4);
+  w.chunks = take((size_t)mq::kMaxChunks * E * 4);
   w.x16 = take((size_t)T * H * 2);
   w.rowscale = take((size_t)T * 4);
   w.h = take(R * (size_t)I * 2);

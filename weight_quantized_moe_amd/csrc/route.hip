@@ -305,55 +305,107 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Stable grouping by expert for any T, one workgroup of 1024 threads.
-//   1. per-expert counts (LDS atomics) and the exclusive scans;
-//   2. tokens in chunks of 1024 (16 waves x 64): each wave records, per expert,
-//      the 64-bit mask of its lanes routed there; ranks inside the chunk are
-//      (rows of earlier waves) + popcount(mask & lanes below me), which keeps
-//      token order inside every expert.
+// Stable grouping by expert for T > 64, in three launches over chunks of
+// consecutive tokens (at most kMaxChunks chunks):
+//   1. hist_kernel:    per-chunk expert counts cnt[c][e];
+//   2. scan_kernel:    one workgroup turns them into the exclusive position of
+//                      every chunk's first row of expert e,
+//                      base[c][e] = offsets[e] + sum_{c' < c} cnt[c'][e],
+//                      plus offsets, M-tile prefix and the active-expert list;
+//   3. scatter_kernel: ranks inside a chunk, 256 tokens at a time (4 waves x 64
+//                      lanes): per wave and expert the 64-bit mask of lanes
+//                      routed there; a row's rank is (rows of earlier waves) +
+//                      popcount(mask & lanes below it), which keeps token order
+//                      inside every expert.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void permute_kernel(
-    const int32_t *__restrict__ ids, int T, int E, int k, int32_t *__restrict__ offsets,
-    int32_t *__restrict__ mtile, int32_t *__restrict__ active, int32_t *__restrict__ sorted_slots,
-    int32_t *__restrict__ inv_pos, int32_t *__restrict__ p_offsets,
-    int32_t *__restrict__ p_sorted_tok, int32_t *__restrict__ p_inv) {
+__global__ __launch_bounds__(256) void hist_kernel(const int32_t *__restrict__ ids, int T, int E,
+                                                   int k, int chunk, int32_t *__restrict__ cnt) {
+  extern __shared__ int32_t sc[];  // [E]
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += 256) sc[e] = 0;
+  __syncthreads();
+  const int t0 = blockIdx.x * chunk, t1 = min(T, t0 + chunk);
+  for (int i = t0 * k + tid; i < t1 * k; i += 256) atomicAdd(&sc[ids[i]], 1);
+  __syncthreads();
+  for (int e = tid; e < E; e += 256) cnt[(size_t)blockIdx.x * E + e] = sc[e];
+}
+
+__global__ __launch_bounds__(1024) void scan_kernel(int32_t *__restrict__ cnt, int nc, int E,
+                                                    int32_t *__restrict__ offsets,
+                                                    int32_t *__restrict__ mtile,
+                                                    int32_t *__restrict__ active,
+                                                    int32_t *__restrict__ p_offsets) {
+  __shared__ int32_t tot[kMaxExperts];
+  __shared__ int32_t off[kMaxExperts];
+  __shared__ int32_t subpre[kMaxExperts][8];
+  const int tid = threadIdx.x, sub = tid & 7;
+  // 8 threads per expert, each over a contiguous range of chunks
+  const int per = (nc + 7) / 8, c0 = min(nc, sub * per), c1 = min(nc, c0 + per);
+  for (int e0 = 0; e0 < E; e0 += 128) {
+    const int e = e0 + (tid >> 3);
+    int s = 0;
+    if (e < E)
+      for (int c = c0; c < c1; ++c) s += cnt[(size_t)c * E + e];
+    int incl = s;
+#pragma unroll
+    for (int d = 1; d < 8; d <<= 1) {
+      const int v = __shfl_up(incl, d, 8);
+      if (sub >= d) incl += v;
+    }
+    if (e < E) {
+      subpre[e][sub] = incl - s;
+      if (sub == 7) tot[e] = incl;
+    }
+  }
+  __syncthreads();
+  if (tid < 64) scan_experts_wave(tot, E, tid, offsets, mtile, active, p_offsets, off);
+  __syncthreads();
+  for (int e0 = 0; e0 < E; e0 += 128) {
+    const int e = e0 + (tid >> 3);
+    if (e >= E) continue;
+    int run = off[e] + subpre[e][sub];
+    for (int c = c0; c < c1; ++c) {
+      const int v = cnt[(size_t)c * E + e];
+      cnt[(size_t)c * E + e] = run;
+      run += v;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void scatter_kernel(
+    const int32_t *__restrict__ ids, int T, int E, int k, int chunk,
+    const int32_t *__restrict__ base, int32_t *__restrict__ sorted_slots,
+    int32_t *__restrict__ inv_pos, int32_t *__restrict__ p_sorted_tok, int32_t *__restrict__ p_inv) {
   extern __shared__ __align__(16) unsigned char smem[];
-  uint64_t *mask = (uint64_t *)smem;                      // [16][E]
-  int32_t *base = (int32_t *)(mask + 16 * E);              // [16][E]
-  int32_t *cnt = base + 16 * E;                            // [E]
-  int32_t *cursor = cnt + E;                               // [E]
-
+  uint64_t *mask = (uint64_t *)smem;              // [4][E]
+  int32_t *wbase = (int32_t *)(mask + 4 * E);     // [4][E]
+  int32_t *cursor = wbase + 4 * E;                // [E]
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int R = T * k;
-  for (int e = tid; e < E; e += 1024) cnt[e] = 0;
-  __syncthreads();
-  for (int i = tid; i < R; i += 1024) atomicAdd(&cnt[ids[i]], 1);
-  __syncthreads();
-  if (tid < 64) scan_experts_wave(cnt, E, lane, offsets, mtile, active, p_offsets, cursor);
-  __syncthreads();
-
-  for (int c0 = 0; c0 < T; c0 += 1024) {
-    for (int i = tid; i < 16 * E; i += 1024) mask[i] = 0ull;
+  for (int e = tid; e < E; e += 256) cursor[e] = base[(size_t)blockIdx.x * E + e];
+  const int t0 = blockIdx.x * chunk, t1 = min(T, t0 + chunk);
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  for (int s0 = t0; s0 < t1; s0 += 256) {
+    for (int i = tid; i < 4 * E; i += 256) mask[i] = 0ull;
     __syncthreads();
-    const int t = c0 + wave * 64 + lane;
-    const bool valid = t < T;
+    const int t = s0 + tid;
+    const bool valid = t < t1;
     if (valid)
       for (int j = 0; j < k; ++j) atomicOr(&mask[wave * E + ids[(size_t)t * k + j]], 1ull << lane);
     __syncthreads();
-    for (int e = tid; e < E; e += 1024) {
+    for (int e = tid; e < E; e += 256) {
       int run = cursor[e];
-      for (int w = 0; w < 16; ++w) {
-        base[w * E + e] = run;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        wbase[w * E + e] = run;
         run += __popcll(mask[w * E + e]);
       }
       cursor[e] = run;
     }
     __syncthreads();
     if (valid) {
-      const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
       for (int j = 0; j < k; ++j) {
         const int e = ids[(size_t)t * k + j];
-        const int pos = base[wave * E + e] + __popcll(mask[wave * E + e] & below);
+        const int pos = wbase[wave * E + e] + __popcll(mask[wave * E + e] & below);
         const int slot = t * k + j;
         sorted_slots[pos] = slot;
         inv_pos[slot] = pos;
@@ -404,17 +456,18 @@ hipError_t launch_permute(const LayerDims &L, const FwdPtrs &P, const Workspace 
                        (int32_t *)(ws + W.inv_pos), P.p_offsets, P.p_sorted_tok, P.p_inv);
     return hipGetLastError();
   }
-  const size_t lds = (size_t)16 * L.E * 8 + (size_t)16 * L.E * 4 + 2 * (size_t)L.E * 4;
-  static bool attr_set = false;
-  if (!attr_set) {
-    (void)hipFuncSetAttribute((const void *)permute_kernel,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    attr_set = true;
-  }
-  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), lds, s, (const int32_t *)(ws + W.topk_ids),
-                     P.T, L.E, L.k, (int32_t *)(ws + W.offsets), (int32_t *)(ws + W.mtile),
-                     (int32_t *)(ws + W.active), (int32_t *)(ws + W.sorted_slots),
-                     (int32_t *)(ws + W.inv_pos), P.p_offsets, P.p_sorted_tok, P.p_inv);
+  int nc, chunk;
+  permute_chunks(P.T, &nc, &chunk);
+  int32_t *cnt = (int32_t *)(ws + W.chunks);
+  hipLaunchKernelGGL(hist_kernel, dim3(nc), dim3(256), (size_t)L.E * 4, s,
+                     (const int32_t *)(ws + W.topk_ids), P.T, L.E, L.k, chunk, cnt);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, cnt, nc, L.E,
+                     (int32_t *)(ws + W.offsets), (int32_t *)(ws + W.mtile),
+                     (int32_t *)(ws + W.active), P.p_offsets);
+  hipLaunchKernelGGL(scatter_kernel, dim3(nc), dim3(256), (size_t)L.E * (4 * 8 + 4 * 4 + 4), s,
+                     (const int32_t *)(ws + W.topk_ids), P.T, L.E, L.k, chunk, (const int32_t *)cnt,
+                     (int32_t *)(ws + W.sorted_slots), (int32_t *)(ws + W.inv_pos), P.p_sorted_tok,
+                     P.p_inv);
   return hipGetLastError();
 }
 
