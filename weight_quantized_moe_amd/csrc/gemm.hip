@@ -27,10 +27,10 @@ struct GemmArgs {
   const float *gscale;
   int N, K;  // weight matrix [N, K] per expert
   int E, I, H, k;
-  const int32_t *active, *offsets, *mtile, *sorted_slots;
+  const int4 *einfo;    // {count}, then {expert, first grouped row, rows, 0} per active expert
+  const int4 *rowinfo;  // per grouped row: {slot, token, row scale bits, routing weight bits}
+  const int32_t *offsets, *mtile;
   const _Float16 *a_src;  // x16 [T, H] (gate/up) or h [R, I] (down)
-  const float *rowscale;  // gate/up: 2^s_t per token
-  const float *topk_w;    // down: routing weight per slot
   _Float16 *h_out;        // gate/up output
   float *partial;         // down output [R, H] indexed by slot
   uint32_t *flags;
@@ -97,12 +97,12 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode(GemmArgs a) {
   const size_t rowbytes = FMT == FMT_FP8 ? (size_t)K : (size_t)K / 2;
   const int gb = (kp * G) / KSPLIT;                               // groups [gb, gb + ng)
   const int ng = NGCT > 0 ? NGCT : ((kp + 1) * G) / KSPLIT - gb;
-  const int n_units = a.active[0] * a.tiles;
+  const int n_units = a.einfo[0].x * a.tiles;
 
   for (int unit = blockIdx.x; unit < n_units; unit += gridDim.x) {
     const int slot_idx = unit / a.tiles, tile = unit - slot_idx * a.tiles;
-    const int e = a.active[1 + slot_idx];
-    const int r0 = a.offsets[e], ne = a.offsets[e + 1] - r0;
+    const int4 ei = a.einfo[1 + slot_idx];
+    const int e = ei.x, r0 = ei.y, ne = ei.z;
     int row[2];
     if (STAGE == 0) {
       const int n0 = (tile * CG + cg) * 16;
@@ -166,6 +166,14 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode(GemmArgs a) {
 #pragma unroll
       for (int d = 0; d < kD; d += 2)
         if (d < ng) load_pair(f[d], f[d + 1], gb + d, d + 1 < ng);
+      // per-row records of the rows this lane stores (issued early; read in
+      // the epilogue)
+      int4 rinf[4];
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int m = 4 * q + ii;
+        rinf[ii] = m < nrows ? a.rowinfo[r0 + mc + m] : int4{0, 0, 0, 0};
+      }
 
       // ---- rows of this expert -> LDS (one pass; gate/up rows arrive in the
       // INT4 k order already, down rows are permuted here)
@@ -175,7 +183,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode(GemmArgs a) {
         for (int idx = threadIdx.x; idx < nrows * cpr; idx += 64 * kDecodeWaves) {
           const int m = idx / cpr, c = idx - m * cpr;
           const int r = r0 + mc + m;
-          const size_t src_row = STAGE == 0 ? (size_t)(a.sorted_slots[r] / a.k) : (size_t)r;
+          const size_t src_row = STAGE == 0 ? (size_t)a.rowinfo[r].y : (size_t)r;
           u4 v = *(const u4 *)(a.a_src + src_row * K + c * 8);
           if (FMT == FMT_INT4 && STAGE == 1) v = perm_0415(v);
           *(u4 *)(As + m * lda + c * 8) = v;
@@ -286,12 +294,12 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode(GemmArgs a) {
           const int m = 4 * q + ii;
           if (m >= nrows) continue;
           const int r = r0 + mc + m;
-          const int slot = a.sorted_slots[r];
+          const int slot = rinf[ii].x;
           if (STAGE == 0) {
-            const float sc = a.rowscale[slot / a.k] * ginv;
+            const float sc = __builtin_bit_cast(float, rinf[ii].z) * ginv;
             store_h(a, r, row[0], acc[0][ii] * sc, acc[1][ii] * sc);
           } else {
-            const float wt = a.topk_w[slot] * ginv;
+            const float wt = __builtin_bit_cast(float, rinf[ii].w) * ginv;
             a.partial[(size_t)slot * a.H + row[0]] = acc[0][ii] * wt;
             a.partial[(size_t)slot * a.H + row[1]] = acc[1][ii] * wt;
           }
@@ -386,7 +394,7 @@ void gemm_prefill(GemmArgs a) {
   for (int p = 0; p < 4; ++p) {
     const int rr = (tid >> 3) + 32 * p;
     const int r = rbeg + (rr < nrows ? rr : nrows - 1);
-    const size_t arow = STAGE == 0 ? (size_t)(a.sorted_slots[r] / a.k) : (size_t)r;
+    const size_t arow = STAGE == 0 ? (size_t)a.rowinfo[r].y : (size_t)r;
     asrc[p] = a.a_src + arow * K + (tid & 7) * 8;
   }
   const int nb = nt * (STAGE == 0 ? kBN / 2 : kBN);
@@ -592,8 +600,9 @@ void gemm_prefill(GemmArgs a) {
     const int row = wm * 64 + tm * 32 + j;
     if (row >= nrows) continue;
     const int r = rbeg + row;
-    const int slot = a.sorted_slots[r];
-    const float rsc = (STAGE == 0 ? a.rowscale[slot / a.k] : a.topk_w[slot]) * ginv;
+    const int4 ri = a.rowinfo[r];
+    const int slot = ri.x;
+    const float rsc = __builtin_bit_cast(float, STAGE == 0 ? ri.z : ri.w) * ginv;
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const int c4 = 8 * g4 + cl;  // first of this lane's 4 columns in the tile
@@ -723,12 +732,10 @@ static GemmArgs make_args(const LayerDims &L, const FwdPtrs &P, const Workspace 
     a.w = L.w2; a.scale = L.s2; a.gscale = L.g2; a.N = L.H; a.K = L.I;
     a.a_src = (const _Float16 *)(ws + W.h);
   }
-  a.active = (const int32_t *)(ws + W.active);
+  a.einfo = (const int4 *)(ws + W.active);
+  a.rowinfo = (const int4 *)(ws + W.rowinfo);
   a.offsets = (const int32_t *)(ws + W.offsets);
   a.mtile = (const int32_t *)(ws + W.mtile);
-  a.sorted_slots = (const int32_t *)(ws + W.sorted_slots);
-  a.rowscale = (const float *)(ws + W.rowscale);
-  a.topk_w = (const float *)(ws + W.topk_w);
   a.h_out = (_Float16 *)(ws + W.h);
   a.partial = (float *)(ws + W.partial);
   a.flags = (uint32_t *)(ws + W.flags);

@@ -25,7 +25,8 @@ inline void permute_chunks(int64_t T, int *nc, int *chunk) {
 struct Workspace {
   size_t topk_ids, topk_w;     // int32 [R], float [R]            (R = T*k)
   size_t offsets;              // int32 [E+1]
-  size_t active;               // int32 [1 + E]: count, then active expert ids
+  size_t active;               // int4 [1 + E]: {count}, then {expert, first row, rows, 0} per active expert
+  size_t rowinfo;              // int4 [R]: {slot, token, row scale bits, routing weight bits} per grouped row
   size_t mtile;                // int32 [E+1]: prefix of ceil(n_e / kPrefillBM)
   size_t sorted_slots;         // int32 [R]: slot t*k+j of each grouped row
   size_t inv_pos;              // int32 [R]

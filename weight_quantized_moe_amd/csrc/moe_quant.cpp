@@ -49,7 +49,8 @@ Workspace workspace_layout(int64_t T, int E, int H, int I, int k) {
   w.topk_ids = take(R * 4);
   w.topk_w = take(R * 4);
   w.offsets = take((size_t)(E + 1) * 4);
-  w.active = take((size_t)(E + 1) * 4);
+  w.active = take((size_t)(E + 1) * 16);
+  w.rowinfo = take(R * 16);
   w.mtile = take((size_t)(E + 1) * 4);
   w.sorted_slots = take(R * 4);
   w.inv_pos = take(R * 4);

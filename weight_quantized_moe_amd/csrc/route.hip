@@ -222,13 +222,15 @@ __global__ __launch_bounds__(256) void route_kernel(const void *__restrict__ log
 
 // ---------------------------------------------------------------------------
 // Exclusive scan of cnt[0..E) (E <= 512) by one wave; also the prefill
-// M-tile counts and the active-expert list.  Writes offsets[E+1], mtile[E+1],
-// active[1+E] and, if given, p_offsets.  Lanes hold 8 consecutive experts.
+// M-tile counts and the table of active experts.  Writes offsets[E+1],
+// mtile[E+1], einfo (the count of active experts, then one {expert, first
+// grouped row, rows, 0} entry per active expert in ascending expert order)
+// and, if given, p_offsets.  Lanes hold 8 consecutive experts.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void scan_experts_wave(const int32_t *cnt, int E, int lane,
                                                   int32_t *__restrict__ offsets,
                                                   int32_t *__restrict__ mtile,
-                                                  int32_t *__restrict__ active,
+                                                  int4 *__restrict__ einfo,
                                                   int32_t *__restrict__ p_offsets,
                                                   int32_t *cursor) {
   int c[8], s0 = 0, s1 = 0, s2 = 0;
@@ -255,7 +257,7 @@ __device__ __forceinline__ void scan_experts_wave(const int32_t *cnt, int E, int
       if (p_offsets) p_offsets[e] = r0;
       if (cursor) cursor[e] = r0;
       mtile[e] = r1;
-      if (c[i] > 0) active[1 + r2] = e;
+      if (c[i] > 0) einfo[1 + r2] = int4{e, r0, c[i], 0};
     }
     r0 += c[i];
     r1 += (c[i] + kPrefillBM - 1) / kPrefillBM;
@@ -265,7 +267,7 @@ __device__ __forceinline__ void scan_experts_wave(const int32_t *cnt, int E, int
     offsets[E] = i0;
     if (p_offsets) p_offsets[E] = i0;
     mtile[E] = i1;
-    active[0] = i2;
+    einfo[0] = int4{i2, 0, 0, 0};
   }
 }
 
@@ -275,9 +277,10 @@ __device__ __forceinline__ void scan_experts_wave(const int32_t *cnt, int E, int
 // (popcount of the mask bits below it).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void permute_small_kernel(
-    const int32_t *__restrict__ ids, int T, int E, int k, int32_t *__restrict__ offsets,
-    int32_t *__restrict__ mtile, int32_t *__restrict__ active, int32_t *__restrict__ sorted_slots,
-    int32_t *__restrict__ inv_pos, int32_t *__restrict__ p_offsets,
+    const int32_t *__restrict__ ids, const float *__restrict__ wts,
+    const float *__restrict__ rowscale, int T, int E, int k, int32_t *__restrict__ offsets,
+    int32_t *__restrict__ mtile, int4 *__restrict__ einfo, int32_t *__restrict__ sorted_slots,
+    int4 *__restrict__ rowinfo, int32_t *__restrict__ inv_pos, int32_t *__restrict__ p_offsets,
     int32_t *__restrict__ p_sorted_tok, int32_t *__restrict__ p_inv) {
   __shared__ int32_t sm_ids[64 * 64];
   __shared__ uint64_t mask[kMaxExperts];
@@ -291,13 +294,14 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(
   __syncthreads();
   for (int e = tid; e < E; e += 1024) cnt[e] = __popcll(mask[e]);
   __syncthreads();
-  if (tid < 64) scan_experts_wave(cnt, E, lane, offsets, mtile, active, p_offsets, off);
+  if (tid < 64) scan_experts_wave(cnt, E, lane, offsets, mtile, einfo, p_offsets, off);
   __syncthreads();
   for (int i = tid; i < T * k; i += 1024) {
     const int tt = i / k, e = sm_ids[i];
     const uint64_t below = tt == 0 ? 0ull : (~0ull >> (64 - tt));
     const int pos = off[e] + __popcll(mask[e] & below);
     sorted_slots[pos] = i;
+    rowinfo[pos] = int4{i, tt, __builtin_bit_cast(int, rowscale[tt]), __builtin_bit_cast(int, wts[i])};
     inv_pos[i] = pos;
     if (p_sorted_tok) p_sorted_tok[pos] = tt;
     if (p_inv) p_inv[i] = pos;
@@ -333,7 +337,7 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t *__restrict__ i
 __global__ __launch_bounds__(1024) void scan_kernel(int32_t *__restrict__ cnt, int nc, int E,
                                                     int32_t *__restrict__ offsets,
                                                     int32_t *__restrict__ mtile,
-                                                    int32_t *__restrict__ active,
+                                                    int4 *__restrict__ einfo,
                                                     int32_t *__restrict__ p_offsets) {
   __shared__ int32_t tot[kMaxExperts];
   __shared__ int32_t off[kMaxExperts];
@@ -358,7 +362,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t *__restrict__ cnt, i
     }
   }
   __syncthreads();
-  if (tid < 64) scan_experts_wave(tot, E, tid, offsets, mtile, active, p_offsets, off);
+  if (tid < 64) scan_experts_wave(tot, E, tid, offsets, mtile, einfo, p_offsets, off);
   __syncthreads();
   for (int e0 = 0; e0 < E; e0 += 128) {
     const int e = e0 + (tid >> 3);
@@ -373,9 +377,11 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t *__restrict__ cnt, i
 }
 
 __global__ __launch_bounds__(256) void scatter_kernel(
-    const int32_t *__restrict__ ids, int T, int E, int k, int chunk,
+    const int32_t *__restrict__ ids, const float *__restrict__ wts,
+    const float *__restrict__ rowscale, int T, int E, int k, int chunk,
     const int32_t *__restrict__ base, int32_t *__restrict__ sorted_slots,
-    int32_t *__restrict__ inv_pos, int32_t *__restrict__ p_sorted_tok, int32_t *__restrict__ p_inv) {
+    int4 *__restrict__ rowinfo, int32_t *__restrict__ inv_pos, int32_t *__restrict__ p_sorted_tok,
+    int32_t *__restrict__ p_inv) {
   extern __shared__ __align__(16) unsigned char smem[];
   uint64_t *mask = (uint64_t *)smem;              // [4][E]
   int32_t *wbase = (int32_t *)(mask + 4 * E);     // [4][E]
@@ -408,6 +414,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(
         const int pos = wbase[wave * E + e] + __popcll(mask[wave * E + e] & below);
         const int slot = t * k + j;
         sorted_slots[pos] = slot;
+        rowinfo[pos] = int4{slot, t, __builtin_bit_cast(int, rowscale[t]), __builtin_bit_cast(int, wts[slot])};
         inv_pos[slot] = pos;
         if (p_sorted_tok) p_sorted_tok[pos] = t;
         if (p_inv) p_inv[slot] = pos;
@@ -450,10 +457,12 @@ hipError_t launch_permute(const LayerDims &L, const FwdPtrs &P, const Workspace 
   char *ws = P.ws;
   if (P.T <= 64) {
     hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(1024), 0, s,
-                       (const int32_t *)(ws + W.topk_ids), P.T, L.E, L.k,
+                       (const int32_t *)(ws + W.topk_ids), (const float *)(ws + W.topk_w),
+                       (const float *)(ws + W.rowscale), P.T, L.E, L.k,
                        (int32_t *)(ws + W.offsets), (int32_t *)(ws + W.mtile),
-                       (int32_t *)(ws + W.active), (int32_t *)(ws + W.sorted_slots),
-                       (int32_t *)(ws + W.inv_pos), P.p_offsets, P.p_sorted_tok, P.p_inv);
+                       (int4 *)(ws + W.active), (int32_t *)(ws + W.sorted_slots),
+                       (int4 *)(ws + W.rowinfo), (int32_t *)(ws + W.inv_pos), P.p_offsets,
+                       P.p_sorted_tok, P.p_inv);
     return hipGetLastError();
   }
   int nc, chunk;
@@ -463,11 +472,12 @@ hipError_t launch_permute(const LayerDims &L, const FwdPtrs &P, const Workspace 
                      (const int32_t *)(ws + W.topk_ids), P.T, L.E, L.k, chunk, cnt);
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, cnt, nc, L.E,
                      (int32_t *)(ws + W.offsets), (int32_t *)(ws + W.mtile),
-                     (int32_t *)(ws + W.active), P.p_offsets);
+                     (int4 *)(ws + W.active), P.p_offsets);
   hipLaunchKernelGGL(scatter_kernel, dim3(nc), dim3(256), (size_t)L.E * (4 * 8 + 4 * 4 + 4), s,
-                     (const int32_t *)(ws + W.topk_ids), P.T, L.E, L.k, chunk, (const int32_t *)cnt,
-                     (int32_t *)(ws + W.sorted_slots), (int32_t *)(ws + W.inv_pos), P.p_sorted_tok,
-                     P.p_inv);
+                     (const int32_t *)(ws + W.topk_ids), (const float *)(ws + W.topk_w),
+                     (const float *)(ws + W.rowscale), P.T, L.E, L.k, chunk, (const int32_t *)cnt,
+                     (int32_t *)(ws + W.sorted_slots), (int4 *)(ws + W.rowinfo),
+                     (int32_t *)(ws + W.inv_pos), P.p_sorted_tok, P.p_inv);
   return hipGetLastError();
 }
 
