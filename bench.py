@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 PEAK_FP16_TFLOPS = 2500.0    # MI355X dense FP16/BF16 MFMA
 STAGES = ("route", "permute", "gate_up", "down", "combine")
+EVERY = 8  # bracket the dominant kernel with events in one step of every EVERY
 KERNEL_SRC = os.path.join(ROOT, "weight_quantized_moe_amd", "csrc", "gemm.hip")
 
 
@@ -159,21 +160,27 @@ def main():
                     for j, s in enumerate(STAGES)}
         dom = max(("gate_up", "down"), key=lambda s: stage_ms[s])
         jd = STAGES.index(dom)
-        # timed region: K steps; HIP events bracket only the dominant kernel
-        dev_ev = [new_events(2) for _ in range(steps)]
+        # timed region: K steps.  HIP events recorded on the layer's stream
+        # bracket the dominant kernel in every EVERY-th step (an event pair
+        # costs a few microseconds of GPU time, so bracketing every launch
+        # would inflate the step time it is part of).
+        sampled = list(range(0, steps, EVERY))
+        dev_ev = {i: new_events(2) for i in sampled}
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         start.record()
         for i in range(steps):
-            ev = [None] * (2 * len(STAGES))
-            ev[2 * jd], ev[2 * jd + 1] = dev_ev[i]
+            ev = None
+            if i in dev_ev:
+                ev = [None] * (2 * len(STAGES))
+                ev[2 * jd], ev[2 * jd + 1] = dev_ev[i]
             layers[i % n_layers].forward(logits, x, out=out, workspace=ws, events=ev)
         end.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         ms = start.elapsed_time(end) / steps
-        dom_ms = sum(a.elapsed_time(b) for a, b in dev_ev) / steps
+        dom_ms = sum(a.elapsed_time(b) for a, b in dev_ev.values()) / len(dev_ev)
         return dict(T=T, ms=ms, wall_ms=wall * 1e3 / steps, stage_ms=stage_ms, touched=touched,
                     dom=dom, dom_ms=dom_ms, logits=logits_np, x=x_np)
 

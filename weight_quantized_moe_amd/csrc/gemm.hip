@@ -30,7 +30,8 @@ struct GemmArgs {
   const int4 *einfo;    // {count}, then {expert, first grouped row, rows, 0} per active expert
   const int4 *rowinfo;  // per grouped row: {slot, token, row scale bits, routing weight bits}
   const int32_t *offsets, *mtile;
-  const _Float16 *a_src;  // x16 [T, H] (gate/up) or h [R, I] (down)
+  const _Float16 *a_src;  // prefill: x16 [T, H] (gate/up) or h [R, I] (down); decode: h
+  const uint16_t *hidden; // BF16 [T, H]: the decode gate/up scales its rows itself
   _Float16 *h_out;        // gate/up output
   float *partial;         // down output [R, H] indexed by slot
   uint32_t *flags;
@@ -93,7 +94,9 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode(GemmArgs a) {
   const int K = GCT > 0 ? GCT * 128 : a.K, N = a.N, G = K / 128;
   const int lda = K + 8;                                          // halves
   _Float16 *As = (_Float16 *)smem;                                // [16][lda]
-  float *red = (float *)(smem + (size_t)16 * lda * 2);            // [KSPLIT-1][CG][512]
+  uint32_t *sm_rmax = (uint32_t *)(smem + (size_t)16 * lda * 2);  // [16] row max |x| bits
+  float *sm_rscale = (float *)(sm_rmax + 16);                     // [2][16]: 2^s, 2^-s
+  float *red = sm_rscale + 32;                                    // [KSPLIT-1][CG][512]
   const size_t rowbytes = FMT == FMT_FP8 ? (size_t)K : (size_t)K / 2;
   const int gb = (kp * G) / KSPLIT;                               // groups [gb, gb + ng)
   const int ng = NGCT > 0 ? NGCT : ((kp + 1) * G) / KSPLIT - gb;
@@ -175,17 +178,43 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode(GemmArgs a) {
         rinf[ii] = m < nrows ? a.rowinfo[r0 + mc + m] : int4{0, 0, 0, 0};
       }
 
-      // ---- rows of this expert -> LDS (one pass; gate/up rows arrive in the
-      // INT4 k order already, down rows are permuted here)
+      // ---- rows of this expert -> LDS.  Gate/up: the tokens' BF16 hidden
+      // rows, each scaled by a power of two into FP16 (max |x| of the row into
+      // [2^14, 2^15), so every BF16 value above max * 2^-31 converts exactly)
+      // and stored in the INT4 k order for INT4; the epilogue multiplies the
+      // row back.  Down: the grouped FP16 intermediate rows (permuted here for
+      // INT4).
       __syncthreads();
       {
         const int cpr = K >> 3;
+        if (STAGE == 0) {
+          if (threadIdx.x < 16) sm_rmax[threadIdx.x] = 0u;
+          __syncthreads();
+          for (int idx = threadIdx.x; idx < nrows * cpr; idx += 64 * kDecodeWaves) {
+            const int m = idx / cpr, c = idx - m * cpr;
+            const u4 v = *(const u4 *)(a.hidden + (size_t)a.rowinfo[r0 + mc + m].y * K + c * 8);
+            atomicMax(&sm_rmax[m], __builtin_bit_cast(uint32_t, absmax_bf16x8(v, 0.f)));
+          }
+          __syncthreads();
+          if (threadIdx.x < nrows) {
+            const int sh = row_shift(__builtin_bit_cast(float, sm_rmax[threadIdx.x]));
+            sm_rscale[threadIdx.x] = pow2f(sh);
+            sm_rscale[16 + threadIdx.x] = pow2f(-sh);
+          }
+          __syncthreads();
+        }
         for (int idx = threadIdx.x; idx < nrows * cpr; idx += 64 * kDecodeWaves) {
           const int m = idx / cpr, c = idx - m * cpr;
           const int r = r0 + mc + m;
-          const size_t src_row = STAGE == 0 ? (size_t)a.rowinfo[r].y : (size_t)r;
-          u4 v = *(const u4 *)(a.a_src + src_row * K + c * 8);
-          if (FMT == FMT_INT4 && STAGE == 1) v = perm_0415(v);
+          u4 v;
+          if (STAGE == 0) {
+            v = bf16x8_to_f16x8(*(const u4 *)(a.hidden + (size_t)a.rowinfo[r].y * K + c * 8),
+                                sm_rscale[16 + m]);
+            if (FMT == FMT_INT4) v = perm_0415(v);
+          } else {
+            v = *(const u4 *)(a.a_src + (size_t)r * K + c * 8);
+            if (FMT == FMT_INT4) v = perm_0415(v);
+          }
           *(u4 *)(As + m * lda + c * 8) = v;
         }
       }
@@ -296,7 +325,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode(GemmArgs a) {
           const int r = r0 + mc + m;
           const int slot = rinf[ii].x;
           if (STAGE == 0) {
-            const float sc = __builtin_bit_cast(float, rinf[ii].z) * ginv;
+            const float sc = sm_rscale[m] * ginv;
             store_h(a, r, row[0], acc[0][ii] * sc, acc[1][ii] * sc);
           } else {
             const float wt = __builtin_bit_cast(float, rinf[ii].w) * ginv;
@@ -732,6 +761,7 @@ static GemmArgs make_args(const LayerDims &L, const FwdPtrs &P, const Workspace 
     a.w = L.w2; a.scale = L.s2; a.gscale = L.g2; a.N = L.H; a.K = L.I;
     a.a_src = (const _Float16 *)(ws + W.h);
   }
+  a.hidden = P.hidden;
   a.einfo = (const int4 *)(ws + W.active);
   a.rowinfo = (const int4 *)(ws + W.rowinfo);
   a.offsets = (const int32_t *)(ws + W.offsets);
@@ -761,7 +791,7 @@ template <int FMT, int STAGE, int KSPLIT, int GCT>
 static hipError_t run_decode_g(GemmArgs a, int slots, hipStream_t s) {
   constexpr int CG = kDecodeWaves / KSPLIT;
   a.tiles = STAGE == 0 ? a.I / (16 * CG) : a.H / (32 * CG);
-  const size_t lds = (size_t)16 * (a.K + 8) * 2 + (size_t)(KSPLIT - 1) * CG * 512 * 4;
+  const size_t lds = (size_t)16 * (a.K + 8) * 2 + 48 * 4 + (size_t)(KSPLIT - 1) * CG * 512 * 4;
   // persistent grid: as many blocks as are resident at once (from the
   // kernel's registers and LDS), never more than the number of units
   static int per_cu = 0;
@@ -798,19 +828,20 @@ static hipError_t run_decode(GemmArgs a, int slots, hipStream_t s) {
 
 template <int FMT, int STAGE>
 static hipError_t run_decode_ks(GemmArgs a, int slots, hipStream_t s) {
-  // Smallest k split whose column groups tile the expert exactly and whose
-  // wave-tasks (tile pair x k split) cover the resident waves about twice.
+  // Smallest k split (at most 4) whose column groups tile the expert exactly
+  // and whose wave-tasks (tile pair x k split) cover the resident waves
+  // (16 per CU): measured on the decode workloads, splitting k further only
+  // adds reduction cost.
   const int cols = STAGE == 0 ? a.I / 16 : a.H / 32;  // tile pairs per expert
   const long waves = (long)num_cus() * 16;
-  const int ksplits[4] = {1, 2, 4, 8};
-  int pick = 8;
+  const int ksplits[3] = {1, 2, 4};
+  int pick = 0;
   for (int ks : ksplits) {
     if (cols % (kDecodeWaves / ks) != 0) continue;
-    if ((long)slots * cols * ks >= 2 * waves) {
-      pick = ks;
-      break;
-    }
+    if (pick == 0 || (long)slots * cols * pick < waves) pick = ks;
+    if ((long)slots * cols * ks >= waves) break;
   }
+  if (pick == 0) pick = 8;  // only KS = 8 (one column group) tiles the expert
   switch (pick) {
     case 1: return run_decode<FMT, STAGE, 1>(a, slots, s);
     case 2: return run_decode<FMT, STAGE, 2>(a, slots, s);

@@ -63,8 +63,10 @@ struct FwdPtrs {
 };
 
 // launchers (return hipGetLastError() after the launch)
-hipError_t launch_route(const LayerDims &L, const FwdPtrs &P, const Workspace &W, hipStream_t s);
-hipError_t launch_permute(const LayerDims &L, const FwdPtrs &P, const Workspace &W, hipStream_t s);
+hipError_t launch_route(const LayerDims &L, const FwdPtrs &P, const Workspace &W, bool decode,
+                        hipStream_t s);
+hipError_t launch_permute(const LayerDims &L, const FwdPtrs &P, const Workspace &W, bool decode,
+                          hipStream_t s);
 hipError_t launch_gate_up(const LayerDims &L, const FwdPtrs &P, const Workspace &W, bool decode,
                           hipStream_t s);
 hipError_t launch_down(const LayerDims &L, const FwdPtrs &P, const Workspace &W, bool decode,

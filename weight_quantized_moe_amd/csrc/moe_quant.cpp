@@ -204,11 +204,11 @@ mq_status moe_quant_forward(const mq_layer *L, const void *router_logits, int32_
   };
   hipError_t e;
   ev(MQ_STAGE_ROUTE, 0);
-  if ((e = mq::launch_route(D, P, W, s)) != hipSuccess)
+  if ((e = mq::launch_route(D, P, W, decode, s)) != hipSuccess)
     return fail(MQ_E_HIP, "forward: route launch: %s", hipGetErrorString(e));
   ev(MQ_STAGE_ROUTE, 1);
   ev(MQ_STAGE_PERMUTE, 0);
-  if ((e = mq::launch_permute(D, P, W, s)) != hipSuccess)
+  if ((e = mq::launch_permute(D, P, W, decode, s)) != hipSuccess)
     return fail(MQ_E_HIP, "forward: permute launch: %s", hipGetErrorString(e));
   ev(MQ_STAGE_PERMUTE, 1);
   ev(MQ_STAGE_GATE_UP, 0);

@@ -69,12 +69,12 @@ __device__ __forceinline__ float max16f(float v) {
 // with the lowest id.  A selected key becomes 0, below every real key (the id
 // half of a real key is never 0 since E <= 512), so the k winners are always k
 // distinct valid experts.  Results go to ids/wts (global) and, if given, to
-// sm_ids (shared, [k]).
+// sm_ids / sm_w (shared, [k]).
 template <int kPer, bool kBf16Logits>
 __device__ __forceinline__ void topk16(const void *__restrict__ logits, int t, int E, int k, int li,
                                        int32_t *__restrict__ ids, float *__restrict__ wts,
                                        int32_t *__restrict__ p_ids, float *__restrict__ p_w,
-                                       int32_t *sm_ids) {
+                                       int32_t *sm_ids, float *sm_w) {
   uint64_t key[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
@@ -126,18 +126,11 @@ __device__ __forceinline__ void topk16(const void *__restrict__ logits, int t, i
       if (p_ids) p_ids[(size_t)t * k + j] = si[s];
       if (p_w) p_w[(size_t)t * k + j] = w;
       if (sm_ids) sm_ids[j] = si[s];
+      if (sm_w) sm_w[j] = w;
     }
   }
 }
 
-// Hidden row of token t -> FP16 scaled by a power of two, on one 16-lane row.
-// With kPermInt4 every 8 consecutive values are stored in the k order of the
-// INT4 unpack ({0,4,1,5,2,6,3,7}, see unpack_int4), so INT4 GEMMs use the rows
-// as they are.
-// With max|x| mapped into [2^14, 2^15), every BF16 value of the row above
-// max * 2^-31 converts to FP16 exactly (BF16 has 8 significant bits, FP16 11,
-// and the FP16 subnormal step there is 2^-24); smaller entries round with an
-// absolute error below max * 2^-39.  The GEMM multiplies its rows back by 2^s.
 // Hidden rows of the wave's 4 tokens -> FP16 scaled by a power of two each,
 // using all 64 lanes per row.  With max|x| mapped into [2^14, 2^15), every BF16
 // value of the row above max * 2^-31 converts to FP16 exactly (BF16 has 8
@@ -200,7 +193,8 @@ __device__ __forceinline__ void rows_to_f16(const uint16_t *__restrict__ hidden,
 }
 
 // General-T routing: 16 tokens per block of 256 threads.  Also zeroes the
-// flags word and, for the prefill path, stages the hidden rows in FP16.
+// flags word and, for the prefill path (stage_rows), stages the hidden rows
+// in FP16.
 template <int kPer, bool kBf16Logits, bool kPermInt4>
 __global__ __launch_bounds__(256) void route_kernel(const void *__restrict__ logits,
                                                     const uint16_t *__restrict__ hidden, int T,
@@ -210,14 +204,14 @@ __global__ __launch_bounds__(256) void route_kernel(const void *__restrict__ log
                                                     float *__restrict__ rowscale,
                                                     uint32_t *__restrict__ flags,
                                                     int32_t *__restrict__ p_ids,
-                                                    float *__restrict__ p_w) {
+                                                    float *__restrict__ p_w, int stage_rows) {
   const int lane = threadIdx.x & 63, li = lane & 15;
   const int t = blockIdx.x * 16 + (threadIdx.x >> 4);
   const int t0 = blockIdx.x * 16 + (threadIdx.x >> 6) * 4;  // first token of this wave
   if (blockIdx.x == 0 && threadIdx.x == 0) flags[0] = 0u;
   if (t0 >= T) return;
-  if (t < T) topk16<kPer, kBf16Logits>(logits, t, E, k, li, ids, wts, p_ids, p_w, nullptr);
-  rows_to_f16<kPermInt4>(hidden, t0, T, H, lane, x16, rowscale);
+  if (t < T) topk16<kPer, kBf16Logits>(logits, t, E, k, li, ids, wts, p_ids, p_w, nullptr, nullptr);
+  if (stage_rows) rows_to_f16<kPermInt4>(hidden, t0, T, H, lane, x16, rowscale);
 }
 
 // ---------------------------------------------------------------------------
@@ -272,23 +266,35 @@ __device__ __forceinline__ void scan_experts_wave(const int32_t *cnt, int E, int
 }
 
 // ---------------------------------------------------------------------------
-// T <= 64: grouping in one workgroup.  One 64-bit token mask per expert gives
-// the counts (popcount) and the stable rank of every token inside its expert
-// (popcount of the mask bits below it).
+// T <= 64: routing and grouping in one workgroup of 1024 threads.  The 16
+// waves take 4 tokens each for the top-k (16 lanes per token), keeping ids
+// and weights in LDS; for the prefill path they also stage the hidden rows in
+// FP16.  Then one 64-bit token mask per expert gives the counts (popcount) and
+// the stable rank of every token inside its expert (popcount of the mask bits
+// below it).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void permute_small_kernel(
-    const int32_t *__restrict__ ids, const float *__restrict__ wts,
-    const float *__restrict__ rowscale, int T, int E, int k, int32_t *__restrict__ offsets,
-    int32_t *__restrict__ mtile, int4 *__restrict__ einfo, int32_t *__restrict__ sorted_slots,
-    int4 *__restrict__ rowinfo, int32_t *__restrict__ inv_pos, int32_t *__restrict__ p_offsets,
+template <int kPer, bool kBf16Logits, bool kPermInt4>
+__global__ __launch_bounds__(1024) void route_small_kernel(
+    const void *__restrict__ logits, const uint16_t *__restrict__ hidden, int T, int E, int H,
+    int k, int32_t *__restrict__ ids, float *__restrict__ wts, _Float16 *__restrict__ x16,
+    float *__restrict__ rowscale, uint32_t *__restrict__ flags, int stage_rows,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ mtile, int4 *__restrict__ einfo,
+    int32_t *__restrict__ sorted_slots, int4 *__restrict__ rowinfo, int32_t *__restrict__ inv_pos,
+    int32_t *__restrict__ p_ids, float *__restrict__ p_w, int32_t *__restrict__ p_offsets,
     int32_t *__restrict__ p_sorted_tok, int32_t *__restrict__ p_inv) {
   __shared__ int32_t sm_ids[64 * 64];
+  __shared__ float sm_w[64 * 64];
   __shared__ uint64_t mask[kMaxExperts];
   __shared__ int32_t cnt[kMaxExperts];
   __shared__ int32_t off[kMaxExperts];
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15;
+  if (tid == 0) flags[0] = 0u;
   for (int e = tid; e < E; e += 1024) mask[e] = 0ull;
-  for (int i = tid; i < T * k; i += 1024) sm_ids[i] = ids[i];
+  const int t = wave * 4 + (lane >> 4);
+  if (t < T)
+    topk16<kPer, kBf16Logits>(logits, t, E, k, li, ids, wts, p_ids, p_w, sm_ids + t * k,
+                              sm_w + t * k);
+  if (stage_rows && wave * 4 < T) rows_to_f16<kPermInt4>(hidden, wave * 4, T, H, lane, x16, rowscale);
   __syncthreads();
   for (int i = tid; i < T * k; i += 1024) atomicOr(&mask[sm_ids[i]], 1ull << (i / k));
   __syncthreads();
@@ -301,7 +307,8 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(
     const uint64_t below = tt == 0 ? 0ull : (~0ull >> (64 - tt));
     const int pos = off[e] + __popcll(mask[e] & below);
     sorted_slots[pos] = i;
-    rowinfo[pos] = int4{i, tt, __builtin_bit_cast(int, rowscale[tt]), __builtin_bit_cast(int, wts[i])};
+    const float rs = stage_rows ? rowscale[tt] : 0.f;
+    rowinfo[pos] = int4{i, tt, __builtin_bit_cast(int, rs), __builtin_bit_cast(int, sm_w[i])};
     inv_pos[i] = pos;
     if (p_sorted_tok) p_sorted_tok[pos] = tt;
     if (p_inv) p_inv[i] = pos;
@@ -414,7 +421,8 @@ __global__ __launch_bounds__(256) void scatter_kernel(
         const int pos = wbase[wave * E + e] + __popcll(mask[wave * E + e] & below);
         const int slot = t * k + j;
         sorted_slots[pos] = slot;
-        rowinfo[pos] = int4{slot, t, __builtin_bit_cast(int, rowscale[t]), __builtin_bit_cast(int, wts[slot])};
+        const float rs = rowscale ? rowscale[t] : 0.f;
+        rowinfo[pos] = int4{slot, t, __builtin_bit_cast(int, rs), __builtin_bit_cast(int, wts[slot])};
         inv_pos[slot] = pos;
         if (p_sorted_tok) p_sorted_tok[pos] = t;
         if (p_inv) p_inv[slot] = pos;
@@ -427,44 +435,50 @@ __global__ __launch_bounds__(256) void scatter_kernel(
 // ---------------------------------------------------------------------------
 template <int kPer, bool kBf16, bool kPerm>
 static hipError_t route_dispatch(const LayerDims &L, const FwdPtrs &P, const Workspace &W,
-                                 hipStream_t s) {
+                                 bool stage_rows, hipStream_t s) {
   char *ws = P.ws;
+  if (P.T <= 64) {
+    hipLaunchKernelGGL((route_small_kernel<kPer, kBf16, kPerm>), dim3(1), dim3(1024), 0, s,
+                       P.logits, P.hidden, P.T, L.E, L.H, L.k, (int32_t *)(ws + W.topk_ids),
+                       (float *)(ws + W.topk_w), (_Float16 *)(ws + W.x16),
+                       (float *)(ws + W.rowscale), (uint32_t *)(ws + W.flags), (int)stage_rows,
+                       (int32_t *)(ws + W.offsets), (int32_t *)(ws + W.mtile),
+                       (int4 *)(ws + W.active), (int32_t *)(ws + W.sorted_slots),
+                       (int4 *)(ws + W.rowinfo), (int32_t *)(ws + W.inv_pos), P.p_ids, P.p_w,
+                       P.p_offsets, P.p_sorted_tok, P.p_inv);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((route_kernel<kPer, kBf16, kPerm>), dim3((P.T + 15) / 16), dim3(256), 0, s,
                      P.logits, P.hidden, P.T, L.E, L.H, L.k, (int32_t *)(ws + W.topk_ids),
                      (float *)(ws + W.topk_w), (_Float16 *)(ws + W.x16), (float *)(ws + W.rowscale),
-                     (uint32_t *)(ws + W.flags), P.p_ids, P.p_w);
+                     (uint32_t *)(ws + W.flags), P.p_ids, P.p_w, (int)stage_rows);
   return hipGetLastError();
 }
 
 template <int kPer>
 static hipError_t route_dispatch2(const LayerDims &L, const FwdPtrs &P, const Workspace &W,
-                                  hipStream_t s) {
+                                  bool stage_rows, hipStream_t s) {
   const bool perm = L.fmt == FMT_INT4;
   if (P.logits_bf16)
-    return perm ? route_dispatch<kPer, true, true>(L, P, W, s)
-                : route_dispatch<kPer, true, false>(L, P, W, s);
-  return perm ? route_dispatch<kPer, false, true>(L, P, W, s)
-              : route_dispatch<kPer, false, false>(L, P, W, s);
+    return perm ? route_dispatch<kPer, true, true>(L, P, W, stage_rows, s)
+                : route_dispatch<kPer, true, false>(L, P, W, stage_rows, s);
+  return perm ? route_dispatch<kPer, false, true>(L, P, W, stage_rows, s)
+              : route_dispatch<kPer, false, false>(L, P, W, stage_rows, s);
 }
 
-hipError_t launch_route(const LayerDims &L, const FwdPtrs &P, const Workspace &W, hipStream_t s) {
-  if (L.E <= 128) return route_dispatch2<8>(L, P, W, s);
-  if (L.E <= 256) return route_dispatch2<16>(L, P, W, s);
-  return route_dispatch2<32>(L, P, W, s);
+hipError_t launch_route(const LayerDims &L, const FwdPtrs &P, const Workspace &W, bool decode,
+                        hipStream_t s) {
+  // the decode GEMMs scale the hidden rows themselves; only prefill stages them
+  const bool stage_rows = !decode;
+  if (L.E <= 128) return route_dispatch2<8>(L, P, W, stage_rows, s);
+  if (L.E <= 256) return route_dispatch2<16>(L, P, W, stage_rows, s);
+  return route_dispatch2<32>(L, P, W, stage_rows, s);
 }
 
-hipError_t launch_permute(const LayerDims &L, const FwdPtrs &P, const Workspace &W, hipStream_t s) {
+hipError_t launch_permute(const LayerDims &L, const FwdPtrs &P, const Workspace &W, bool decode,
+                          hipStream_t s) {
   char *ws = P.ws;
-  if (P.T <= 64) {
-    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(1024), 0, s,
-                       (const int32_t *)(ws + W.topk_ids), (const float *)(ws + W.topk_w),
-                       (const float *)(ws + W.rowscale), P.T, L.E, L.k,
-                       (int32_t *)(ws + W.offsets), (int32_t *)(ws + W.mtile),
-                       (int4 *)(ws + W.active), (int32_t *)(ws + W.sorted_slots),
-                       (int4 *)(ws + W.rowinfo), (int32_t *)(ws + W.inv_pos), P.p_offsets,
-                       P.p_sorted_tok, P.p_inv);
-    return hipGetLastError();
-  }
+  if (P.T <= 64) return hipSuccess;  // grouped by the routing kernel
   int nc, chunk;
   permute_chunks(P.T, &nc, &chunk);
   int32_t *cnt = (int32_t *)(ws + W.chunks);
@@ -475,9 +489,10 @@ hipError_t launch_permute(const LayerDims &L, const FwdPtrs &P, const Workspace 
                      (int4 *)(ws + W.active), P.p_offsets);
   hipLaunchKernelGGL(scatter_kernel, dim3(nc), dim3(256), (size_t)L.E * (4 * 8 + 4 * 4 + 4), s,
                      (const int32_t *)(ws + W.topk_ids), (const float *)(ws + W.topk_w),
-                     (const float *)(ws + W.rowscale), P.T, L.E, L.k, chunk, (const int32_t *)cnt,
-                     (int32_t *)(ws + W.sorted_slots), (int4 *)(ws + W.rowinfo),
-                     (int32_t *)(ws + W.inv_pos), P.p_sorted_tok, P.p_inv);
+                     decode ? nullptr : (const float *)(ws + W.rowscale), P.T, L.E, L.k, chunk,
+                     (const int32_t *)cnt, (int32_t *)(ws + W.sorted_slots),
+                     (int4 *)(ws + W.rowinfo), (int32_t *)(ws + W.inv_pos), P.p_sorted_tok,
+                     P.p_inv);
   return hipGetLastError();
 }
 
