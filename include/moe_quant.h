@@ -62,7 +62,7 @@ typedef enum {
   MQ_E_WORKSPACE = 6, /* workspace NULL or smaller than moe_quant_workspace_size()   */
   MQ_E_ABI = 7,       /* descriptor built against another MOE_QUANT_ABI_VERSION      */
   MQ_E_HIP = 8,       /* a HIP launch or runtime call failed                         */
-  MQ_E_OVERFLOW = 9   /* the FP16 SwiGLU intermediate saturated (moe_quant_check)    */
+  MQ_E_OVERFLOW = 9   /* an FP16 intermediate saturated (moe_quant_check)           */
 } mq_status;
 
 /*
@@ -188,7 +188,8 @@ mq_status moe_quant_forward(const mq_layer *L, const void *router_logits, int32_
 
 /*
  * Synchronize `stream` and report whether the last forward that used
- * `workspace` saturated its FP16 SwiGLU intermediate (|h| > 65504 clamped):
+ * `workspace` saturated one of its FP16 intermediates (the SwiGLU output h or a
+ * routing-weighted per-slot expert output; values beyond +-65504 are clamped):
  * MQ_OK if not, MQ_E_OVERFLOW if it did.  workspace as passed to forward.
  */
 mq_status moe_quant_check(const mq_layer *L, const void *workspace, struct ihipStream_t *stream);

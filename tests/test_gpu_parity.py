@@ -129,6 +129,20 @@ def test_small_layers(fmt, T, k):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("T", [65, 128])
+def test_decode_after_chunked_grouping(fmt, T):
+    """E 64, top-8, T 65 / 128: T > 64 takes the chunked grouping, while
+    T * k <= 16 E keeps the weight-streaming decode GEMMs."""
+    log(f"[decode T>64] fmt={fmt} T={T}")
+    E, H, I, k = 64, 256, 128, 8
+    p13, p2 = quantized_layer(fmt, 17, T, E, H, I)
+    g = GpuLayer(p13, p2, k)
+    lg = synth.router_logits(17, T, T, E)
+    x = synth.hidden_bf16(17, T, T, H)
+    _check_layer(g, lg, x, tag=f"{fmt} E=64 T={T}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("T", [20, 700])
 def test_hidden_not_multiple_of_256(fmt, T):
     """H = 384: the prefill down projection's last 256-column tile is half full."""

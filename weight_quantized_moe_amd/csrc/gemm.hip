@@ -33,10 +33,17 @@ struct GemmArgs {
   const _Float16 *a_src;  // prefill: x16 [T, H] (gate/up) or h [R, I] (down); decode: h
   const uint16_t *hidden; // BF16 [T, H]: the decode gate/up scales its rows itself
   _Float16 *h_out;        // gate/up output
-  float *partial;         // down output [R, H] indexed by slot
+  _Float16 *partial;      // down output [R, H] indexed by slot (FP16, routing-weighted)
   uint32_t *flags;
   int tiles;              // decode: column tiles per expert; prefill: N tiles
 };
+
+// Saturate to the FP16 range, remembering whether anything was clamped.
+__device__ __forceinline__ _Float16 to_f16_sat(float v, uint32_t &sat) {
+  const float c = fminf(fmaxf(v, -65504.f), 65504.f);
+  sat |= c != v;
+  return (_Float16)c;
+}
 
 __device__ __forceinline__ void store_h(const GemmArgs &a, int r, int col, float g, float u) {
   float hv = silu(g) * u;
@@ -329,8 +336,10 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode(GemmArgs a) {
             store_h(a, r, row[0], acc[0][ii] * sc, acc[1][ii] * sc);
           } else {
             const float wt = __builtin_bit_cast(float, rinf[ii].w) * ginv;
-            a.partial[(size_t)slot * a.H + row[0]] = acc[0][ii] * wt;
-            a.partial[(size_t)slot * a.H + row[1]] = acc[1][ii] * wt;
+            uint32_t sat = 0u;
+            a.partial[(size_t)slot * a.H + row[0]] = to_f16_sat(acc[0][ii] * wt, sat);
+            a.partial[(size_t)slot * a.H + row[1]] = to_f16_sat(acc[1][ii] * wt, sat);
+            if (sat) atomicOr(a.flags, 1u);
           }
         }
       }
@@ -658,22 +667,24 @@ void gemm_prefill(GemmArgs a) {
         for (int tn = 0; tn < 4; ++tn) {
           if (tcol[tn] >= N) continue;
           const f4 ic = *(const f4 *)(colinv + bl[tn] - j + c4);
-          f4 o;
+          h2 o[2];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) o[i] = acc[tm][tn][4 * g4 + i] * (rsc * ic[i]);
-          *(f4 *)(a.partial + (size_t)slot * a.H + tcol[tn] + c4) = o;
+          for (int i = 0; i < 4; ++i) o[i >> 1][i & 1] = to_f16_sat(acc[tm][tn][4 * g4 + i] * (rsc * ic[i]), sat);
+          typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+          *(u2 *)(a.partial + (size_t)slot * a.H + tcol[tn] + c4) = u2{as_u32(o[0]), as_u32(o[1])};
         }
       }
     }
   }
-  if (STAGE == 0 && __builtin_amdgcn_ballot_w64(sat != 0u) != 0ull && lane == 0) atomicOr(a.flags, 1u);
+  if (__builtin_amdgcn_ballot_w64(sat != 0u) != 0ull && lane == 0) atomicOr(a.flags, 1u);
 }
 
 // ===========================================================================
-// Combine: out[t] = bf16(sum_j partial[t*k + j] (+ residual[t])), slots added
-// in order j = 0..k-1 so repeated runs are bit-identical.
+// Combine: out[t] = bf16(sum_j partial[t*k + j] (+ residual[t])), the FP16
+// partials widened to FP32 and added in order j = 0..k-1 so repeated runs are
+// bit-identical.
 // ===========================================================================
-__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ partial,
+__global__ __launch_bounds__(256) void combine_kernel(const _Float16 *__restrict__ partial,
                                                       const uint16_t *__restrict__ residual,
                                                       uint16_t *__restrict__ out, int T, int H,
                                                       int k) {
@@ -685,13 +696,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
   for (int j = 0; j < k; ++j) {
-    const f4 *p = (const f4 *)(partial + ((size_t)t * k + j) * H + c);
-    const f4 x0 = p[0], x1 = p[1];
+    const h8 x = as_h8(*(const u4 *)(partial + ((size_t)t * k + j) * H + c));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[i] += x0[i];
-      acc[4 + i] += x1[i];
-    }
+    for (int i = 0; i < 8; ++i) acc[i] += (float)x[i];
   }
   if (residual) {
     const u4 rv = *(const u4 *)(residual + (size_t)t * H + c);
@@ -767,7 +774,7 @@ static GemmArgs make_args(const LayerDims &L, const FwdPtrs &P, const Workspace 
   a.offsets = (const int32_t *)(ws + W.offsets);
   a.mtile = (const int32_t *)(ws + W.mtile);
   a.h_out = (_Float16 *)(ws + W.h);
-  a.partial = (float *)(ws + W.partial);
+  a.partial = (_Float16 *)(ws + W.partial);
   a.flags = (uint32_t *)(ws + W.flags);
   a.tiles = 0;
   return a;
@@ -901,7 +908,7 @@ hipError_t launch_down(const LayerDims &L, const FwdPtrs &P, const Workspace &W,
 hipError_t launch_combine(const LayerDims &L, const FwdPtrs &P, const Workspace &W, hipStream_t s) {
   const size_t items = (size_t)P.T * (L.H / 8);
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s,
-                     (const float *)(P.ws + W.partial), P.residual, P.out, P.T, L.H, L.k);
+                     (const _Float16 *)(P.ws + W.partial), P.residual, P.out, P.T, L.H, L.k);
   return hipGetLastError();
 }
 

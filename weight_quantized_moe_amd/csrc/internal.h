@@ -33,9 +33,9 @@ struct Workspace {
   size_t x16;                  // fp16 [T, H]: hidden rows scaled by 2^-s_t (INT4: k order of the unpack)
   size_t rowscale;             // float [T]: 2^s_t
   size_t h;                    // fp16 [R, I]
-  size_t partial;              // float [R, H]: routing-weighted expert outputs per slot
+  size_t partial;              // fp16 [R, H]: routing-weighted expert outputs per slot
   size_t chunks;               // int32 [kMaxChunks, E]: per-chunk expert counts, then bases
-  size_t flags;                // uint32 [4] at offset 0: bit 0 = FP16 intermediate saturated
+  size_t flags;                // uint32 [4] at offset 0: bit 0 = an FP16 intermediate saturated
   size_t total;
 };
 

@@ -58,7 +58,7 @@ Workspace workspace_layout(int64_t T, int E, int H, int I, int k) {
   w.x16 = take((size_t)T * H * 2);
   w.rowscale = take((size_t)T * 4);
   w.h = take(R * (size_t)I * 2);
-  w.partial = take(R * (size_t)H * 4);
+  w.partial = take(R * (size_t)H * 2);
   w.total = o;
   return w;
 }
@@ -82,7 +82,7 @@ const char *moe_quant_status_string(mq_status s) {
     case MQ_E_WORKSPACE: return "MQ_E_WORKSPACE: workspace missing or too small";
     case MQ_E_ABI: return "MQ_E_ABI: descriptor ABI version mismatch";
     case MQ_E_HIP: return "MQ_E_HIP: HIP runtime or launch failure";
-    case MQ_E_OVERFLOW: return "MQ_E_OVERFLOW: FP16 SwiGLU intermediate saturated";
+    case MQ_E_OVERFLOW: return "MQ_E_OVERFLOW: an FP16 intermediate saturated";
   }
   return "unknown mq_status";
 }
@@ -240,7 +240,7 @@ mq_status moe_quant_check(const mq_layer *L, const void *workspace, struct ihipS
   uint32_t flag = 0;
   e = hipMemcpy(&flag, workspace, sizeof(flag), hipMemcpyDeviceToHost);
   if (e != hipSuccess) return fail(MQ_E_HIP, "check: %s", hipGetErrorString(e));
-  if (flag) return fail(MQ_E_OVERFLOW, "check: FP16 SwiGLU intermediate saturated");
+  if (flag) return fail(MQ_E_OVERFLOW, "check: an FP16 intermediate saturated");
   g_err[0] = 0;
   return MQ_OK;
 }
