@@ -497,12 +497,12 @@ void gemm_prefill(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       if (FMT == FMT_FP8) {
-        const u4 v = ld_nt((const u4 *)(wsrc[i] + kb));
+        const u4 v = *(const u4 *)(wsrc[i] + kb);  // cached: every M tile of the expert reads it
 #pragma unroll
         for (int q = 0; q < 4; ++q) R.b[i][q] = v[q];
       } else {
         typedef uint32_t u2 __attribute__((ext_vector_type(2)));
-        const u2 v = ld_nt((const u2 *)(wsrc[i] + kb / 2));
+        const u2 v = *(const u2 *)(wsrc[i] + kb / 2);
         R.b[i][0] = v[0];
         R.b[i][1] = v[1];
       }
