@@ -10,7 +10,8 @@ through several distinct layers' weights (>= 1.5 GiB in total, more than the
 a real model's consecutive layers would.
 
 Prints one JSON line: whole-step tokens/s, the roofline position of the
-dominant kernel (timed live with HIP events on the stream it runs on), and the
+dominant kernel (timed live with HIP events on the stream it runs on, which
+the library has the runtime take at the kernel's own start and end), and the
 CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -160,10 +161,10 @@ def main():
                     for j, s in enumerate(STAGES)}
         dom = max(("gate_up", "down"), key=lambda s: stage_ms[s])
         jd = STAGES.index(dom)
-        # timed region: K steps.  HIP events recorded on the layer's stream
-        # bracket the dominant kernel in every EVERY-th step (an event pair
-        # costs a few microseconds of GPU time, so bracketing every launch
-        # would inflate the step time it is part of).
+        # timed region: K steps.  HIP events on the layer's stream bracket the
+        # dominant kernel in every EVERY-th step (an event pair costs a few
+        # microseconds of GPU time, so bracketing every launch would inflate
+        # the step time it is part of).
         sampled = list(range(0, steps, EVERY))
         dev_ev = {i: new_events(2) for i in sampled}
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

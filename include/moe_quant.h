@@ -140,8 +140,10 @@ enum {
  *   inv_pos          int32 [T * k]  grouped row of slot t * k + j
  *   h                uint16 [T*k, I] FP16 bits of the SwiGLU intermediate in
  *                                   grouped row order
- * events[2 * s] / events[2 * s + 1] (hipEvent_t) are recorded on the stream
- * right before / after stage s.
+ * events[2 * s] / events[2 * s + 1] (hipEvent_t, created by the caller) are
+ * recorded on the stream right before / after stage s; for the two GEMM
+ * stages the runtime takes them at the start and the end of the GEMM kernel
+ * itself (hipExtLaunchKernel), so they exclude the gap before its dispatch.
  */
 typedef struct {
   int32_t *topk_ids;

@@ -16,6 +16,8 @@
 // per lane.
 #include <algorithm>
 
+#include <hip/hip_ext.h>
+
 #include "device.h"
 #include "internal.h"
 
@@ -795,7 +797,7 @@ static int num_cus() {
 }
 
 template <int FMT, int STAGE, int KSPLIT, int GCT>
-static hipError_t run_decode_g(GemmArgs a, int slots, hipStream_t s) {
+static hipError_t run_decode_g(GemmArgs a, int slots, const GemmLaunch &s) {
   constexpr int CG = kDecodeWaves / KSPLIT;
   a.tiles = STAGE == 0 ? a.I / (16 * CG) : a.H / (32 * CG);
   const size_t lds = (size_t)16 * (a.K + 8) * 2 + 48 * 4 + (size_t)(KSPLIT - 1) * CG * 512 * 4;
@@ -815,13 +817,13 @@ static hipError_t run_decode_g(GemmArgs a, int slots, hipStream_t s) {
   }
   const long units = (long)slots * a.tiles;
   const long grid = std::min<long>(units, (long)num_cus() * per_cu);
-  hipLaunchKernelGGL((gemm_decode<FMT, STAGE, KSPLIT, GCT>), dim3((unsigned)grid),
-                     dim3(64 * kDecodeWaves), lds, s, a);
+  hipExtLaunchKernelGGL((gemm_decode<FMT, STAGE, KSPLIT, GCT>), dim3((unsigned)grid),
+                        dim3(64 * kDecodeWaves), (uint32_t)lds, s.stream, s.start, s.stop, 0u, a);
   return hipGetLastError();
 }
 
 template <int FMT, int STAGE, int KSPLIT>
-static hipError_t run_decode(GemmArgs a, int slots, hipStream_t s) {
+static hipError_t run_decode(GemmArgs a, int slots, const GemmLaunch &s) {
   switch (a.K / 128) {  // k groups per row; unrolled variants for common sizes
     case 4: return run_decode_g<FMT, STAGE, KSPLIT, 4>(a, slots, s);
     case 6: return run_decode_g<FMT, STAGE, KSPLIT, 6>(a, slots, s);
@@ -834,7 +836,7 @@ static hipError_t run_decode(GemmArgs a, int slots, hipStream_t s) {
 }
 
 template <int FMT, int STAGE>
-static hipError_t run_decode_ks(GemmArgs a, int slots, hipStream_t s) {
+static hipError_t run_decode_ks(GemmArgs a, int slots, const GemmLaunch &s) {
   // Smallest k split (at most 4) whose column groups tile the expert exactly
   // and whose wave-tasks (tile pair x k split) cover the resident waves
   // (16 per CU): measured on the decode workloads, splitting k further only
@@ -858,7 +860,7 @@ static hipError_t run_decode_ks(GemmArgs a, int slots, hipStream_t s) {
 }
 
 template <int FMT, int STAGE>
-static hipError_t run_prefill(GemmArgs a, int64_t R, hipStream_t s) {
+static hipError_t run_prefill(GemmArgs a, int64_t R, const GemmLaunch &s) {
   constexpr int NS = MQ_PREFILL_NSTAGE;
   // gate/up: I is a multiple of 128, so kBN / 2 = 128 columns tile it exactly
   a.tiles = STAGE == 0 ? a.I / (kBN / 2) : (a.H + kBN - 1) / kBN;
@@ -871,13 +873,14 @@ static hipError_t run_prefill(GemmArgs a, int64_t R, hipStream_t s) {
                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     attr_set = true;
   }
-  hipLaunchKernelGGL((gemm_prefill<FMT, STAGE, NS>), dim3((unsigned)grid), dim3(256), lds, s, a);
+  hipExtLaunchKernelGGL((gemm_prefill<FMT, STAGE, NS>), dim3((unsigned)grid), dim3(256), (uint32_t)lds, s.stream,
+                        s.start, s.stop, 0u, a);
   return hipGetLastError();
 }
 
 template <int STAGE>
 static hipError_t dispatch(const LayerDims &L, const FwdPtrs &P, const Workspace &W, bool decode,
-                           hipStream_t s) {
+                           const GemmLaunch &s) {
   GemmArgs a = make_args(L, P, W, STAGE);
   const int64_t R = (int64_t)P.T * L.k;
   const int slots = (int)(R < L.E ? R : L.E);
@@ -896,12 +899,12 @@ static hipError_t dispatch(const LayerDims &L, const FwdPtrs &P, const Workspace
 }
 
 hipError_t launch_gate_up(const LayerDims &L, const FwdPtrs &P, const Workspace &W, bool decode,
-                          hipStream_t s) {
+                          const GemmLaunch &s) {
   return dispatch<0>(L, P, W, decode, s);
 }
 
 hipError_t launch_down(const LayerDims &L, const FwdPtrs &P, const Workspace &W, bool decode,
-                       hipStream_t s) {
+                       const GemmLaunch &s) {
   return dispatch<1>(L, P, W, decode, s);
 }
 

@@ -67,10 +67,16 @@ hipError_t launch_route(const LayerDims &L, const FwdPtrs &P, const Workspace &W
                         hipStream_t s);
 hipError_t launch_permute(const LayerDims &L, const FwdPtrs &P, const Workspace &W, bool decode,
                           hipStream_t s);
+// Stream of a GEMM launch, and optional events that the runtime records at
+// the start and the end of the kernel's own execution (null: none).
+struct GemmLaunch {
+  hipStream_t stream;
+  hipEvent_t start, stop;
+};
 hipError_t launch_gate_up(const LayerDims &L, const FwdPtrs &P, const Workspace &W, bool decode,
-                          hipStream_t s);
+                          const GemmLaunch &s);
 hipError_t launch_down(const LayerDims &L, const FwdPtrs &P, const Workspace &W, bool decode,
-                       hipStream_t s);
+                       const GemmLaunch &s);
 hipError_t launch_combine(const LayerDims &L, const FwdPtrs &P, const Workspace &W, hipStream_t s);
 hipError_t launch_dequantize(const LayerDims &L, int which, int expert, float *out, hipStream_t s);
 

@@ -211,19 +211,25 @@ mq_status moe_quant_forward(const mq_layer *L, const void *router_logits, int32_
   if ((e = mq::launch_permute(D, P, W, decode, s)) != hipSuccess)
     return fail(MQ_E_HIP, "forward: permute launch: %s", hipGetErrorString(e));
   ev(MQ_STAGE_PERMUTE, 1);
-  ev(MQ_STAGE_GATE_UP, 0);
-  if ((e = mq::launch_gate_up(D, P, W, decode, s)) != hipSuccess)
+  // the GEMM stages' events are taken by the runtime at the start and the end
+  // of the kernel itself
+  auto kev = [&](int stage) {
+    mq::GemmLaunch g{s, nullptr, nullptr};
+    if (probe) {
+      g.start = (hipEvent_t)probe->events[2 * stage];
+      g.stop = (hipEvent_t)probe->events[2 * stage + 1];
+    }
+    return g;
+  };
+  if ((e = mq::launch_gate_up(D, P, W, decode, kev(MQ_STAGE_GATE_UP))) != hipSuccess)
     return fail(MQ_E_HIP, "forward: gate_up launch: %s", hipGetErrorString(e));
-  ev(MQ_STAGE_GATE_UP, 1);
   if (P.p_h) {
     e = hipMemcpyAsync(P.p_h, P.ws + W.h, (size_t)num_tokens * D.k * D.I * 2,
                        hipMemcpyDeviceToDevice, s);
     if (e != hipSuccess) return fail(MQ_E_HIP, "forward: probe copy: %s", hipGetErrorString(e));
   }
-  ev(MQ_STAGE_DOWN, 0);
-  if ((e = mq::launch_down(D, P, W, decode, s)) != hipSuccess)
+  if ((e = mq::launch_down(D, P, W, decode, kev(MQ_STAGE_DOWN))) != hipSuccess)
     return fail(MQ_E_HIP, "forward: down launch: %s", hipGetErrorString(e));
-  ev(MQ_STAGE_DOWN, 1);
   ev(MQ_STAGE_COMBINE, 0);
   if ((e = mq::launch_combine(D, P, W, s)) != hipSuccess)
     return fail(MQ_E_HIP, "forward: combine launch: %s", hipGetErrorString(e));
