@@ -160,9 +160,4 @@ __device__ __forceinline__ float absmax_bf16x8(u4 v, float m) {
   return m;
 }
 
-template <typename T>
-__device__ __forceinline__ T ld_nt(const T *p) {
-  return __builtin_nontemporal_load(p);
-}
-
 }  // namespace mq
