@@ -699,10 +699,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const _Float16 *__restrict
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const h8 x = as_h8(*(const u4 *)(partial + ((size_t)t * k + j) * H + c));
+  // the partials of up to 8 slots are loaded together, then summed in slot order
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    h8 x[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] += (float)x[i];
+    for (int jj = 0; jj < 8; ++jj)
+      if (j0 + jj < k) x[jj] = as_h8(*(const u4 *)(partial + ((size_t)t * k + j0 + jj) * H + c));
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj)
+      if (j0 + jj < k) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += (float)x[jj][i];
+      }
   }
   if (residual) {
     const u4 rv = *(const u4 *)(residual + (size_t)t * H + c);

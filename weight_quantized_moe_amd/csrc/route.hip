@@ -68,13 +68,11 @@ __device__ __forceinline__ float max16f(float v) {
 // Keys pack (ordered logit, ~expert id): the row maximum is the largest logit
 // with the lowest id.  A selected key becomes 0, below every real key (the id
 // half of a real key is never 0 since E <= 512), so the k winners are always k
-// distinct valid experts.  Results go to ids/wts (global) and, if given, to
-// sm_ids / sm_w (shared, [k]).
+// distinct valid experts.  Results go to ids/wts (and the probe arrays).
 template <int kPer, bool kBf16Logits>
 __device__ __forceinline__ void topk16(const void *__restrict__ logits, int t, int E, int k, int li,
                                        int32_t *__restrict__ ids, float *__restrict__ wts,
-                                       int32_t *__restrict__ p_ids, float *__restrict__ p_w,
-                                       int32_t *sm_ids, float *sm_w) {
+                                       int32_t *__restrict__ p_ids, float *__restrict__ p_w) {
   uint64_t key[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
@@ -125,8 +123,6 @@ __device__ __forceinline__ void topk16(const void *__restrict__ logits, int t, i
       wts[(size_t)t * k + j] = w;
       if (p_ids) p_ids[(size_t)t * k + j] = si[s];
       if (p_w) p_w[(size_t)t * k + j] = w;
-      if (sm_ids) sm_ids[j] = si[s];
-      if (sm_w) sm_w[j] = w;
     }
   }
 }
@@ -210,7 +206,7 @@ __global__ __launch_bounds__(256) void route_kernel(const void *__restrict__ log
   const int t0 = blockIdx.x * 16 + (threadIdx.x >> 6) * 4;  // first token of this wave
   if (blockIdx.x == 0 && threadIdx.x == 0) flags[0] = 0u;
   if (t0 >= T) return;
-  if (t < T) topk16<kPer, kBf16Logits>(logits, t, E, k, li, ids, wts, p_ids, p_w, nullptr, nullptr);
+  if (t < T) topk16<kPer, kBf16Logits>(logits, t, E, k, li, ids, wts, p_ids, p_w);
   if (stage_rows) rows_to_f16<kPermInt4>(hidden, t0, T, H, lane, x16, rowscale);
 }
 
@@ -266,35 +262,25 @@ __device__ __forceinline__ void scan_experts_wave(const int32_t *cnt, int E, int
 }
 
 // ---------------------------------------------------------------------------
-// T <= 64: routing and grouping in one workgroup of 1024 threads.  The 16
-// waves take 4 tokens each for the top-k (16 lanes per token), keeping ids
-// and weights in LDS; for the prefill path they also stage the hidden rows in
-// FP16.  Then one 64-bit token mask per expert gives the counts (popcount) and
-// the stable rank of every token inside its expert (popcount of the mask bits
-// below it).
+// T <= 64: grouping in one workgroup of 1024 threads, after route_kernel's
+// top-k (whose 16-lane-per-token selection is VALU work worth spreading over
+// several CUs).  One 64-bit token mask per expert gives the counts (popcount)
+// and the stable rank of every token inside its expert (popcount of the mask
+// bits below it).
 // ---------------------------------------------------------------------------
-template <int kPer, bool kBf16Logits, bool kPermInt4>
-__global__ __launch_bounds__(1024) void route_small_kernel(
-    const void *__restrict__ logits, const uint16_t *__restrict__ hidden, int T, int E, int H,
-    int k, int32_t *__restrict__ ids, float *__restrict__ wts, _Float16 *__restrict__ x16,
-    float *__restrict__ rowscale, uint32_t *__restrict__ flags, int stage_rows,
-    int32_t *__restrict__ offsets, int32_t *__restrict__ mtile, int4 *__restrict__ einfo,
-    int32_t *__restrict__ sorted_slots, int4 *__restrict__ rowinfo, int32_t *__restrict__ inv_pos,
-    int32_t *__restrict__ p_ids, float *__restrict__ p_w, int32_t *__restrict__ p_offsets,
-    int32_t *__restrict__ p_sorted_tok, int32_t *__restrict__ p_inv) {
+__global__ __launch_bounds__(1024) void group_small_kernel(
+    const int32_t *__restrict__ ids, const float *__restrict__ wts, const float *__restrict__ rowscale,
+    int T, int E, int k, int32_t *__restrict__ offsets, int32_t *__restrict__ mtile,
+    int4 *__restrict__ einfo, int32_t *__restrict__ sorted_slots, int4 *__restrict__ rowinfo,
+    int32_t *__restrict__ inv_pos, int32_t *__restrict__ p_offsets, int32_t *__restrict__ p_sorted_tok,
+    int32_t *__restrict__ p_inv) {
   __shared__ int32_t sm_ids[64 * 64];
-  __shared__ float sm_w[64 * 64];
   __shared__ uint64_t mask[kMaxExperts];
   __shared__ int32_t cnt[kMaxExperts];
   __shared__ int32_t off[kMaxExperts];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, li = lane & 15;
-  if (tid == 0) flags[0] = 0u;
+  const int tid = threadIdx.x, lane = tid & 63;
   for (int e = tid; e < E; e += 1024) mask[e] = 0ull;
-  const int t = wave * 4 + (lane >> 4);
-  if (t < T)
-    topk16<kPer, kBf16Logits>(logits, t, E, k, li, ids, wts, p_ids, p_w, sm_ids + t * k,
-                              sm_w + t * k);
-  if (stage_rows && wave * 4 < T) rows_to_f16<kPermInt4>(hidden, wave * 4, T, H, lane, x16, rowscale);
+  for (int i = tid; i < T * k; i += 1024) sm_ids[i] = ids[i];
   __syncthreads();
   for (int i = tid; i < T * k; i += 1024) atomicOr(&mask[sm_ids[i]], 1ull << (i / k));
   __syncthreads();
@@ -307,8 +293,8 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
     const uint64_t below = tt == 0 ? 0ull : (~0ull >> (64 - tt));
     const int pos = off[e] + __popcll(mask[e] & below);
     sorted_slots[pos] = i;
-    const float rs = stage_rows ? rowscale[tt] : 0.f;
-    rowinfo[pos] = int4{i, tt, __builtin_bit_cast(int, rs), __builtin_bit_cast(int, sm_w[i])};
+    const float rs = rowscale ? rowscale[tt] : 0.f;
+    rowinfo[pos] = int4{i, tt, __builtin_bit_cast(int, rs), __builtin_bit_cast(int, wts[i])};
     inv_pos[i] = pos;
     if (p_sorted_tok) p_sorted_tok[pos] = tt;
     if (p_inv) p_inv[i] = pos;
@@ -437,17 +423,6 @@ template <int kPer, bool kBf16, bool kPerm>
 static hipError_t route_dispatch(const LayerDims &L, const FwdPtrs &P, const Workspace &W,
                                  bool stage_rows, hipStream_t s) {
   char *ws = P.ws;
-  if (P.T <= 64) {
-    hipLaunchKernelGGL((route_small_kernel<kPer, kBf16, kPerm>), dim3(1), dim3(1024), 0, s,
-                       P.logits, P.hidden, P.T, L.E, L.H, L.k, (int32_t *)(ws + W.topk_ids),
-                       (float *)(ws + W.topk_w), (_Float16 *)(ws + W.x16),
-                       (float *)(ws + W.rowscale), (uint32_t *)(ws + W.flags), (int)stage_rows,
-                       (int32_t *)(ws + W.offsets), (int32_t *)(ws + W.mtile),
-                       (int4 *)(ws + W.active), (int32_t *)(ws + W.sorted_slots),
-                       (int4 *)(ws + W.rowinfo), (int32_t *)(ws + W.inv_pos), P.p_ids, P.p_w,
-                       P.p_offsets, P.p_sorted_tok, P.p_inv);
-    return hipGetLastError();
-  }
   hipLaunchKernelGGL((route_kernel<kPer, kBf16, kPerm>), dim3((P.T + 15) / 16), dim3(256), 0, s,
                      P.logits, P.hidden, P.T, L.E, L.H, L.k, (int32_t *)(ws + W.topk_ids),
                      (float *)(ws + W.topk_w), (_Float16 *)(ws + W.x16), (float *)(ws + W.rowscale),
@@ -478,7 +453,14 @@ hipError_t launch_route(const LayerDims &L, const FwdPtrs &P, const Workspace &W
 hipError_t launch_permute(const LayerDims &L, const FwdPtrs &P, const Workspace &W, bool decode,
                           hipStream_t s) {
   char *ws = P.ws;
-  if (P.T <= 64) return hipSuccess;  // grouped by the routing kernel
+  if (P.T <= 64) {
+    hipLaunchKernelGGL(group_small_kernel, dim3(1), dim3(1024), 0, s, (const int32_t *)(ws + W.topk_ids),
+                       (const float *)(ws + W.topk_w), decode ? (const float *)nullptr : (const float *)(ws + W.rowscale),
+                       P.T, L.E, L.k, (int32_t *)(ws + W.offsets), (int32_t *)(ws + W.mtile),
+                       (int4 *)(ws + W.active), (int32_t *)(ws + W.sorted_slots), (int4 *)(ws + W.rowinfo),
+                       (int32_t *)(ws + W.inv_pos), P.p_offsets, P.p_sorted_tok, P.p_inv);
+    return hipGetLastError();
+  }
   int nc, chunk;
   permute_chunks(P.T, &nc, &chunk);
   int32_t *cnt = (int32_t *)(ws + W.chunks);
