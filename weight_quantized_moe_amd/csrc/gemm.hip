@@ -72,10 +72,7 @@ __device__ __forceinline__ void store_h(const GemmArgs &a, int r, int col, float
 // is persistent: resident blocks loop over (expert, tile group) units.
 // ===========================================================================
 constexpr int kDecodeWaves = 8;
-#ifndef MQ_DECODE_DEPTH
-#define MQ_DECODE_DEPTH 4
-#endif
-constexpr int kD = MQ_DECODE_DEPTH;  // weight groups in flight per wave (even)
+constexpr int kD = 4;  // weight groups in flight per wave (even; 6 and 8 measured slower)
 static_assert(kD % 2 == 0, "groups are prefetched in pairs");
 
 // Registers of one group in flight.  Scales stay raw until use: a conversion
@@ -370,18 +367,14 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode(GemmArgs a) {
 // up columns; wave (wm, wn) holds gate columns 64 wn + [0, 64) in tiles 0-1
 // and the matching up columns in tiles 2-3, so SwiGLU runs in registers.
 //
-// Two pipelines (NSTAGE):
-//  2: double-buffered LDS, one block (4 waves) per CU; the HBM loads of k step
-//     s are issued two steps ahead into one of two register sets, written to
-//     LDS one step ahead; one barrier per step.
-//  1: one LDS buffer, two blocks per CU; loads one step ahead.
+// Pipeline: one LDS buffer, two blocks per CU (one block's barriers overlap
+// the other's work); the HBM loads of k step s + 1 are issued before step s's
+// MFMAs.  (A double-buffered variant with one block per CU and loads two steps
+// ahead measured slower.)
 // Tiles are numbered (M-tile, N-tile) with N fastest and dealt to the 8 XCDs
 // in contiguous ranges (blocks are dispatched to XCDs round robin), so tiles
 // that share activation rows or an expert's weights run on the same L2.
 // ===========================================================================
-#ifndef MQ_PREFILL_NSTAGE
-#define MQ_PREFILL_NSTAGE 1
-#endif
 constexpr int kBM = kPrefillBM, kBN = 256, kBK = 64, kLD = kBK + 8;  // kLD in halves
 constexpr size_t kPrefillStage = (size_t)(kBM + kBN) * kLD * 2;        // bytes per LDS stage
 
@@ -402,11 +395,11 @@ struct PrefillRegs {
   uint32_t s[4];  // INT4: FP16 scale bits; FP8: FP32 scale bits; NVFP4: E4M3 scale byte
 };
 
-template <int FMT, int STAGE, int NSTAGE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NSTAGE == 2 ? 1 : 2, NSTAGE == 2 ? 1 : 2)))
+template <int FMT, int STAGE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_prefill(GemmArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  float *colinv = (float *)(smem + NSTAGE * kPrefillStage);  // [kBN]: 2^-p of each B row
+  float *colinv = (float *)(smem + kPrefillStage);  // [kBN]: 2^-p of each B row
   float *rowfs = colinv + kBN;                                // [kBN]: 2^p of each B row
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
@@ -522,8 +515,8 @@ void gemm_prefill(GemmArgs a) {
     }
   };
   float rowf[4] = {1.f, 1.f, 1.f, 1.f};
-  auto stage = [&](const PrefillRegs<FMT> &R, int buf) {
-    _Float16 *As = (_Float16 *)(smem + buf * kPrefillStage);
+  auto stage = [&](const PrefillRegs<FMT> &R) {
+    _Float16 *As = (_Float16 *)smem;
     _Float16 *Bs = As + kBM * kLD;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
@@ -577,8 +570,8 @@ void gemm_prefill(GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[tm][tn][i] = 0.f;
 
-  auto compute = [&](int buf) {
-    const _Float16 *As = (const _Float16 *)(smem + buf * kPrefillStage);
+  auto compute = [&]() {
+    const _Float16 *As = (const _Float16 *)smem;
     const _Float16 *Bs = As + kBM * kLD;
 #pragma unroll
     for (int s = 0; s < kBK / 16; ++s) {
@@ -595,39 +588,14 @@ void gemm_prefill(GemmArgs a) {
     }
   };
 
-  if constexpr (NSTAGE == 2) {
-    PrefillRegs<FMT> R0, R1;
-    gload(R0, 0);
-    gload(R1, 1);
-    stage(R0, 0);
-    if (2 < nK) gload(R0, 2);
+  PrefillRegs<FMT> R;
+  gload(R, 0);
+  for (int ks = 0; ks < nK; ++ks) {
     __syncthreads();
-    // nK is even (K is a multiple of 128): iterations in pairs keep the
-    // register-set index static
-    for (int ks = 0; ks < nK; ks += 2) {
-      // even step ks: buffer 0 computes, step ks+1 (set R1) goes to buffer 1
-      stage(R1, 1);
-      if (ks + 3 < nK) gload(R1, ks + 3);
-      compute(0);
-      __syncthreads();
-      // odd step ks+1: buffer 1 computes, step ks+2 (set R0) goes to buffer 0
-      if (ks + 2 < nK) {
-        stage(R0, 0);
-        if (ks + 4 < nK) gload(R0, ks + 4);
-      }
-      compute(1);
-      __syncthreads();
-    }
-  } else {
-    PrefillRegs<FMT> R;
-    gload(R, 0);
-    for (int ks = 0; ks < nK; ++ks) {
-      __syncthreads();
-      stage(R, 0);
-      __syncthreads();
-      if (ks + 1 < nK) gload(R, ks + 1);
-      compute(0);
-    }
+    stage(R);
+    __syncthreads();
+    if (ks + 1 < nK) gload(R, ks + 1);
+    compute();
   }
 
   // ---- epilogue.  The MFMA ran as C[n][m] (weights as its A operand), so
@@ -871,19 +839,18 @@ static hipError_t run_decode_ks(GemmArgs a, int slots, const GemmLaunch &s) {
 
 template <int FMT, int STAGE>
 static hipError_t run_prefill(GemmArgs a, int64_t R, const GemmLaunch &s) {
-  constexpr int NS = MQ_PREFILL_NSTAGE;
   // gate/up: I is a multiple of 128, so kBN / 2 = 128 columns tile it exactly
   a.tiles = STAGE == 0 ? a.I / (kBN / 2) : (a.H + kBN - 1) / kBN;
   const int64_t max_mt = R / kBM + a.E;  // >= sum_e ceil(n_e / kBM)
   const int64_t grid = 8 * ((max_mt * a.tiles + 7) / 8);
-  const size_t lds = NS * kPrefillStage + 2 * kBN * sizeof(float);
+  const size_t lds = kPrefillStage + 2 * kBN * sizeof(float);
   static bool attr_set = false;
   if (!attr_set) {
-    (void)hipFuncSetAttribute((const void *)gemm_prefill<FMT, STAGE, NS>,
+    (void)hipFuncSetAttribute((const void *)gemm_prefill<FMT, STAGE>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     attr_set = true;
   }
-  hipExtLaunchKernelGGL((gemm_prefill<FMT, STAGE, NS>), dim3((unsigned)grid), dim3(256), (uint32_t)lds, s.stream,
+  hipExtLaunchKernelGGL((gemm_prefill<FMT, STAGE>), dim3((unsigned)grid), dim3(256), (uint32_t)lds, s.stream,
                         s.start, s.stop, 0u, a);
   return hipGetLastError();
 }
