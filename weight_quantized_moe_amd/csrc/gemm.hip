@@ -605,18 +605,19 @@ void gemm_prefill(GemmArgs a) {
   const float ginv = FMT == FMT_NVFP4 ? 1.0f / a.gscale[e] : 1.0f;
   const int cl = 4 * (lane >> 5);
   uint32_t sat = 0u;
+  float vmax = 0.f, vnan = 0.f;  // down: largest |value| before the FP16 clamp; NaN sentinel
+  typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+  if constexpr (STAGE == 0) {
+    // gate/up: SwiGLU, then 8 bytes per lane straight to the rows of h
 #pragma unroll
-  for (int tm = 0; tm < 2; ++tm) {
-    const int row = wm * 64 + tm * 32 + j;
-    if (row >= nrows) continue;
-    const int r = rbeg + row;
-    const int4 ri = a.rowinfo[r];
-    const int slot = ri.x;
-    const float rsc = __builtin_bit_cast(float, STAGE == 0 ? ri.z : ri.w) * ginv;
+    for (int tm = 0; tm < 2; ++tm) {
+      const int row = wm * 64 + tm * 32 + j;
+      if (row >= nrows) continue;
+      const int r = rbeg + row;
+      const float rsc = __builtin_bit_cast(float, a.rowinfo[r].z) * ginv;
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int c4 = 8 * g4 + cl;  // first of this lane's 4 columns in the tile
-      if (STAGE == 0) {
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int c4 = 8 * g4 + cl;  // first of this lane's 4 columns in the tile
 #pragma unroll
         for (int tn = 0; tn < 2; ++tn) {
           const f4 ig = *(const f4 *)(colinv + bl[tn] - j + c4);
@@ -631,23 +632,62 @@ void gemm_prefill(GemmArgs a) {
             sat |= hc != hv;
             o[i >> 1][i & 1] = (_Float16)hc;
           }
-          typedef uint32_t u2 __attribute__((ext_vector_type(2)));
           *(u2 *)(a.h_out + (size_t)r * a.I + tcol[tn] + c4) = u2{as_u32(o[0]), as_u32(o[1])};
-        }
-      } else {
-#pragma unroll
-        for (int tn = 0; tn < 4; ++tn) {
-          if (tcol[tn] >= N) continue;
-          const f4 ic = *(const f4 *)(colinv + bl[tn] - j + c4);
-          h2 o[2];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) o[i >> 1][i & 1] = to_f16_sat(acc[tm][tn][4 * g4 + i] * (rsc * ic[i]), sat);
-          typedef uint32_t u2 __attribute__((ext_vector_type(2)));
-          *(u2 *)(a.partial + (size_t)slot * a.H + tcol[tn] + c4) = u2{as_u32(o[0]), as_u32(o[1])};
         }
       }
     }
+  } else {
+    // down: the rows go to scattered slots of the partial buffer, so each
+    // 32-row half of the wave's tile is converted and transposed through LDS
+    // and every store writes 256 contiguous bytes of a row (16 per lane)
+    // instead of 8 bytes in each of 32 rows per instruction.
+    constexpr int kTL = 128 + 8;  // LDS row stride in halves
+    static_assert(4 * 32 * kTL * 2 <= (int)kPrefillStage, "transpose buffers fit the tile buffer");
+    _Float16 *tb = (_Float16 *)smem + wave * 32 * kTL;
+    const int ocol = tcol[0];  // first output column of the wave
+    __syncthreads();           // every wave is done reading the k-step tiles
+#pragma unroll
+    for (int tm = 0; tm < 2; ++tm) {
+      const int row = wm * 64 + tm * 32 + j;
+      float rsc = 0.f;  // rows past the expert's end: zeros, never stored
+      if (row < nrows) rsc = __builtin_bit_cast(float, a.rowinfo[rbeg + row].w) * ginv;
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int c4 = 8 * g4 + cl;
+#pragma unroll
+        for (int tn = 0; tn < 4; ++tn) {
+          const f4 ic = *(const f4 *)(colinv + bl[tn] - j + c4);
+          h2 o[2];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float v = acc[tm][tn][4 * g4 + i] * (rsc * ic[i]);
+            vmax = fmaxf(vmax, fabsf(v));
+            vnan = __builtin_fmaf(v, 0.f, vnan);  // stays 0 unless v is NaN or infinite
+            o[i >> 1][i & 1] = (_Float16)fminf(fmaxf(v, -65504.f), 65504.f);
+          }
+          *(u2 *)(tb + j * kTL + tn * 32 + c4) = u2{as_u32(o[0]), as_u32(o[1])};
+          __builtin_amdgcn_sched_barrier(0);  // column group by group (register pressure)
+        }
+      }
+      // the wave reads back what its own lanes wrote: its LDS operations run
+      // in order, and the compiler keeps them ordered (same buffer)
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      __builtin_amdgcn_wave_barrier();
+      const int ch = lane & 15;
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int rr = it * 4 + (lane >> 4);
+        const int orow = wm * 64 + tm * 32 + rr;
+        const u4 v = *(const u4 *)(tb + rr * kTL + ch * 8);
+        if (orow < nrows && ocol + ch * 8 < N)  // a half tile ends at H
+          *(u4 *)(a.partial + (size_t)a.rowinfo[rbeg + orow].x * a.H + ocol + ch * 8) = v;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_wave_barrier();
+    }
   }
+  sat |= !(vmax <= 65504.f) || vnan != 0.f;  // NaN counts as saturated, as in to_f16_sat
   if (__builtin_amdgcn_ballot_w64(sat != 0u) != 0ull && lane == 0) atomicOr(a.flags, 1u);
 }
 
