@@ -15,6 +15,7 @@
 // lane therefore owns one output column, so a per-column scale is one scalar
 // per lane.
 #include <algorithm>
+#include <type_traits>
 
 #include <hip/hip_ext.h>
 
@@ -443,11 +444,18 @@ void gemm_prefill(GemmArgs a) {
   if (FMT != FMT_NVFP4) {
     const int gr = grow(tid);
     float m = 0.f;
-    for (int g = 0; g < G; ++g) {
-      const float sv = FMT == FMT_INT4
-                           ? (float)((const _Float16 *)a.scale)[((size_t)e * N + gr) * G + g]
-                           : ((const float *)a.scale)[((size_t)e * (N / 128) + gr / 128) * G + g];
-      m = fmaxf(m, fabsf(sv));
+    // 8 scale loads in flight per round trip (indices clamped to the last
+    // group: a repeated value does not change the max)
+    for (int g0 = 0; g0 < G; g0 += 8) {
+      float sv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int g = min(g0 + u, G - 1);
+        sv[u] = FMT == FMT_INT4 ? (float)((const _Float16 *)a.scale)[((size_t)e * N + gr) * G + g]
+                                : ((const float *)a.scale)[((size_t)e * (N / 128) + gr / 128) * G + g];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) m = fmaxf(m, fabsf(sv[u]));
     }
     float inv;
     rowfs[tid] = row_pow2(m * (FMT == FMT_INT4 ? 8.f : 448.f), &inv);
@@ -570,7 +578,11 @@ void gemm_prefill(GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[tm][tn][i] = 0.f;
 
-  auto compute = [&]() {
+  // NV: the wave's 32-row M subtiles that hold grouped rows of the expert
+  // (the last M tile of an expert is often partly empty; MFMAs of empty
+  // subtiles are skipped, which frees the matrix unit for the other block)
+  auto compute = [&](auto nv_c) {
+    constexpr int NV = decltype(nv_c)::value;
     const _Float16 *As = (const _Float16 *)smem;
     const _Float16 *Bs = As + kBM * kLD;
 #pragma unroll
@@ -578,25 +590,35 @@ void gemm_prefill(GemmArgs a) {
       const int kk = s * 16 + 8 * (lane >> 5);
       h8 av[2], bv[4];
 #pragma unroll
-      for (int tm = 0; tm < 2; ++tm) av[tm] = *(const h8 *)(As + (wm * 64 + tm * 32 + j) * kLD + kk);
+      for (int tm = 0; tm < NV; ++tm) av[tm] = *(const h8 *)(As + (wm * 64 + tm * 32 + j) * kLD + kk);
 #pragma unroll
-      for (int tn = 0; tn < 4; ++tn) bv[tn] = *(const h8 *)(Bs + bl[tn] * kLD + kk);
+      for (int tn = 0; tn < 4; ++tn)
+        if (NV > 0) bv[tn] = *(const h8 *)(Bs + bl[tn] * kLD + kk);
 #pragma unroll
-      for (int tm = 0; tm < 2; ++tm)
+      for (int tm = 0; tm < NV; ++tm)
 #pragma unroll
         for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = mfma32(bv[tn], av[tm], acc[tm][tn]);
     }
   };
-
-  PrefillRegs<FMT> R;
-  gload(R, 0);
-  for (int ks = 0; ks < nK; ++ks) {
-    __syncthreads();
-    stage(R);
-    __syncthreads();
-    if (ks + 1 < nK) gload(R, ks + 1);
-    compute();
-  }
+  // every variant runs the same barriers: all waves take part in the staging
+  auto main_loop = [&](auto nv_c) {
+    PrefillRegs<FMT> R;
+    gload(R, 0);
+    for (int ks = 0; ks < nK; ++ks) {
+      __syncthreads();
+      stage(R);
+      __syncthreads();
+      if (ks + 1 < nK) gload(R, ks + 1);
+      compute(nv_c);
+    }
+  };
+  const int nv = min(2, max(0, (nrows - wm * 64 + 31) / 32));  // wave-uniform
+  if (nv == 2)
+    main_loop(std::integral_constant<int, 2>{});
+  else if (nv == 1)
+    main_loop(std::integral_constant<int, 1>{});
+  else
+    main_loop(std::integral_constant<int, 0>{});
 
   // ---- epilogue.  The MFMA ran as C[n][m] (weights as its A operand), so
   // lane l holds grouped row m = l % 32 of each M tile and, in register v,
