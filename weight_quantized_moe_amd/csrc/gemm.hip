@@ -191,10 +191,24 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode(GemmArgs a) {
       // rows, each scaled by a power of two into FP16 (max |x| of the row into
       // [2^14, 2^15), so every BF16 value above max * 2^-31 converts exactly)
       // and stored in the INT4 k order for INT4; the epilogue multiplies the
-      // row back.  Down: the grouped FP16 intermediate rows (permuted here for
-      // INT4).
+      // row back.  For rows of up to 2048 values the routing kernel has found
+      // each row's power of two; longer rows are scanned here first.  Down:
+      // the grouped FP16 intermediate rows (permuted here for INT4).
       __syncthreads();
-      {
+      if (STAGE == 0 && K <= 2048) {
+        // the routing kernel left each row's power of two 2^s in its record
+        // (row scale bits); convert with the exact inverse 2^-s
+        const int cpr = K >> 3;
+        for (int idx = threadIdx.x; idx < nrows * cpr; idx += 64 * kDecodeWaves) {
+          const int m = idx / cpr, c = idx - m * cpr;
+          const int4 ri = a.rowinfo[r0 + mc + m];
+          const float down = __builtin_bit_cast(float, (uint32_t)(254u << 23) - (uint32_t)ri.z);
+          u4 v = bf16x8_to_f16x8(*(const u4 *)(a.hidden + (size_t)ri.y * K + c * 8), down);
+          if (FMT == FMT_INT4) v = perm_0415(v);
+          *(u4 *)(As + m * lda + c * 8) = v;
+        }
+        if (threadIdx.x < nrows) sm_rscale[threadIdx.x] = __builtin_bit_cast(float, a.rowinfo[r0 + mc + threadIdx.x].z);
+      } else {
         const int cpr = K >> 3;
         if (STAGE == 0) {
           if (threadIdx.x < 16) sm_rmax[threadIdx.x] = 0u;

@@ -70,10 +70,8 @@ __device__ __forceinline__ float max16f(float v) {
 // half of a real key is never 0 since E <= 512), so the k winners are always k
 // distinct valid experts.  Results go to ids/wts (and the probe arrays).
 template <int kPer, bool kBf16Logits>
-__device__ __forceinline__ void topk16(const void *__restrict__ logits, int t, int E, int k, int li,
-                                       int32_t *__restrict__ ids, float *__restrict__ wts,
-                                       int32_t *__restrict__ p_ids, float *__restrict__ p_w) {
-  uint64_t key[kPer];
+__device__ __forceinline__ void topk16_keys(const void *__restrict__ logits, int t, int E, int li,
+                                            uint64_t *key) {
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int e = li + 16 * i;
@@ -87,6 +85,11 @@ __device__ __forceinline__ void topk16(const void *__restrict__ logits, int t, i
       key[i] = ((uint64_t)ordered_key(v) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
     }
   }
+}
+template <int kPer>
+__device__ __forceinline__ void topk16_select(uint64_t *key, int t, int k, int li,
+                                              int32_t *__restrict__ ids, float *__restrict__ wts,
+                                              int32_t *__restrict__ p_ids, float *__restrict__ p_w) {
   float sv[4] = {0.f, 0.f, 0.f, 0.f};  // slot j = li + 16 s held by this lane
   int si[4] = {0, 0, 0, 0};
   float vmax = 0.f;
@@ -125,6 +128,14 @@ __device__ __forceinline__ void topk16(const void *__restrict__ logits, int t, i
       if (p_w) p_w[(size_t)t * k + j] = w;
     }
   }
+}
+template <int kPer, bool kBf16Logits>
+__device__ __forceinline__ void topk16(const void *__restrict__ logits, int t, int E, int k, int li,
+                                       int32_t *__restrict__ ids, float *__restrict__ wts,
+                                       int32_t *__restrict__ p_ids, float *__restrict__ p_w) {
+  uint64_t key[kPer];
+  topk16_keys<kPer, kBf16Logits>(logits, t, E, li, key);
+  topk16_select<kPer>(key, t, k, li, ids, wts, p_ids, p_w);
 }
 
 // Hidden rows of the wave's 4 tokens -> FP16 scaled by a power of two each,
@@ -188,7 +199,28 @@ __device__ __forceinline__ void rows_to_f16(const uint16_t *__restrict__ hidden,
   }
 }
 
-// General-T routing: 16 tokens per block of 256 threads.  Also zeroes the
+// Decode: only the power of two of each hidden row (rowscale[t] = 2^s), for
+// the wave's 4 tokens (rows of H <= 2048, read once into registers).  The
+// decode gate/up GEMM scales the rows into FP16 itself while staging them.
+__device__ __forceinline__ void row_scale_regs(const u4 (&v)[4][4], int t0, int T, int H, int lane,
+                                               float *__restrict__ rowscale) {
+  float m[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (t0 + r < T && lane * 8 + 512 * u < H) m[r] = absmax_bf16x8(v[r][u], m[r]);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    m[r] = max16f(m[r]);
+    m[r] = fmaxf(m[r], __shfl_xor(m[r], 16, 64));
+    m[r] = fmaxf(m[r], __shfl_xor(m[r], 32, 64));
+    if (lane == 0 && t0 + r < T) rowscale[t0 + r] = pow2f(row_shift(m[r]));
+  }
+}
+
+// General-T routing: 16 lanes per token, 4 tokens per wave, one or four
+// waves per block.  Also zeroes the
 // flags word and, for the prefill path (stage_rows), stages the hidden rows
 // in FP16.
 template <int kPer, bool kBf16Logits, bool kPermInt4>
@@ -202,10 +234,27 @@ __global__ __launch_bounds__(256) void route_kernel(const void *__restrict__ log
                                                     int32_t *__restrict__ p_ids,
                                                     float *__restrict__ p_w, int stage_rows) {
   const int lane = threadIdx.x & 63, li = lane & 15;
-  const int t = blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int t0 = blockIdx.x * 16 + (threadIdx.x >> 6) * 4;  // first token of this wave
+  const int tpb = blockDim.x >> 4;  // tokens per block: 16 lanes each
+  const int t = blockIdx.x * tpb + (threadIdx.x >> 4);
+  const int t0 = blockIdx.x * tpb + (threadIdx.x >> 6) * 4;  // first token of this wave
   if (blockIdx.x == 0 && threadIdx.x == 0) flags[0] = 0u;
   if (t0 >= T) return;
+  if (stage_rows == 2 && H <= 2048) {
+    // decode: the rows' loads and the logits' loads in flight together
+    uint64_t key[kPer];
+    if (t < T) topk16_keys<kPer, kBf16Logits>(logits, t, E, li, key);
+    u4 v[4][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        v[r][u] = t0 + r < T && lane * 8 + 512 * u < H
+                      ? *(const u4 *)(hidden + (size_t)(t0 + r) * H + lane * 8 + 512 * u)
+                      : u4{0u, 0u, 0u, 0u};
+    row_scale_regs(v, t0, T, H, lane, rowscale);
+    if (t < T) topk16_select<kPer>(key, t, k, li, ids, wts, p_ids, p_w);
+    return;
+  }
   if (t < T) topk16<kPer, kBf16Logits>(logits, t, E, k, li, ids, wts, p_ids, p_w);
   if (stage_rows) rows_to_f16<kPermInt4>(hidden, t0, T, H, lane, x16, rowscale);
 }
@@ -421,18 +470,21 @@ __global__ __launch_bounds__(256) void scatter_kernel(
 // ---------------------------------------------------------------------------
 template <int kPer, bool kBf16, bool kPerm>
 static hipError_t route_dispatch(const LayerDims &L, const FwdPtrs &P, const Workspace &W,
-                                 bool stage_rows, hipStream_t s) {
+                                 int stage_rows, hipStream_t s) {
   char *ws = P.ws;
-  hipLaunchKernelGGL((route_kernel<kPer, kBf16, kPerm>), dim3((P.T + 15) / 16), dim3(256), 0, s,
+  // decode row scales: one wave (4 tokens) per workgroup spreads the row
+  // reads over more CUs; otherwise 16 tokens per workgroup
+  const int threads = stage_rows == 2 ? 64 : 256, tpb = threads / 16;
+  hipLaunchKernelGGL((route_kernel<kPer, kBf16, kPerm>), dim3((P.T + tpb - 1) / tpb), dim3(threads), 0, s,
                      P.logits, P.hidden, P.T, L.E, L.H, L.k, (int32_t *)(ws + W.topk_ids),
                      (float *)(ws + W.topk_w), (_Float16 *)(ws + W.x16), (float *)(ws + W.rowscale),
-                     (uint32_t *)(ws + W.flags), P.p_ids, P.p_w, (int)stage_rows);
+                     (uint32_t *)(ws + W.flags), P.p_ids, P.p_w, stage_rows);
   return hipGetLastError();
 }
 
 template <int kPer>
 static hipError_t route_dispatch2(const LayerDims &L, const FwdPtrs &P, const Workspace &W,
-                                  bool stage_rows, hipStream_t s) {
+                                  int stage_rows, hipStream_t s) {
   const bool perm = L.fmt == FMT_INT4;
   if (P.logits_bf16)
     return perm ? route_dispatch<kPer, true, true>(L, P, W, stage_rows, s)
@@ -443,8 +495,10 @@ static hipError_t route_dispatch2(const LayerDims &L, const FwdPtrs &P, const Wo
 
 hipError_t launch_route(const LayerDims &L, const FwdPtrs &P, const Workspace &W, bool decode,
                         hipStream_t s) {
-  // the decode GEMMs scale the hidden rows themselves; only prefill stages them
-  const bool stage_rows = !decode;
+  // prefill: FP16 rows and their scales (1); decode with H <= 2048: the
+  // scales only (2), the decode gate/up GEMM converts the rows it stages;
+  // larger decode rows: the GEMM takes the scales too (0)
+  const int stage_rows = !decode ? 1 : L.H <= 2048 ? 2 : 0;
   if (L.E <= 128) return route_dispatch2<8>(L, P, W, stage_rows, s);
   if (L.E <= 256) return route_dispatch2<16>(L, P, W, stage_rows, s);
   return route_dispatch2<32>(L, P, W, stage_rows, s);
@@ -455,7 +509,7 @@ hipError_t launch_permute(const LayerDims &L, const FwdPtrs &P, const Workspace 
   char *ws = P.ws;
   if (P.T <= 64) {
     hipLaunchKernelGGL(group_small_kernel, dim3(1), dim3(1024), 0, s, (const int32_t *)(ws + W.topk_ids),
-                       (const float *)(ws + W.topk_w), decode ? (const float *)nullptr : (const float *)(ws + W.rowscale),
+                       (const float *)(ws + W.topk_w), decode && L.H > 2048 ? (const float *)nullptr : (const float *)(ws + W.rowscale),
                        P.T, L.E, L.k, (int32_t *)(ws + W.offsets), (int32_t *)(ws + W.mtile),
                        (int4 *)(ws + W.active), (int32_t *)(ws + W.sorted_slots), (int4 *)(ws + W.rowinfo),
                        (int32_t *)(ws + W.inv_pos), P.p_offsets, P.p_sorted_tok, P.p_inv);
@@ -471,7 +525,7 @@ hipError_t launch_permute(const LayerDims &L, const FwdPtrs &P, const Workspace 
                      (int4 *)(ws + W.active), P.p_offsets);
   hipLaunchKernelGGL(scatter_kernel, dim3(nc), dim3(256), (size_t)L.E * (4 * 8 + 4 * 4 + 4), s,
                      (const int32_t *)(ws + W.topk_ids), (const float *)(ws + W.topk_w),
-                     decode ? nullptr : (const float *)(ws + W.rowscale), P.T, L.E, L.k, chunk,
+                     decode && L.H > 2048 ? nullptr : (const float *)(ws + W.rowscale), P.T, L.E, L.k, chunk,
                      (const int32_t *)cnt, (int32_t *)(ws + W.sorted_slots),
                      (int4 *)(ws + W.rowinfo), (int32_t *)(ws + W.inv_pos), P.p_sorted_tok,
                      P.p_inv);
