@@ -203,7 +203,7 @@ __device__ __forceinline__ void rows_to_f16(const uint16_t *__restrict__ hidden,
 // the wave's 4 tokens (rows of H <= 2048, read once into registers).  The
 // decode gate/up GEMM scales the rows into FP16 itself while staging them.
 __device__ __forceinline__ void row_scale_regs(const u4 (&v)[4][4], int t0, int T, int H, int lane,
-                                               float *__restrict__ rowscale) {
+                                               float *__restrict__ rowscale, float *down = nullptr) {
   float m[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int r = 0; r < 4; ++r)
@@ -215,7 +215,9 @@ __device__ __forceinline__ void row_scale_regs(const u4 (&v)[4][4], int t0, int 
     m[r] = max16f(m[r]);
     m[r] = fmaxf(m[r], __shfl_xor(m[r], 16, 64));
     m[r] = fmaxf(m[r], __shfl_xor(m[r], 32, 64));
-    if (lane == 0 && t0 + r < T) rowscale[t0 + r] = pow2f(row_shift(m[r]));
+    const int sh = row_shift(m[r]);
+    if (lane == 0 && t0 + r < T) rowscale[t0 + r] = pow2f(sh);
+    if (down) down[r] = pow2f(-sh);
   }
 }
 
@@ -239,8 +241,10 @@ __global__ __launch_bounds__(256) void route_kernel(const void *__restrict__ log
   const int t0 = blockIdx.x * tpb + (threadIdx.x >> 6) * 4;  // first token of this wave
   if (blockIdx.x == 0 && threadIdx.x == 0) flags[0] = 0u;
   if (t0 >= T) return;
-  if (stage_rows == 2 && H <= 2048) {
-    // decode: the rows' loads and the logits' loads in flight together
+  if (stage_rows != 0 && H <= 2048) {
+    // rows of up to 2048 values: the rows' loads and the logits' loads in
+    // flight together, each row read once (decode keeps only its scale,
+    // prefill also writes the FP16 row)
     uint64_t key[kPer];
     if (t < T) topk16_keys<kPer, kBf16Logits>(logits, t, E, li, key);
     u4 v[4][4];
@@ -251,7 +255,18 @@ __global__ __launch_bounds__(256) void route_kernel(const void *__restrict__ log
         v[r][u] = t0 + r < T && lane * 8 + 512 * u < H
                       ? *(const u4 *)(hidden + (size_t)(t0 + r) * H + lane * 8 + 512 * u)
                       : u4{0u, 0u, 0u, 0u};
-    row_scale_regs(v, t0, T, H, lane, rowscale);
+    float down[4];
+    row_scale_regs(v, t0, T, H, lane, rowscale, down);
+    if (stage_rows == 1) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (t0 + r < T && lane * 8 + 512 * u < H) {
+            const u4 o = bf16x8_to_f16x8(v[r][u], down[r]);
+            *(u4 *)(x16 + (size_t)(t0 + r) * H + lane * 8 + 512 * u) = kPermInt4 ? perm_0415(o) : o;
+          }
+    }
     if (t < T) topk16_select<kPer>(key, t, k, li, ids, wts, p_ids, p_w);
     return;
   }
@@ -497,7 +512,7 @@ hipError_t launch_route(const LayerDims &L, const FwdPtrs &P, const Workspace &W
                         hipStream_t s) {
   // prefill: FP16 rows and their scales (1); decode with H <= 2048: the
   // scales only (2), the decode gate/up GEMM converts the rows it stages;
-  // larger decode rows: the GEMM takes the scales too (0)
+  // larger decode rows: the GEMM finds the scales too (0)
   const int stage_rows = !decode ? 1 : L.H <= 2048 ? 2 : 0;
   if (L.E <= 128) return route_dispatch2<8>(L, P, W, stage_rows, s);
   if (L.E <= 256) return route_dispatch2<16>(L, P, W, stage_rows, s);
