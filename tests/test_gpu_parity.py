@@ -156,6 +156,21 @@ def test_hidden_not_multiple_of_256(fmt, T):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("T", [3, 100])
+def test_hidden_above_2048(fmt, T):
+    """H = 2304 > 2048: decode (T=3) scans each row for its power of two inside
+    the gate/up GEMM instead of taking it from the routing kernel; prefill
+    (T=100) stages the FP16 rows in two passes over the row."""
+    log(f"[h2304] fmt={fmt} T={T}")
+    E, H, I, k = 4, 2304, 256, 2
+    p13, p2 = quantized_layer(fmt, 18, T, E, H, I)
+    g = GpuLayer(p13, p2, k)
+    lg = synth.router_logits(18, T, T, E)
+    x = synth.hidden_bf16(18, T, T, H)
+    _check_layer(g, lg, x, tag=f"{fmt} H=2304 T={T}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 def test_residual_and_determinism(fmt):
     log(f"[residual] fmt={fmt}")
     E, H, I, k, T = 16, 256, 256, 4, 200
