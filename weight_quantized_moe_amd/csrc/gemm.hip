@@ -195,7 +195,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode(GemmArgs a) {
       // each row's power of two; longer rows are scanned here first.  Down:
       // the grouped FP16 intermediate rows (permuted here for INT4).
       __syncthreads();
-      if (STAGE == 0 && K <= 2048) {
+      if (STAGE == 0 && K <= kRowRegsMaxH) {
         // the routing kernel left each row's power of two 2^s in its record
         // (row scale bits); convert with the exact inverse 2^-s
         const int cpr = K >> 3;

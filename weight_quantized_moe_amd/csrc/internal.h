@@ -9,6 +9,11 @@ namespace mq {
 constexpr int kMaxExperts = 512;
 constexpr int kPrefillBM = 128;  // token rows per prefill M-tile
 constexpr int kMaxChunks = 256;  // token chunks of the grouping for T > 64
+// Hidden rows of at most this many values are read whole into the registers
+// of one wave by the routing kernel, which then also finds each row's power of
+// two (and, for prefill, writes the FP16 row); longer rows are scanned by the
+// GEMM that stages them (decode) or in two passes (prefill).
+constexpr int kRowRegsMaxH = 2048;
 
 // Chunks of the grouping: at most kMaxChunks, each a multiple of 256 tokens.
 inline void permute_chunks(int64_t T, int *nc, int *chunk) {

@@ -200,7 +200,7 @@ __device__ __forceinline__ void rows_to_f16(const uint16_t *__restrict__ hidden,
 }
 
 // Decode: only the power of two of each hidden row (rowscale[t] = 2^s), for
-// the wave's 4 tokens (rows of H <= 2048, read once into registers).  The
+// the wave's 4 tokens (rows of H <= kRowRegsMaxH, read once into registers).  The
 // decode gate/up GEMM scales the rows into FP16 itself while staging them.
 __device__ __forceinline__ void row_scale_regs(const u4 (&v)[4][4], int t0, int T, int H, int lane,
                                                float *__restrict__ rowscale, float *down = nullptr) {
@@ -241,7 +241,8 @@ __global__ __launch_bounds__(256) void route_kernel(const void *__restrict__ log
   const int t0 = blockIdx.x * tpb + (threadIdx.x >> 6) * 4;  // first token of this wave
   if (blockIdx.x == 0 && threadIdx.x == 0) flags[0] = 0u;
   if (t0 >= T) return;
-  if (stage_rows != 0 && H <= 2048) {
+  static_assert(kRowRegsMaxH == 4 * 64 * 8, "4 x 16 bytes per lane cover one row");
+  if (stage_rows != 0 && H <= kRowRegsMaxH) {
     // rows of up to 2048 values: the rows' loads and the logits' loads in
     // flight together, each row read once (decode keeps only its scale,
     // prefill also writes the FP16 row)
@@ -513,7 +514,7 @@ hipError_t launch_route(const LayerDims &L, const FwdPtrs &P, const Workspace &W
   // prefill: FP16 rows and their scales (1); decode with H <= 2048: the
   // scales only (2), the decode gate/up GEMM converts the rows it stages;
   // larger decode rows: the GEMM finds the scales too (0)
-  const int stage_rows = !decode ? 1 : L.H <= 2048 ? 2 : 0;
+  const int stage_rows = !decode ? 1 : L.H <= kRowRegsMaxH ? 2 : 0;
   if (L.E <= 128) return route_dispatch2<8>(L, P, W, stage_rows, s);
   if (L.E <= 256) return route_dispatch2<16>(L, P, W, stage_rows, s);
   return route_dispatch2<32>(L, P, W, stage_rows, s);
@@ -524,7 +525,7 @@ hipError_t launch_permute(const LayerDims &L, const FwdPtrs &P, const Workspace 
   char *ws = P.ws;
   if (P.T <= 64) {
     hipLaunchKernelGGL(group_small_kernel, dim3(1), dim3(1024), 0, s, (const int32_t *)(ws + W.topk_ids),
-                       (const float *)(ws + W.topk_w), decode && L.H > 2048 ? (const float *)nullptr : (const float *)(ws + W.rowscale),
+                       (const float *)(ws + W.topk_w), decode && L.H > kRowRegsMaxH ? (const float *)nullptr : (const float *)(ws + W.rowscale),
                        P.T, L.E, L.k, (int32_t *)(ws + W.offsets), (int32_t *)(ws + W.mtile),
                        (int4 *)(ws + W.active), (int32_t *)(ws + W.sorted_slots), (int4 *)(ws + W.rowinfo),
                        (int32_t *)(ws + W.inv_pos), P.p_offsets, P.p_sorted_tok, P.p_inv);
@@ -540,7 +541,7 @@ hipError_t launch_permute(const LayerDims &L, const FwdPtrs &P, const Workspace 
                      (int4 *)(ws + W.active), P.p_offsets);
   hipLaunchKernelGGL(scatter_kernel, dim3(nc), dim3(256), (size_t)L.E * (4 * 8 + 4 * 4 + 4), s,
                      (const int32_t *)(ws + W.topk_ids), (const float *)(ws + W.topk_w),
-                     decode && L.H > 2048 ? nullptr : (const float *)(ws + W.rowscale), P.T, L.E, L.k, chunk,
+                     decode && L.H > kRowRegsMaxH ? nullptr : (const float *)(ws + W.rowscale), P.T, L.E, L.k, chunk,
                      (const int32_t *)cnt, (int32_t *)(ws + W.sorted_slots),
                      (int4 *)(ws + W.rowinfo), (int32_t *)(ws + W.inv_pos), P.p_sorted_tok,
                      P.p_inv);
