@@ -90,6 +90,34 @@ def cpu_baseline(layer_np, logits, x, budget_s=12.0):
                       f"float64 NumPy per-expert loop incl. dequantization), {el:.1f} s"}
 
 
+def vendor_bmm(dev, steps):
+    """Reference point, not part of the layer: the vendor dense FP16 batched GEMM
+    (torch.bmm, hipBLASLt) at the expert-GEMM shapes of the prefill workloads,
+    with uniform rows per expert and weights already in FP16."""
+    import torch
+    out = []
+    for name, (E, M, N, K) in (("gate/up, 256 rows per expert", (128, 256, 1536, 2048)),
+                               ("down, 256 rows per expert", (128, 256, 2048, 768)),
+                               ("gate/up, 1024 rows per expert", (128, 1024, 1536, 2048)),
+                               ("gate/up, one GEMM of 32768 rows", (1, 32768, 1536, 2048))):
+        a = torch.randn(E, M, K, device=dev, dtype=torch.float16).contiguous()
+        b = torch.randn(E, K, N, device=dev, dtype=torch.float16).contiguous()
+        for _ in range(5):
+            torch.bmm(a, b)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            torch.bmm(a, b)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        tf = 2.0 * E * M * N * K / us / 1e6
+        out.append({"gemm": name, "shape_EMNK": [E, M, N, K], "us": round(us, 2),
+                    "TFLOP_s": round(tf, 1), "frac_of_2.5PF": round(tf / 2500.0, 4)})
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -99,6 +127,8 @@ def main():
     ap.add_argument("--tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true", help="also time every batch size of the workload")
+    ap.add_argument("--vendor-bmm", action="store_true",
+                    help="only time torch.bmm (hipBLASLt) FP16 at the prefill expert-GEMM shapes, for reference")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -110,6 +140,10 @@ def main():
     import torch
     from weight_quantized_moe_amd import Layer, load_library, synth
 
+    if args.vendor_bmm:
+        print(json.dumps({"reference": "torch.bmm FP16 (hipBLASLt), not this library",
+                          "results": vendor_bmm(torch.device("cuda:0"), max(args.steps, 20))}))
+        return
     load_library()
     wl = synth.WORKLOADS[args.workload]
     if wl.fmt == "stack":
