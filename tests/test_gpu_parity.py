@@ -206,6 +206,28 @@ def test_zero_tokens_is_a_noop():
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("T", [16, 64])
+@pytest.mark.parametrize("which", ["h", "partial"])
+def test_fp16_overflow_flag_both_paths(which, T):
+    """Saturating the SwiGLU intermediate h or the routing-weighted FP16
+    partials sets the flag, on the decode (T=16) and the prefill (T=64) GEMMs,
+    and the outputs stay finite."""
+    log(f"[overflow2] which={which} T={T}")
+    E, H, I, k = 4, 256, 128, 2
+    p13, p2 = quantized_layer(formats.INT4, 19, T, E, H, I)
+    if which == "h":
+        p13.scale[:] = np.float16(60000.0)
+    else:
+        p2.scale[:] = np.float16(60000.0)
+    g = GpuLayer(p13, p2, k)
+    lg = synth.router_logits(19, T, T, E)
+    x = synth.hidden_bf16(19, T, T, H)
+    out, pr, ovf = g.run(lg, x, probe=True)
+    assert ovf
+    assert np.nanmax(np.abs(pr["h"].astype(np.float32))) <= 65504.0
+    assert np.all(np.isfinite(moe.bf16_bits_to_f64(out)))
+
+
 def test_fp16_intermediate_overflow_flag():
     """Saturating the FP16 SwiGLU intermediate sets the flag and clamps."""
     log("[overflow]")
