@@ -87,7 +87,7 @@ struct DecodeFrag {
   uint32_t sb[2];   // INT4: FP16 group-scale bits; NVFP4: two E4M3 block-scale bytes
 };
 
-template <int FMT, int STAGE, int KSPLIT, int GCT>
+template <int FMT, int STAGE, int KSPLIT, int GCT, int TPW>
 __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode(GemmArgs a) {
   // GCT > 0: the k groups per row (K / 128) known at compile time; the group
   // loop is then fully unrolled, so every wait on a prefetch is an exact
@@ -108,43 +108,53 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode(GemmArgs a) {
   const int gb = (kp * G) / KSPLIT;                               // groups [gb, gb + ng)
   const int ng = NGCT > 0 ? NGCT : ((kp + 1) * G) / KSPLIT - gb;
   const int n_units = a.einfo[0].x * a.tiles;
+  // TPW > 1 (down projection with few k groups): each wave streams TPW tile
+  // pairs of the unit in one ring, so a unit's ring fill and drain cover more
+  // weight bytes
+  static_assert(TPW == 1 || (NGCT > 0 && NGCT % 2 == 0 && KSPLIT == 1), "pairs of groups stay in one tile pair");
+  constexpr int NGT = NGCT * TPW;  // groups of the wave's ring (unrolled case)
 
   for (int unit = blockIdx.x; unit < n_units; unit += gridDim.x) {
     const int slot_idx = unit / a.tiles, tile = unit - slot_idx * a.tiles;
     const int4 ei = a.einfo[1 + slot_idx];
     const int e = ei.x, r0 = ei.y, ne = ei.z;
-    int row[2];
-    if (STAGE == 0) {
-      const int n0 = (tile * CG + cg) * 16;
-      row[0] = n0 + nl;
-      row[1] = a.I + n0 + nl;
-    } else {
-      const int n0 = (tile * CG + cg) * 32;
-      row[0] = n0 + nl;
-      row[1] = n0 + 16 + nl;
-    }
-    const uint8_t *wrow[2];
-    const void *srow[2];
+    int row[TPW][2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      wrow[t] = a.w + ((size_t)e * N + row[t]) * rowbytes;
-      if (FMT == FMT_INT4)
-        srow[t] = (const _Float16 *)a.scale + ((size_t)e * N + row[t]) * G;
-      else if (FMT == FMT_FP8)
-        srow[t] = (const float *)a.scale + ((size_t)e * (N / 128) + row[t] / 128) * G;
-      else
-        srow[t] = (const uint8_t *)a.scale + ((size_t)e * N + row[t]) * (K / 16);
+    for (int p = 0; p < TPW; ++p) {
+      if (STAGE == 0) {
+        const int n0 = ((tile * TPW + p) * CG + cg) * 16;
+        row[p][0] = n0 + nl;
+        row[p][1] = a.I + n0 + nl;
+      } else {
+        const int n0 = ((tile * TPW + p) * CG + cg) * 32;
+        row[p][0] = n0 + nl;
+        row[p][1] = n0 + 16 + nl;
+      }
     }
+    const uint8_t *wrow[TPW][2];
+    const void *srow[TPW][2];
+#pragma unroll
+    for (int p = 0; p < TPW; ++p)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        wrow[p][t] = a.w + ((size_t)e * N + row[p][t]) * rowbytes;
+        if (FMT == FMT_INT4)
+          srow[p][t] = (const _Float16 *)a.scale + ((size_t)e * N + row[p][t]) * G;
+        else if (FMT == FMT_FP8)
+          srow[p][t] = (const float *)a.scale + ((size_t)e * (N / 128) + row[p][t] / 128) * G;
+        else
+          srow[p][t] = (const uint8_t *)a.scale + ((size_t)e * N + row[p][t]) * (K / 16);
+      }
 
     // Groups g and g + 1 (if `two`), issued tile by tile so the two halves of
     // every 128-byte line of a 4-bit row are requested back to back.  Plain
     // (cached) loads: measured faster than non-temporal ones here, as the
     // second half of a line then finds the first's fill in L2.
-    auto load_pair = [&](DecodeFrag<FMT> &fa, DecodeFrag<FMT> &fb, int g, bool two) {
+    auto load_pair_p = [&](DecodeFrag<FMT> &fa, DecodeFrag<FMT> &fb, int pp, int g, bool two) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         if (FMT == FMT_FP8) {
-          const u4 *p = (const u4 *)(wrow[t] + (size_t)g * 128 + q * 32);
+          const u4 *p = (const u4 *)(wrow[pp][t] + (size_t)g * 128 + q * 32);
           fa.w[t] = p[0];
           fa.w2[t] = p[1];
           if (two) {
@@ -152,7 +162,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode(GemmArgs a) {
             fb.w2[t] = p[9];
           }
         } else {
-          const u4 *p = (const u4 *)(wrow[t] + (size_t)g * 64 + q * 16);
+          const u4 *p = (const u4 *)(wrow[pp][t] + (size_t)g * 64 + q * 16);
           fa.w[t] = p[0];
           if (two) fb.w[t] = p[4];
         }
@@ -160,16 +170,23 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode(GemmArgs a) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         if (FMT == FMT_FP8) {
-          fa.s[t] = ((const float *)srow[t])[g];
-          if (two) fb.s[t] = ((const float *)srow[t])[g + 1];
+          fa.s[t] = ((const float *)srow[pp][t])[g];
+          if (two) fb.s[t] = ((const float *)srow[pp][t])[g + 1];
         } else if (FMT == FMT_INT4) {
-          fa.sb[t] = ((const uint16_t *)srow[t])[g];
-          if (two) fb.sb[t] = ((const uint16_t *)srow[t])[g + 1];
+          fa.sb[t] = ((const uint16_t *)srow[pp][t])[g];
+          if (two) fb.sb[t] = ((const uint16_t *)srow[pp][t])[g + 1];
         } else {
-          fa.sb[t] = *(const uint16_t *)((const uint8_t *)srow[t] + 8 * g + 2 * q);
-          if (two) fb.sb[t] = *(const uint16_t *)((const uint8_t *)srow[t] + 8 * (g + 1) + 2 * q);
+          fa.sb[t] = *(const uint16_t *)((const uint8_t *)srow[pp][t] + 8 * g + 2 * q);
+          if (two) fb.sb[t] = *(const uint16_t *)((const uint8_t *)srow[pp][t] + 8 * (g + 1) + 2 * q);
         }
       }
+    };
+    // ring position i -> (tile pair i / NGCT, group i % NGCT) when unrolled
+    auto load_pair = [&](DecodeFrag<FMT> &fa, DecodeFrag<FMT> &fb, int i, bool two) {
+      if (TPW == 1)
+        load_pair_p(fa, fb, 0, i, two);
+      else
+        load_pair_p(fa, fb, i / NGCT, i % NGCT, two);
     };
 
     for (int mc = 0; mc < ne; mc += 16) {
@@ -177,7 +194,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode(GemmArgs a) {
       DecodeFrag<FMT> f[kD];
 #pragma unroll
       for (int d = 0; d < kD; d += 2)
-        if (d < ng) load_pair(f[d], f[d + 1], gb + d, d + 1 < ng);
+        if (d < ng * TPW) load_pair(f[d], f[d + 1], gb + d, d + 1 < ng * TPW);
       // per-row records of the rows this lane stores (issued early; read in
       // the epilogue)
       int4 rinf[4];
@@ -243,11 +260,14 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode(GemmArgs a) {
       }
       __syncthreads();
 
-      f4 acc[2];
-      acc[0] = f4{0.f, 0.f, 0.f, 0.f};
-      acc[1] = acc[0];
+      f4 acc[TPW][2];
+#pragma unroll
+      for (int p = 0; p < TPW; ++p) acc[p][0] = acc[p][1] = f4{0.f, 0.f, 0.f, 0.f};
       const _Float16 *abase = As + nl * lda + 32 * q;
-      auto compute = [&](const DecodeFrag<FMT> &fr, int g) {
+      // ring position i: group i of tile pair 0, or with TPW > 1 group i % NGCT
+      // of tile pair i / NGCT (constants once the ring is unrolled)
+      auto compute = [&](const DecodeFrag<FMT> &fr, int i) {
+        const int pp = TPW == 1 ? 0 : i / NGCT, g = TPW == 1 ? i : i % NGCT;
         const _Float16 *ap = abase + g * 128;
         f4 tmp[2];
         tmp[0] = f4{0.f, 0.f, 0.f, 0.f};
@@ -267,7 +287,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode(GemmArgs a) {
               bv = unpack_nvfp4(fr.w[t][j], e4m3_to_f16((fr.sb[t] >> (8 * (j >> 1))) & 0xFFu));
             }
             if (FMT == FMT_NVFP4)
-              acc[t] = mfma16(av, bv, acc[t]);
+              acc[pp][t] = mfma16(av, bv, acc[pp][t]);
             else
               tmp[t] = mfma16(av, bv, tmp[t]);
           }
@@ -275,21 +295,21 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode(GemmArgs a) {
         if (FMT == FMT_INT4) {
 #pragma unroll
           for (int t = 0; t < 2; ++t)
-            acc[t] += tmp[t] * (float)__builtin_bit_cast(_Float16, (uint16_t)fr.sb[t]);
+            acc[pp][t] += tmp[t] * (float)__builtin_bit_cast(_Float16, (uint16_t)fr.sb[t]);
         } else if (FMT == FMT_FP8) {
 #pragma unroll
-          for (int t = 0; t < 2; ++t) acc[t] += tmp[t] * fr.s[t];
+          for (int t = 0; t < 2; ++t) acc[pp][t] += tmp[t] * fr.s[t];
         }
       };
 
       if constexpr (NGCT > 0) {
-        // fully unrolled ring of kD groups
+        // fully unrolled ring of kD groups (over TPW tile pairs)
 #pragma unroll
-        for (int i = 0; i < NGCT; i += 2) {
+        for (int i = 0; i < NGT; i += 2) {
           compute(f[i % kD], gb + i);
-          if (i + 1 < NGCT) compute(f[(i + 1) % kD], gb + i + 1);
-          if (i + kD < NGCT) {
-            load_pair(f[i % kD], f[(i + 1) % kD], gb + i + kD, i + kD + 1 < NGCT);
+          if (i + 1 < NGT) compute(f[(i + 1) % kD], gb + i + 1);
+          if (i + kD < NGT) {
+            load_pair(f[i % kD], f[(i + 1) % kD], gb + i + kD, i + kD + 1 < NGT);
             __builtin_amdgcn_sched_barrier(0);
           }
         }
@@ -326,7 +346,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode(GemmArgs a) {
 #pragma unroll
           for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) rb[(t * 4 + ii) * 64 + lane] = acc[t][ii];
+            for (int ii = 0; ii < 4; ++ii) rb[(t * 4 + ii) * 64 + lane] = acc[0][t][ii];
         }
         __syncthreads();
         if (kp == 0) {
@@ -335,7 +355,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode(GemmArgs a) {
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
-              for (int ii = 0; ii < 4; ++ii) acc[t][ii] += rb[(t * 4 + ii) * 64 + lane];
+              for (int ii = 0; ii < 4; ++ii) acc[0][t][ii] += rb[(t * 4 + ii) * 64 + lane];
           }
         }
       }
@@ -349,12 +369,15 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode(GemmArgs a) {
           const int slot = rinf[ii].x;
           if (STAGE == 0) {
             const float sc = sm_rscale[m] * ginv;
-            store_h(a, r, row[0], acc[0][ii] * sc, acc[1][ii] * sc);
+            store_h(a, r, row[0][0], acc[0][0][ii] * sc, acc[0][1][ii] * sc);
           } else {
             const float wt = __builtin_bit_cast(float, rinf[ii].w) * ginv;
             uint32_t sat = 0u;
-            a.partial[(size_t)slot * a.H + row[0]] = to_f16_sat(acc[0][ii] * wt, sat);
-            a.partial[(size_t)slot * a.H + row[1]] = to_f16_sat(acc[1][ii] * wt, sat);
+#pragma unroll
+            for (int p = 0; p < TPW; ++p) {
+              a.partial[(size_t)slot * a.H + row[p][0]] = to_f16_sat(acc[p][0][ii] * wt, sat);
+              a.partial[(size_t)slot * a.H + row[p][1]] = to_f16_sat(acc[p][1][ii] * wt, sat);
+            }
             if (sat) atomicOr(a.flags, 1u);
           }
         }
@@ -850,20 +873,20 @@ static int num_cus() {
   return g_num_cus;
 }
 
-template <int FMT, int STAGE, int KSPLIT, int GCT>
-static hipError_t run_decode_g(GemmArgs a, int slots, const GemmLaunch &s) {
+template <int FMT, int STAGE, int KSPLIT, int GCT, int TPW>
+static hipError_t run_decode_t(GemmArgs a, int slots, const GemmLaunch &s) {
   constexpr int CG = kDecodeWaves / KSPLIT;
-  a.tiles = STAGE == 0 ? a.I / (16 * CG) : a.H / (32 * CG);
+  a.tiles = STAGE == 0 ? a.I / (16 * CG * TPW) : a.H / (32 * CG * TPW);
   const size_t lds = (size_t)16 * (a.K + 8) * 2 + 48 * 4 + (size_t)(KSPLIT - 1) * CG * 512 * 4;
   // persistent grid: as many blocks as are resident at once (from the
   // kernel's registers and LDS), never more than the number of units
   static int per_cu = 0;
   static size_t per_cu_lds = 0;
   if (per_cu == 0 || per_cu_lds != lds) {
-    (void)hipFuncSetAttribute((const void *)gemm_decode<FMT, STAGE, KSPLIT, GCT>,
+    (void)hipFuncSetAttribute((const void *)gemm_decode<FMT, STAGE, KSPLIT, GCT, TPW>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_decode<FMT, STAGE, KSPLIT, GCT>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_decode<FMT, STAGE, KSPLIT, GCT, TPW>,
                                                      64 * kDecodeWaves, lds) != hipSuccess || n < 1)
       n = 1;
     per_cu = n;
@@ -871,9 +894,22 @@ static hipError_t run_decode_g(GemmArgs a, int slots, const GemmLaunch &s) {
   }
   const long units = (long)slots * a.tiles;
   const long grid = std::min<long>(units, (long)num_cus() * per_cu);
-  hipExtLaunchKernelGGL((gemm_decode<FMT, STAGE, KSPLIT, GCT>), dim3((unsigned)grid),
+  hipExtLaunchKernelGGL((gemm_decode<FMT, STAGE, KSPLIT, GCT, TPW>), dim3((unsigned)grid),
                         dim3(64 * kDecodeWaves), (uint32_t)lds, s.stream, s.start, s.stop, 0u, a);
   return hipGetLastError();
+}
+
+// Down projection with an even number of k groups up to 8 per wave: two tile
+// pairs per wave when they tile H and the halved unit count still gives every
+// CU two units (a unit's ring then streams twice the bytes).
+template <int FMT, int STAGE, int KSPLIT, int GCT>
+static hipError_t run_decode_g(GemmArgs a, int slots, const GemmLaunch &s) {
+  constexpr int CG = kDecodeWaves / KSPLIT;
+  if constexpr (STAGE == 1 && KSPLIT == 1 && GCT > 0 && GCT % 2 == 0 && GCT <= 8) {
+    if (a.H % (32 * CG * 2) == 0 && (long)slots * (a.H / (32 * CG * 2)) >= 2L * num_cus())
+      return run_decode_t<FMT, STAGE, KSPLIT, GCT, 2>(a, slots, s);
+  }
+  return run_decode_t<FMT, STAGE, KSPLIT, GCT, 1>(a, slots, s);
 }
 
 template <int FMT, int STAGE, int KSPLIT>
