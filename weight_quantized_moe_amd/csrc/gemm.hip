@@ -751,15 +751,16 @@ void gemm_prefill(GemmArgs a) {
 }
 
 // ===========================================================================
-// Prefill path, weights in registers.  One block of 4 waves per CU (one wave
-// per SIMD) covers 128 grouped rows of one expert and 512 weight columns; each
-// wave owns 128 columns and all 128 rows, a 4 x 4 grid of MFMA 32x32x16 tiles
-// whose 256 accumulators per lane live in the accumulation registers.  Only
-// the FP16 activation tile goes through LDS (written once per k step by the
-// block, read by its 4 waves); every wave streams the packed codes of its own
-// columns into registers, two k steps deep, and unpacks them straight into the
-// MFMA A operand with the column's scale folded in (same FP16 values as the
-// LDS-staged kernel above, so the same error bound).
+// Prefill gate/up path, weights in registers.  A block of 4 waves covers 128
+// grouped rows of one expert; each wave owns TN 32-column weight tiles and all
+// 128 rows, a TN x 4 grid of MFMA 32x32x16 tiles.  TN = 2 (the one launched):
+// 128 accumulators per lane, two blocks per CU; TN = 4: 256 accumulators in
+// the accumulation registers, one block per CU.  Only the FP16 activation tile
+// goes through LDS (written once by the block, read by its 4 waves); every
+// wave streams the packed codes of its own columns into registers one k step
+// ahead and unpacks them straight into the MFMA A operand with the column's
+// scale folded in (the same FP16 values as the LDS-staged kernel above, so
+// the same error bound).
 //
 // Per k step of 64 a lane holds 32 k values of its column: FP8 bytes
 // 16 h + [0, 16) and 32 + 16 h + [0, 16) of the step (h = lane / 32), INT4 and
@@ -767,21 +768,30 @@ void gemm_prefill(GemmArgs a) {
 // lane's 8 values s; the activation fragment of lane half h reads the same k
 // offsets (any k order works when both operands follow it).
 //
-// gate/up: wave w of column tile nt holds gate columns 256 nt + 64 w + [0, 64)
-// in tiles 0-1 and the matching up columns in tiles 2-3.  down: wave w holds
-// columns 512 nt + 128 w + [0, 128).  A wave whose columns lie past the end
-// (I or H not a multiple of the block width) stages activations and takes the
-// barriers but multiplies and stores nothing.
+// Wave w of column tile nt holds gate columns 64 TN nt + 16 TN w + [0, 16 TN)
+// in tiles [0, TN/2) and the matching up columns in the others, so SwiGLU runs
+// in registers.  A wave whose columns lie past I (I not a multiple of the
+// block width) stages activations and takes the barriers but multiplies and
+// stores nothing.
 // ===========================================================================
-constexpr int kWK = 64;                               // k step
-constexpr int kWLD = 2 * kWK + 8;                     // activation LDS row stride, halves (two k steps)
-constexpr int kWBN = 512;                             // weight columns per block
-constexpr size_t kWABuf = (size_t)kBM * kWLD * 2;    // bytes of one activation buffer
+constexpr int kWK = 64;  // k step
 
-template <int FMT>
+// Shape of a variant with TN 32-column tiles per wave: k steps per activation
+// buffer (one barrier each), LDS row stride in halves, bytes of one buffer,
+// weight columns per block, and dynamic LDS per block.
+template <int TN>
+struct WideShape {
+  static constexpr int SPB = TN == 4 ? 4 : 2;
+  static constexpr int LD = SPB * kWK + 8;
+  static constexpr size_t ABUF = (size_t)kBM * LD * 2;
+  static constexpr int BC = 4 * 32 * TN;
+  static constexpr size_t LDS = 2 * ABUF + 2 * BC * sizeof(float);
+};
+
+template <int FMT, int TN>
 struct WideRegs {
-  uint32_t w[4][FMT == FMT_FP8 ? 8 : 4];  // codes of column tile tn
-  uint32_t s[4];  // INT4: FP16 scale bits; FP8: FP32 scale bits; NVFP4: two E4M3 bytes
+  uint32_t w[TN][FMT == FMT_FP8 ? 8 : 4];  // codes of column tile tn
+  uint32_t s[TN];  // INT4: FP16 scale bits; FP8: FP32 scale bits; NVFP4: two E4M3 bytes
 };
 
 template <int FMT>
@@ -789,12 +799,15 @@ __device__ __forceinline__ int wide_koff(int s, int hh) {
   return FMT == FMT_FP8 ? 16 * hh + 8 * (s & 1) + 32 * (s >> 1) : 32 * hh + 8 * s;
 }
 
-template <int FMT, int STAGE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int FMT, int TN>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4 / TN, 4 / TN)))
 void gemm_prefill_wide(GemmArgs a) {
+  constexpr int SPB = WideShape<TN>::SPB, LD = WideShape<TN>::LD, BC = WideShape<TN>::BC;
+  constexpr int WC = 32 * TN, TH = TN / 2;  // columns per wave; gate (and up) tiles per wave
+  constexpr size_t ABUF = WideShape<TN>::ABUF;
   extern __shared__ __align__(16) unsigned char smem[];
-  float *colinv = (float *)(smem + 2 * kWABuf);  // [kWBN]: 2^-p of each weight column
-  float *rowfs = colinv + kWBN;                  // [kWBN]: 2^p
+  float *colinv = (float *)(smem + 2 * ABUF);  // [BC]: 2^-p of each weight column
+  float *rowfs = colinv + BC;                  // [BC]: 2^p
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int j = lane & 31, hh = lane >> 5;
   // ---- tile of this block
@@ -818,12 +831,12 @@ void gemm_prefill_wide(GemmArgs a) {
   const size_t rowbytes = FMT == FMT_FP8 ? (size_t)K : (size_t)K / 2;
 
   // ---- the wave's columns: global weight row of this lane in each tile
-  const int cb = STAGE == 0 ? nt * (kWBN / 2) + wave * 64 : nt * kWBN + wave * 128;
-  const bool wvalid = cb < (STAGE == 0 ? a.I : N);  // wave-uniform
-  int gr[4];
+  const int cb = nt * (BC / 2) + wave * (WC / 2);  // first gate (h) column of the wave
+  const bool wvalid = cb < a.I;                    // wave-uniform
+  int gr[TN];
 #pragma unroll
-  for (int tn = 0; tn < 4; ++tn) {
-    const int c = STAGE == 0 ? (tn < 2 ? cb : a.I + cb) + (tn & 1) * 32 + j : cb + tn * 32 + j;
+  for (int tn = 0; tn < TN; ++tn) {
+    const int c = (tn < TH ? cb : a.I + cb) + (tn % TH) * 32 + j;
     gr[tn] = wvalid ? c : j;  // a row that exists; never stored
   }
 
@@ -831,8 +844,8 @@ void gemm_prefill_wide(GemmArgs a) {
   // takes tiles 2 hh and 2 hh + 1, shared through LDS
   if (FMT != FMT_NVFP4) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int tn = 2 * hh + q;
+    for (int q = 0; q < TH; ++q) {
+      const int tn = hh * TH + q;
       float m = 0.f;
       for (int g0 = 0; g0 < G; g0 += 8) {
         float sv[8];
@@ -846,12 +859,12 @@ void gemm_prefill_wide(GemmArgs a) {
         for (int u = 0; u < 8; ++u) m = fmaxf(m, fabsf(sv[u]));
       }
       float inv;
-      rowfs[wave * 128 + tn * 32 + j] = row_pow2(m * (FMT == FMT_INT4 ? 8.f : 448.f), &inv);
-      colinv[wave * 128 + tn * 32 + j] = inv;
+      rowfs[wave * WC + tn * 32 + j] = row_pow2(m * (FMT == FMT_INT4 ? 8.f : 448.f), &inv);
+      colinv[wave * WC + tn * 32 + j] = inv;
     }
   } else if (hh == 0) {
 #pragma unroll
-    for (int tn = 0; tn < 4; ++tn) colinv[wave * 128 + tn * 32 + j] = 1.f;
+    for (int tn = 0; tn < TN; ++tn) colinv[wave * WC + tn * 32 + j] = 1.f;
   }
 
   // ---- activation staging: row (tid >> 3) + 32 p, 16-byte chunk tid & 7
@@ -860,14 +873,13 @@ void gemm_prefill_wide(GemmArgs a) {
   for (int p = 0; p < 4; ++p) {
     const int rr = (tid >> 3) + 32 * p;
     const int r = rbeg + (rr < nrows ? rr : nrows - 1);
-    const size_t arow = STAGE == 0 ? (size_t)a.rowinfo[r].y : (size_t)r;
-    asrc[p] = a.a_src + arow * K + (tid & 7) * 8;
+    asrc[p] = a.a_src + (size_t)a.rowinfo[r].y * K + (tid & 7) * 8;
   }
   // ---- weight and scale streams of the lane's four columns
-  const uint8_t *wsrc[4];
-  const uint8_t *ssrc[4];
+  const uint8_t *wsrc[TN];
+  const uint8_t *ssrc[TN];
 #pragma unroll
-  for (int tn = 0; tn < 4; ++tn) {
+  for (int tn = 0; tn < TN; ++tn) {
     wsrc[tn] = a.w + ((size_t)e * N + gr[tn]) * rowbytes + 16 * hh;
     if (FMT == FMT_INT4)
       ssrc[tn] = (const uint8_t *)((const uint16_t *)a.scale + ((size_t)e * N + gr[tn]) * G);
@@ -881,19 +893,17 @@ void gemm_prefill_wide(GemmArgs a) {
 #pragma unroll
     for (int p = 0; p < 4; ++p) ar[p] = *(const u4 *)(asrc[p] + ks * kWK);
   };
-  auto write_a = [&](const u4 (&ar)[4], int buf, int half) {
-    _Float16 *As = (_Float16 *)(smem + buf * kWABuf) + half * kWK;
+  auto write_a = [&](const u4 (&ar)[4], int buf, int sub) {
+    _Float16 *As = (_Float16 *)(smem + buf * ABUF) + sub * kWK;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      u4 v = ar[p];
-      if (FMT == FMT_INT4 && STAGE == 1) v = perm_0415(v);  // gate/up rows come INT4-ordered
-      *(u4 *)(As + ((tid >> 3) + 32 * p) * kWLD + (tid & 7) * 8) = v;
+      *(u4 *)(As + ((tid >> 3) + 32 * p) * LD + (tid & 7) * 8) = ar[p];  // INT4: x16 is stored INT4-ordered
     }
   };
-  auto load_w = [&](WideRegs<FMT> &R, int ks) {
+  auto load_w = [&](WideRegs<FMT, TN> &R, int ks) {
     const int kb = ks * kWK;
 #pragma unroll
-    for (int tn = 0; tn < 4; ++tn) {
+    for (int tn = 0; tn < TN; ++tn) {
       if (FMT == FMT_FP8) {
         const u4 v0 = *(const u4 *)(wsrc[tn] + kb);
         const u4 v1 = *(const u4 *)(wsrc[tn] + kb + 32);
@@ -909,7 +919,7 @@ void gemm_prefill_wide(GemmArgs a) {
       }
     }
 #pragma unroll
-    for (int tn = 0; tn < 4; ++tn) {
+    for (int tn = 0; tn < TN; ++tn) {
       if (FMT == FMT_INT4)
         R.s[tn] = ((const uint16_t *)ssrc[tn])[kb >> 7];
       else if (FMT == FMT_FP8)
@@ -920,15 +930,17 @@ void gemm_prefill_wide(GemmArgs a) {
   };
 
   __syncthreads();  // rowfs / colinv
-  float rowf[4] = {1.f, 1.f, 1.f, 1.f};
+  float rowf[TN];
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn) rowf[tn] = 1.f;
   if (FMT != FMT_NVFP4) {
 #pragma unroll
-    for (int tn = 0; tn < 4; ++tn) rowf[tn] = rowfs[wave * 128 + tn * 32 + j];
+    for (int tn = 0; tn < TN; ++tn) rowf[tn] = rowfs[wave * WC + tn * 32 + j];
   }
 
-  f16v acc[4][4];
+  f16v acc[TN][4];
 #pragma unroll
-  for (int tn = 0; tn < 4; ++tn)
+  for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
     for (int tm = 0; tm < 4; ++tm)
 #pragma unroll
@@ -936,14 +948,14 @@ void gemm_prefill_wide(GemmArgs a) {
 
   // NV: 32-row M subtiles that hold rows of the expert (block-uniform; 0 for
   // a wave past the last column)
-  auto compute = [&](auto nv_c, const WideRegs<FMT> &R, int buf, int half) {
+  auto compute = [&](auto nv_c, const WideRegs<FMT, TN> &R, int buf, int sub) {
     constexpr int NV = decltype(nv_c)::value;
     if constexpr (NV > 0) {
-      const _Float16 *As = (const _Float16 *)(smem + buf * kWABuf) + half * kWK;
-      h2 sc[4];
+      const _Float16 *As = (const _Float16 *)(smem + buf * ABUF) + sub * kWK;
+      h2 sc[TN];
       if (FMT != FMT_NVFP4) {
 #pragma unroll
-        for (int tn = 0; tn < 4; ++tn) {
+        for (int tn = 0; tn < TN; ++tn) {
           const float sv = FMT == FMT_INT4 ? (float)__builtin_bit_cast(_Float16, (uint16_t)R.s[tn])
                                            : __builtin_bit_cast(float, R.s[tn]);
           const _Float16 s16 = (_Float16)(sv * rowf[tn]);
@@ -958,16 +970,16 @@ void gemm_prefill_wide(GemmArgs a) {
       constexpr int VP = (kValuPerTile + NV - 1) / NV;
       h8 afc[NV], afn[NV];
 #pragma unroll
-      for (int tm = 0; tm < NV; ++tm) afc[tm] = *(const h8 *)(As + (tm * 32 + j) * kWLD + wide_koff<FMT>(0, hh));
+      for (int tm = 0; tm < NV; ++tm) afc[tm] = *(const h8 *)(As + (tm * 32 + j) * LD + wide_koff<FMT>(0, hh));
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         if (s < 3) {
 #pragma unroll
           for (int tm = 0; tm < NV; ++tm)
-            afn[tm] = *(const h8 *)(As + (tm * 32 + j) * kWLD + wide_koff<FMT>(s + 1, hh));
+            afn[tm] = *(const h8 *)(As + (tm * 32 + j) * LD + wide_koff<FMT>(s + 1, hh));
         }
 #pragma unroll
-        for (int tn = 0; tn < 4; ++tn) {
+        for (int tn = 0; tn < TN; ++tn) {
           h8 wf;
           if (FMT == FMT_INT4) {
             wf = unpack_int4(R.w[tn][s]);
@@ -992,7 +1004,7 @@ void gemm_prefill_wide(GemmArgs a) {
           __builtin_amdgcn_sched_group_barrier(0x100, NV, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, kValuPerTile, 0);
 #pragma unroll
-        for (int i = 0; i < 4 * NV; ++i) {
+        for (int i = 0; i < TN * NV; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x002, VP, 0);
         }
@@ -1004,43 +1016,40 @@ void gemm_prefill_wide(GemmArgs a) {
       }
     }
   };
-  // One barrier per two k steps: an LDS buffer holds the activations of a
-  // step pair, and while the block multiplies from one buffer it fills the
-  // other, half by half (so the staging registers hold one k step).  Weights
-  // for k step t + 1 load while step t multiplies.
+  // One barrier per SPB k steps: an LDS buffer holds the activations of
+  // SPB steps, and while the block multiplies from one buffer it fills the
+  // other one k step at a time (so the staging registers hold one step).
+  // Weights for k step t + 1 load while step t multiplies.
   auto main_loop = [&](auto nv_c) {
-    WideRegs<FMT> R0, R1;
-    u4 ar[4], a0[4], a1[4];
+    WideRegs<FMT, TN> R[2];
+    u4 ar[4], a0[SPB][4];
     // same load order as in the loop (activations of a later step, then
     // weights), so that the loop's first LDS write waits for the activation
     // loads alone
-    load_a(a0, 0);
-    load_a(a1, 1);
-    load_a(ar, min(2, nK - 1));
+#pragma unroll
+    for (int u = 0; u < SPB; ++u) load_a(a0[u], u);
+    load_a(ar, min(SPB, nK - 1));
     __builtin_amdgcn_sched_barrier(0);
-    load_w(R0, 0);
+    load_w(R[0], 0);
     __builtin_amdgcn_sched_barrier(0);
-    write_a(a0, 0, 0);
-    write_a(a1, 0, 1);
-    for (int t = 0; t < nK; t += 2) {  // nK = K / 64 is even (K is a multiple of 128)
-      const int q = (t >> 1) & 1;
+#pragma unroll
+    for (int u = 0; u < SPB; ++u) write_a(a0[u], 0, u);
+    for (int t = 0; t < nK; t += SPB) {  // nK is a multiple of SPB (checked by the launcher)
+      const int q = (t / SPB) & 1;
       __syncthreads();
-      // first half: k step t from buffer q; stage step t + 2 into the other
-      write_a(ar, q ^ 1, 0);  // (past the end: a repeat of the last step, never read)
-      load_a(ar, min(t + 3, nK - 1));
-      __builtin_amdgcn_sched_barrier(0);
-      load_w(R1, t + 1);
-      // keep the loads ahead of the MFMAs (left alone, the scheduler sinks
-      // them to the end of the step and the next step waits for them)
-      __builtin_amdgcn_sched_barrier(0);
-      compute(nv_c, R0, q, 0);
-      // second half: k step t + 1; stage step t + 3
-      write_a(ar, q ^ 1, 1);
-      load_a(ar, min(t + 4, nK - 1));
-      __builtin_amdgcn_sched_barrier(0);
-      load_w(R0, min(t + 2, nK - 1));
-      __builtin_amdgcn_sched_barrier(0);
-      compute(nv_c, R1, q, 1);
+#pragma unroll
+      for (int u = 0; u < SPB; ++u) {
+        // k step t + u from buffer q; stage step t + SPB + u into the other
+        // (past the end: a repeat of the last step, never read)
+        write_a(ar, q ^ 1, u);
+        load_a(ar, min(t + SPB + u + 1, nK - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(R[(u + 1) & 1], min(t + u + 1, nK - 1));
+        // keep the loads ahead of the MFMAs (left alone, the scheduler sinks
+        // them to the end of the step and the next step waits for them)
+        __builtin_amdgcn_sched_barrier(0);
+        compute(nv_c, R[u & 1], q, u);
+      }
     }
   };
   const int nv = wvalid ? min(4, (nrows + 31) / 32) : 0;
@@ -1056,11 +1065,10 @@ void gemm_prefill_wide(GemmArgs a) {
   // register v of tile tn, column 8 (v / 4) + 4 (l / 32) + v % 4 of the tile
   const float ginv = FMT == FMT_NVFP4 ? 1.0f / a.gscale[e] : 1.0f;
   const int cl = 4 * hh;
-  const float *cinv = colinv + wave * 128;
+  const float *cinv = colinv + wave * WC;
   uint32_t sat = 0u;
-  float vmax = 0.f, vnan = 0.f;
   typedef uint32_t u2 __attribute__((ext_vector_type(2)));
-  if constexpr (STAGE == 0) {
+  {
     if (wvalid) {
 #pragma unroll
       for (int tm = 0; tm < 4; ++tm) {
@@ -1072,14 +1080,14 @@ void gemm_prefill_wide(GemmArgs a) {
         for (int g4 = 0; g4 < 4; ++g4) {
           const int c4 = 8 * g4 + cl;
 #pragma unroll
-          for (int tn = 0; tn < 2; ++tn) {
+          for (int tn = 0; tn < TH; ++tn) {
             const f4 ig = *(const f4 *)(cinv + tn * 32 + c4);
-            const f4 iu = *(const f4 *)(cinv + (tn + 2) * 32 + c4);
+            const f4 iu = *(const f4 *)(cinv + (tn + TH) * 32 + c4);
             h2 o[2];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const float gv = acc[tn][tm][4 * g4 + i] * (rsc * ig[i]);
-              const float uv = acc[tn + 2][tm][4 * g4 + i] * (rsc * iu[i]);
+              const float uv = acc[tn + TH][tm][4 * g4 + i] * (rsc * iu[i]);
               const float hv = silu(gv) * uv;
               const float hc = fminf(fmaxf(hv, -65504.f), 65504.f);
               sat |= hc != hv;
@@ -1090,55 +1098,7 @@ void gemm_prefill_wide(GemmArgs a) {
         }
       }
     }
-  } else {
-    // down: each 32-row slice of the wave's tile is converted and transposed
-    // through LDS, then stored 16 bytes per lane, 256 contiguous bytes per row
-    constexpr int kTL = 128 + 8;
-    static_assert(4 * 32 * kTL * 2 <= (int)(2 * kWABuf), "transpose buffers fit the activation buffers");
-    _Float16 *tb = (_Float16 *)smem + wave * 32 * kTL;
-    __syncthreads();  // every wave is done reading the activation buffers
-    if (wvalid) {
-#pragma unroll
-      for (int tm = 0; tm < 4; ++tm) {
-        if (tm * 32 >= nrows) break;
-        const int row = tm * 32 + j;
-        float rsc = 0.f;  // rows past the expert's end: zeros, never stored
-        if (row < nrows) rsc = __builtin_bit_cast(float, a.rowinfo[rbeg + row].w) * ginv;
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int c4 = 8 * g4 + cl;
-#pragma unroll
-          for (int tn = 0; tn < 4; ++tn) {
-            const f4 ic = *(const f4 *)(cinv + tn * 32 + c4);
-            h2 o[2];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float v = acc[tn][tm][4 * g4 + i] * (rsc * ic[i]);
-              vmax = fmaxf(vmax, fabsf(v));
-              vnan = __builtin_fmaf(v, 0.f, vnan);  // stays 0 unless v is NaN or infinite
-              o[i >> 1][i & 1] = (_Float16)fminf(fmaxf(v, -65504.f), 65504.f);
-            }
-            *(u2 *)(tb + j * kTL + tn * 32 + c4) = u2{as_u32(o[0]), as_u32(o[1])};
-          }
-        }
-        // the wave reads back what its own lanes wrote (in-order LDS queue)
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-        __builtin_amdgcn_wave_barrier();
-        const int ch = lane & 15;
-#pragma unroll
-        for (int it = 0; it < 8; ++it) {
-          const int rr = it * 4 + (lane >> 4);
-          const int orow = tm * 32 + rr;
-          const u4 v = *(const u4 *)(tb + rr * kTL + ch * 8);
-          if (orow < nrows)
-            *(u4 *)(a.partial + (size_t)a.rowinfo[rbeg + orow].x * a.H + cb + ch * 8) = v;
-        }
-        __builtin_amdgcn_s_waitcnt(0xC07F);
-        __builtin_amdgcn_wave_barrier();
-      }
-    }
   }
-  sat |= !(vmax <= 65504.f) || vnan != 0.f;
   if (__builtin_amdgcn_ballot_w64(sat != 0u) != 0ull && lane == 0) atomicOr(a.flags, 1u);
 }
 
@@ -1359,19 +1319,20 @@ static hipError_t run_prefill(GemmArgs a, int64_t R, const GemmLaunch &s) {
   return hipGetLastError();
 }
 
-template <int FMT, int STAGE>
+template <int FMT, int TN>
 static hipError_t run_prefill_wide(GemmArgs a, int64_t R, const GemmLaunch &s) {
-  a.tiles = STAGE == 0 ? (a.I + kWBN / 2 - 1) / (kWBN / 2) : (a.H + kWBN - 1) / kWBN;
+  constexpr int BC = WideShape<TN>::BC;
+  a.tiles = (a.I + BC / 2 - 1) / (BC / 2);
   const int64_t max_mt = R / kBM + a.E;  // >= sum_e ceil(n_e / kBM)
   const int64_t grid = 8 * ((max_mt * a.tiles + 7) / 8);
-  const size_t lds = 2 * kWABuf + 2 * kWBN * sizeof(float);  // 72 KiB: above the default limit
+  constexpr size_t lds = WideShape<TN>::LDS;  // above the default limit
   static bool attr_set = false;
   if (!attr_set) {
-    (void)hipFuncSetAttribute((const void *)gemm_prefill_wide<FMT, STAGE>,
+    (void)hipFuncSetAttribute((const void *)gemm_prefill_wide<FMT, TN>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     attr_set = true;
   }
-  hipExtLaunchKernelGGL((gemm_prefill_wide<FMT, STAGE>), dim3((unsigned)grid), dim3(256), (uint32_t)lds,
+  hipExtLaunchKernelGGL((gemm_prefill_wide<FMT, TN>), dim3((unsigned)grid), dim3(256), (uint32_t)lds,
                         s.stream, s.start, s.stop, 0u, a);
   return hipGetLastError();
 }
@@ -1389,12 +1350,18 @@ static hipError_t dispatch(const LayerDims &L, const FwdPtrs &P, const Workspace
       default: return run_decode_ks<FMT_NVFP4, STAGE>(a, slots, s);
     }
   }
+  // two 32-column tiles per wave, two blocks per CU: equal to four tiles at
+  // one block per CU on FP8 gate/up at T=4096 (271 us) and faster on NVFP4 Zipf
+  // T=16384 (887 against 897 us) and INT4 T=4096 (268 against 282 us)
+  constexpr int TN = 2;
+  const bool wide = STAGE == 0 && a.K % (WideShape<TN>::SPB * kWK) == 0;
   switch (L.fmt) {
     // gate/up (K = H) runs the register-streamed kernel; the down projection
     // (K = I, scattered output rows) measured faster on the LDS-staged one
-    case FMT_INT4: return STAGE == 0 ? run_prefill_wide<FMT_INT4, 0>(a, R, s) : run_prefill<FMT_INT4, 1>(a, R, s);
-    case FMT_FP8: return STAGE == 0 ? run_prefill_wide<FMT_FP8, 0>(a, R, s) : run_prefill<FMT_FP8, 1>(a, R, s);
-    default: return STAGE == 0 ? run_prefill_wide<FMT_NVFP4, 0>(a, R, s) : run_prefill<FMT_NVFP4, 1>(a, R, s);
+    // (K a multiple of kWSPB k steps; other shapes take the LDS-staged one too)
+    case FMT_INT4: return wide ? run_prefill_wide<FMT_INT4, TN>(a, R, s) : run_prefill<FMT_INT4, STAGE>(a, R, s);
+    case FMT_FP8: return wide ? run_prefill_wide<FMT_FP8, TN>(a, R, s) : run_prefill<FMT_FP8, STAGE>(a, R, s);
+    default: return wide ? run_prefill_wide<FMT_NVFP4, TN>(a, R, s) : run_prefill<FMT_NVFP4, STAGE>(a, R, s);
   }
 }
 
