@@ -387,8 +387,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode(GemmArgs a) {
 }
 
 // ===========================================================================
-// Prefill path: tiles of 128 grouped rows x 256 weight columns, stepping k by
-// 64.  The weight tile is dequantized once per block into LDS as FP16 and
+// Prefill down projection: tiles of 128 grouped rows x 256 weight columns,
+// stepping k by 64.  The weight tile is dequantized once per block into LDS as FP16 and
 // shared by the 4 waves; the waves form a 2 x 2 grid and each owns 64 rows x
 // 128 columns (2 x 4 MFMA 32x32x16 tiles), so every 16-k step reads 6 operand
 // fragments from LDS for 8 MFMAs.
@@ -400,10 +400,6 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode(GemmArgs a) {
 // accumulator of that column is multiplied by 2^-p at the end.  NVFP4
 // e2m1 * e4m3 products are exact in FP16; its global scale divides the
 // finished sum.
-//
-// For the gate/up projection a block covers 128 gate columns and the same 128
-// up columns; wave (wm, wn) holds gate columns 64 wn + [0, 64) in tiles 0-1
-// and the matching up columns in tiles 2-3, so SwiGLU runs in registers.
 //
 // Pipeline: one LDS buffer, two blocks per CU (one block's barriers overlap
 // the other's work); the HBM loads of k step s + 1 are issued before step s's
@@ -433,9 +429,9 @@ struct PrefillRegs {
   uint32_t s[4];  // INT4: FP16 scale bits; FP8: FP32 scale bits; NVFP4: E4M3 scale byte
 };
 
-template <int FMT, int STAGE>
+template <int FMT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void gemm_prefill(GemmArgs a) {
+void gemm_prefill_down(GemmArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   float *colinv = (float *)(smem + kPrefillStage);  // [kBN]: 2^-p of each B row
   float *rowfs = colinv + kBN;                                // [kBN]: 2^p of each B row
@@ -467,15 +463,14 @@ void gemm_prefill(GemmArgs a) {
   for (int p = 0; p < 4; ++p) {
     const int rr = (tid >> 3) + 32 * p;
     const int r = rbeg + (rr < nrows ? rr : nrows - 1);
-    const size_t arow = STAGE == 0 ? (size_t)a.rowinfo[r].y : (size_t)r;
-    asrc[p] = a.a_src + arow * K + (tid & 7) * 8;
+    asrc[p] = a.a_src + (size_t)r * K + (tid & 7) * 8;  // h rows are in grouped order
   }
-  const int nb = nt * (STAGE == 0 ? kBN / 2 : kBN);
+  const int nb = nt * kBN;
   // global weight row of local B row lr.  (down: H need only be a multiple of
   // 128, so the last N tile may be half empty; its missing rows re-read row
   // H-1 and are never stored)
   auto grow = [&](int lr) {
-    return STAGE == 0 ? (lr < kBN / 2 ? nb + lr : a.I + nb + lr - kBN / 2) : min(nb + lr, N - 1);
+    return min(nb + lr, N - 1);
   };
   // ---- power of two of B row tid (from its largest scale), shared via LDS
   if (FMT != FMT_NVFP4) {
@@ -522,14 +517,8 @@ void gemm_prefill(GemmArgs a) {
   int tcol[4], bl[4];
 #pragma unroll
   for (int tn = 0; tn < 4; ++tn) {
-    if (STAGE == 0) {
-      const int c = wn * 64 + (tn & 1) * 32;
-      bl[tn] = (tn < 2 ? 0 : kBN / 2) + c + j;
-      tcol[tn] = (tn < 2 ? nb : a.I + nb) + c;
-    } else {
-      bl[tn] = wn * 128 + tn * 32 + j;
-      tcol[tn] = nb + wn * 128 + tn * 32;  // may reach past H in a half tile
-    }
+    bl[tn] = wn * 128 + tn * 32 + j;
+    tcol[tn] = nb + wn * 128 + tn * 32;  // may reach past H in a half tile
   }
 
   auto gload = [&](PrefillRegs<FMT> &R, int ks) {
@@ -566,7 +555,7 @@ void gemm_prefill(GemmArgs a) {
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       u4 v = R.a[p];
-      if (FMT == FMT_INT4 && STAGE == 1) v = perm_0415(v);  // gate/up rows come INT4-ordered
+      if (FMT == FMT_INT4) v = perm_0415(v);  // h is stored in natural order
       *(u4 *)(As + ((tid >> 3) + 32 * p) * kLD + (tid & 7) * 8) = v;
     }
 #pragma unroll
@@ -664,87 +653,56 @@ void gemm_prefill(GemmArgs a) {
   const float ginv = FMT == FMT_NVFP4 ? 1.0f / a.gscale[e] : 1.0f;
   const int cl = 4 * (lane >> 5);
   uint32_t sat = 0u;
-  float vmax = 0.f, vnan = 0.f;  // down: largest |value| before the FP16 clamp; NaN sentinel
+  float vmax = 0.f, vnan = 0.f;  // largest |value| before the FP16 clamp; NaN sentinel
   typedef uint32_t u2 __attribute__((ext_vector_type(2)));
-  if constexpr (STAGE == 0) {
-    // gate/up: SwiGLU, then 8 bytes per lane straight to the rows of h
+  // The rows go to scattered slots of the partial buffer, so each
+  // 32-row half of the wave's tile is converted and transposed through LDS
+  // and every store writes 256 contiguous bytes of a row (16 per lane)
+  // instead of 8 bytes in each of 32 rows per instruction.
+  constexpr int kTL = 128 + 8;  // LDS row stride in halves
+  static_assert(4 * 32 * kTL * 2 <= (int)kPrefillStage, "transpose buffers fit the tile buffer");
+  _Float16 *tb = (_Float16 *)smem + wave * 32 * kTL;
+  const int ocol = tcol[0];  // first output column of the wave
+  __syncthreads();           // every wave is done reading the k-step tiles
 #pragma unroll
-    for (int tm = 0; tm < 2; ++tm) {
-      const int row = wm * 64 + tm * 32 + j;
-      if (row >= nrows) continue;
-      const int r = rbeg + row;
-      const float rsc = __builtin_bit_cast(float, a.rowinfo[r].z) * ginv;
+  for (int tm = 0; tm < 2; ++tm) {
+    const int row = wm * 64 + tm * 32 + j;
+    float rsc = 0.f;  // rows past the expert's end: zeros, never stored
+    if (row < nrows) rsc = __builtin_bit_cast(float, a.rowinfo[rbeg + row].w) * ginv;
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int c4 = 8 * g4 + cl;  // first of this lane's 4 columns in the tile
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int c4 = 8 * g4 + cl;
 #pragma unroll
-        for (int tn = 0; tn < 2; ++tn) {
-          const f4 ig = *(const f4 *)(colinv + bl[tn] - j + c4);
-          const f4 iu = *(const f4 *)(colinv + bl[tn + 2] - j + c4);
-          h2 o[2];
+      for (int tn = 0; tn < 4; ++tn) {
+        const f4 ic = *(const f4 *)(colinv + bl[tn] - j + c4);
+        h2 o[2];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float gv = acc[tm][tn][4 * g4 + i] * (rsc * ig[i]);
-            const float uv = acc[tm][tn + 2][4 * g4 + i] * (rsc * iu[i]);
-            float hv = silu(gv) * uv;
-            const float hc = fminf(fmaxf(hv, -65504.f), 65504.f);
-            sat |= hc != hv;
-            o[i >> 1][i & 1] = (_Float16)hc;
-          }
-          *(u2 *)(a.h_out + (size_t)r * a.I + tcol[tn] + c4) = u2{as_u32(o[0]), as_u32(o[1])};
+        for (int i = 0; i < 4; ++i) {
+          const float v = acc[tm][tn][4 * g4 + i] * (rsc * ic[i]);
+          vmax = fmaxf(vmax, fabsf(v));
+          vnan = __builtin_fmaf(v, 0.f, vnan);  // stays 0 unless v is NaN or infinite
+          o[i >> 1][i & 1] = (_Float16)fminf(fmaxf(v, -65504.f), 65504.f);
         }
+        *(u2 *)(tb + j * kTL + tn * 32 + c4) = u2{as_u32(o[0]), as_u32(o[1])};
+        __builtin_amdgcn_sched_barrier(0);  // column group by group (register pressure)
       }
     }
-  } else {
-    // down: the rows go to scattered slots of the partial buffer, so each
-    // 32-row half of the wave's tile is converted and transposed through LDS
-    // and every store writes 256 contiguous bytes of a row (16 per lane)
-    // instead of 8 bytes in each of 32 rows per instruction.
-    constexpr int kTL = 128 + 8;  // LDS row stride in halves
-    static_assert(4 * 32 * kTL * 2 <= (int)kPrefillStage, "transpose buffers fit the tile buffer");
-    _Float16 *tb = (_Float16 *)smem + wave * 32 * kTL;
-    const int ocol = tcol[0];  // first output column of the wave
-    __syncthreads();           // every wave is done reading the k-step tiles
+    // the wave reads back what its own lanes wrote: its LDS operations run
+    // in order, and the compiler keeps them ordered (same buffer)
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+    const int ch = lane & 15;
 #pragma unroll
-    for (int tm = 0; tm < 2; ++tm) {
-      const int row = wm * 64 + tm * 32 + j;
-      float rsc = 0.f;  // rows past the expert's end: zeros, never stored
-      if (row < nrows) rsc = __builtin_bit_cast(float, a.rowinfo[rbeg + row].w) * ginv;
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int c4 = 8 * g4 + cl;
-#pragma unroll
-        for (int tn = 0; tn < 4; ++tn) {
-          const f4 ic = *(const f4 *)(colinv + bl[tn] - j + c4);
-          h2 o[2];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float v = acc[tm][tn][4 * g4 + i] * (rsc * ic[i]);
-            vmax = fmaxf(vmax, fabsf(v));
-            vnan = __builtin_fmaf(v, 0.f, vnan);  // stays 0 unless v is NaN or infinite
-            o[i >> 1][i & 1] = (_Float16)fminf(fmaxf(v, -65504.f), 65504.f);
-          }
-          *(u2 *)(tb + j * kTL + tn * 32 + c4) = u2{as_u32(o[0]), as_u32(o[1])};
-          __builtin_amdgcn_sched_barrier(0);  // column group by group (register pressure)
-        }
-      }
-      // the wave reads back what its own lanes wrote: its LDS operations run
-      // in order, and the compiler keeps them ordered (same buffer)
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-      __builtin_amdgcn_wave_barrier();
-      const int ch = lane & 15;
-#pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const int rr = it * 4 + (lane >> 4);
-        const int orow = wm * 64 + tm * 32 + rr;
-        const u4 v = *(const u4 *)(tb + rr * kTL + ch * 8);
-        if (orow < nrows && ocol + ch * 8 < N)  // a half tile ends at H
-          *(u4 *)(a.partial + (size_t)a.rowinfo[rbeg + orow].x * a.H + ocol + ch * 8) = v;
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      __builtin_amdgcn_s_waitcnt(0xC07F);
-      __builtin_amdgcn_wave_barrier();
+    for (int it = 0; it < 8; ++it) {
+      const int rr = it * 4 + (lane >> 4);
+      const int orow = wm * 64 + tm * 32 + rr;
+      const u4 v = *(const u4 *)(tb + rr * kTL + ch * 8);
+      if (orow < nrows && ocol + ch * 8 < N)  // a half tile ends at H
+        *(u4 *)(a.partial + (size_t)a.rowinfo[rbeg + orow].x * a.H + ocol + ch * 8) = v;
+      __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_wave_barrier();
   }
   sat |= !(vmax <= 65504.f) || vnan != 0.f;  // NaN counts as saturated, as in to_f16_sat
   if (__builtin_amdgcn_ballot_w64(sat != 0u) != 0ull && lane == 0) atomicOr(a.flags, 1u);
@@ -1301,20 +1259,19 @@ static hipError_t run_decode_ks(GemmArgs a, int slots, const GemmLaunch &s) {
   }
 }
 
-template <int FMT, int STAGE>
-static hipError_t run_prefill(GemmArgs a, int64_t R, const GemmLaunch &s) {
-  // gate/up: I is a multiple of 128, so kBN / 2 = 128 columns tile it exactly
-  a.tiles = STAGE == 0 ? a.I / (kBN / 2) : (a.H + kBN - 1) / kBN;
+template <int FMT>
+static hipError_t run_prefill_down(GemmArgs a, int64_t R, const GemmLaunch &s) {
+  a.tiles = (a.H + kBN - 1) / kBN;       // H need only be a multiple of 128
   const int64_t max_mt = R / kBM + a.E;  // >= sum_e ceil(n_e / kBM)
   const int64_t grid = 8 * ((max_mt * a.tiles + 7) / 8);
   const size_t lds = kPrefillStage + 2 * kBN * sizeof(float);
   static bool attr_set = false;
   if (!attr_set) {
-    (void)hipFuncSetAttribute((const void *)gemm_prefill<FMT, STAGE>,
+    (void)hipFuncSetAttribute((const void *)gemm_prefill_down<FMT>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     attr_set = true;
   }
-  hipExtLaunchKernelGGL((gemm_prefill<FMT, STAGE>), dim3((unsigned)grid), dim3(256), (uint32_t)lds, s.stream,
+  hipExtLaunchKernelGGL((gemm_prefill_down<FMT>), dim3((unsigned)grid), dim3(256), (uint32_t)lds, s.stream,
                         s.start, s.stop, 0u, a);
   return hipGetLastError();
 }
@@ -1322,6 +1279,7 @@ static hipError_t run_prefill(GemmArgs a, int64_t R, const GemmLaunch &s) {
 template <int FMT, int TN>
 static hipError_t run_prefill_wide(GemmArgs a, int64_t R, const GemmLaunch &s) {
   constexpr int BC = WideShape<TN>::BC;
+  if (a.K % (WideShape<TN>::SPB * kWK) != 0) return hipErrorInvalidValue;  // K fills whole LDS buffers
   a.tiles = (a.I + BC / 2 - 1) / (BC / 2);
   const int64_t max_mt = R / kBM + a.E;  // >= sum_e ceil(n_e / kBM)
   const int64_t grid = 8 * ((max_mt * a.tiles + 7) / 8);
@@ -1350,18 +1308,22 @@ static hipError_t dispatch(const LayerDims &L, const FwdPtrs &P, const Workspace
       default: return run_decode_ks<FMT_NVFP4, STAGE>(a, slots, s);
     }
   }
-  // two 32-column tiles per wave, two blocks per CU: equal to four tiles at
-  // one block per CU on FP8 gate/up at T=4096 (271 us) and faster on NVFP4 Zipf
-  // T=16384 (887 against 897 us) and INT4 T=4096 (268 against 282 us)
-  constexpr int TN = 2;
-  const bool wide = STAGE == 0 && a.K % (WideShape<TN>::SPB * kWK) == 0;
+  // gate/up runs the register-streamed kernel with two 32-column tiles per
+  // wave at two blocks per CU (equal to four tiles at one block per CU on FP8
+  // T=4096 gate/up, 271 us, and faster on NVFP4 Zipf T=16384, 887 against
+  // 897 us, and INT4 T=4096, 268 against 282 us); the down projection (K = I,
+  // scattered output rows) runs the LDS-staged kernel, measured faster there
+  if constexpr (STAGE == 0) {
+    switch (L.fmt) {
+      case FMT_INT4: return run_prefill_wide<FMT_INT4, 2>(a, R, s);
+      case FMT_FP8: return run_prefill_wide<FMT_FP8, 2>(a, R, s);
+      default: return run_prefill_wide<FMT_NVFP4, 2>(a, R, s);
+    }
+  }
   switch (L.fmt) {
-    // gate/up (K = H) runs the register-streamed kernel; the down projection
-    // (K = I, scattered output rows) measured faster on the LDS-staged one
-    // (K a multiple of kWSPB k steps; other shapes take the LDS-staged one too)
-    case FMT_INT4: return wide ? run_prefill_wide<FMT_INT4, TN>(a, R, s) : run_prefill<FMT_INT4, STAGE>(a, R, s);
-    case FMT_FP8: return wide ? run_prefill_wide<FMT_FP8, TN>(a, R, s) : run_prefill<FMT_FP8, STAGE>(a, R, s);
-    default: return wide ? run_prefill_wide<FMT_NVFP4, TN>(a, R, s) : run_prefill<FMT_NVFP4, STAGE>(a, R, s);
+    case FMT_INT4: return run_prefill_down<FMT_INT4>(a, R, s);
+    case FMT_FP8: return run_prefill_down<FMT_FP8>(a, R, s);
+    default: return run_prefill_down<FMT_NVFP4>(a, R, s);
   }
 }
 
