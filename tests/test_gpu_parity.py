@@ -156,6 +156,33 @@ def test_hidden_not_multiple_of_256(fmt, T):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+def test_prefill_tile_edges(fmt):
+    """Routing crafted so the experts hold 1, 31, 32, 33, 96, 97, 128 and 130
+    rows: the prefill GEMMs see every count of 32-row subtiles that hold rows
+    in a 128-row tile (1 to 4), a full tile, and a second tile with 2 rows."""
+    log(f"[tile-edges] fmt={fmt}")
+    E, H, I, k = 8, 256, 256, 2
+    counts = np.array([1, 31, 32, 33, 96, 97, 128, 130])
+    T = int(counts.sum()) // k
+    assert T * k > 16 * E                     # the prefill path
+    ids = np.repeat(np.arange(E), counts)     # sorted; no expert holds more than T rows,
+    first, second = ids[:T], ids[T:]          # so a token's two experts differ
+    assert np.all(first != second)
+    rng = np.random.default_rng(21)
+    perm = rng.permutation(T)
+    first, second = first[perm], second[perm]
+    lg = rng.uniform(-1.0, 0.0, size=(T, E)).astype(np.float32)
+    lg[np.arange(T), first] = 3.0 + rng.uniform(0.0, 0.5, size=T).astype(np.float32)
+    lg[np.arange(T), second] = 2.0 + rng.uniform(0.0, 0.5, size=T).astype(np.float32)
+    p13, p2 = quantized_layer(fmt, 21, 0, E, H, I)
+    g = GpuLayer(p13, p2, k)
+    x = synth.hidden_bf16(21, 0, T, H)
+    ids, _ = moe.route(lg, k)
+    assert np.array_equal(np.bincount(ids.ravel(), minlength=E), counts)
+    _check_layer(g, lg, x, tag=f"{fmt} tile edges")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("T", [3, 100])
 def test_hidden_above_2048(fmt, T):
     """H = 2304 > 2048: decode (T=3) scans each row for its power of two inside

@@ -387,30 +387,20 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode(GemmArgs a) {
 }
 
 // ===========================================================================
-// Prefill down projection: tiles of 128 grouped rows x 256 weight columns,
-// stepping k by 64.  The weight tile is dequantized once per block into LDS as FP16 and
-// shared by the 4 waves; the waves form a 2 x 2 grid and each owns 64 rows x
-// 128 columns (2 x 4 MFMA 32x32x16 tiles), so every 16-k step reads 6 operand
-// fragments from LDS for 8 MFMAs.
+// Prefill path (many rows per expert).  Tiles of 128 grouped rows of one
+// expert; weight codes are dequantized exactly into FP16 MFMA operands:
+// INT4 (c - 8) * s and FP8 e4m3 * s carry their group / block scale,
+// multiplied by a power of two 2^p per weight column chosen from the column's
+// largest scale so the values sit high in FP16 range; the product is rounded
+// once to FP16 (relative error <= 2^-11) and the accumulator of that column is
+// multiplied by 2^-p at the end.  NVFP4 e2m1 * e4m3 products are exact in
+// FP16; its global scale divides the finished sum.
 //
-// Dequantization into the tile: INT4 (c - 8) * s and FP8 e4m3 * sinv carry
-// their group / block scale, multiplied by a power of two 2^p per weight row
-// chosen from the row's largest scale so the values sit high in FP16 range;
-// the product is rounded once to FP16 (relative error <= 2^-11) and the
-// accumulator of that column is multiplied by 2^-p at the end.  NVFP4
-// e2m1 * e4m3 products are exact in FP16; its global scale divides the
-// finished sum.
-//
-// Pipeline: one LDS buffer, two blocks per CU (one block's barriers overlap
-// the other's work); the HBM loads of k step s + 1 are issued before step s's
-// MFMAs.  (A double-buffered variant with one block per CU and loads two steps
-// ahead measured slower.)
 // Tiles are numbered (M-tile, N-tile) with N fastest and dealt to the 8 XCDs
 // in contiguous ranges (blocks are dispatched to XCDs round robin), so tiles
 // that share activation rows or an expert's weights run on the same L2.
 // ===========================================================================
-constexpr int kBM = kPrefillBM, kBN = 256, kBK = 64, kLD = kBK + 8;  // kLD in halves
-constexpr size_t kPrefillStage = (size_t)(kBM + kBN) * kLD * 2;        // bytes per LDS stage
+constexpr int kBM = kPrefillBM;  // grouped rows per M tile
 
 // Power of two that maps a row's largest weight magnitude `m` to [2^14, 2^15).
 __device__ __forceinline__ float row_pow2(float m, float *inv) {
@@ -419,306 +409,15 @@ __device__ __forceinline__ float row_pow2(float m, float *inv) {
   return pow2f(sh);
 }
 
-// Raw HBM data of one k step for one thread.  B rows are taken 4 lanes to a
-// row (rows 64 i + tid / 4, i = 0..3; 16 consecutive k each, chunk tid % 4), so
-// one wave load touches 16 weight rows with contiguous bytes per row.
-template <int FMT>
-struct PrefillRegs {
-  u4 a[4];
-  uint32_t b[4][FMT == FMT_FP8 ? 4 : 2];  // 16 codes of row i
-  uint32_t s[4];  // INT4: FP16 scale bits; FP8: FP32 scale bits; NVFP4: E4M3 scale byte
-};
-
-template <int FMT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void gemm_prefill_down(GemmArgs a) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  float *colinv = (float *)(smem + kPrefillStage);  // [kBN]: 2^-p of each B row
-  float *rowfs = colinv + kBN;                                // [kBN]: 2^p of each B row
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
-  // ---- tile of this block
-  const int NT = a.tiles;
-  const int n_tiles = a.mtile[a.E] * NT;
-  const int per_xcd = (n_tiles + 7) >> 3;
-  const int xslot = blockIdx.x >> 3;
-  if (xslot >= per_xcd) return;
-  const int L = (blockIdx.x & 7) * per_xcd + xslot;
-  if (L >= n_tiles) return;
-  const int mt = L / NT, nt = L - mt * NT;
-  int lo = 0, hi = a.E - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (a.mtile[mid] <= mt) lo = mid; else hi = mid - 1;
-  }
-  const int e = lo;
-  const int rbeg = a.offsets[e] + (mt - a.mtile[e]) * kBM;
-  const int nrows = min(kBM, a.offsets[e + 1] - rbeg);
-  const int K = a.K, N = a.N, G = K / 128, nK = K / kBK;
-  const size_t rowbytes = FMT == FMT_FP8 ? (size_t)K : (size_t)K / 2;
-
-  // ---- A staging: row (tid >> 3) + 32 p, 16-byte chunk tid & 7
-  const _Float16 *asrc[4];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int rr = (tid >> 3) + 32 * p;
-    const int r = rbeg + (rr < nrows ? rr : nrows - 1);
-    asrc[p] = a.a_src + (size_t)r * K + (tid & 7) * 8;  // h rows are in grouped order
-  }
-  const int nb = nt * kBN;
-  // global weight row of local B row lr.  (down: H need only be a multiple of
-  // 128, so the last N tile may be half empty; its missing rows re-read row
-  // H-1 and are never stored)
-  auto grow = [&](int lr) {
-    return min(nb + lr, N - 1);
-  };
-  // ---- power of two of B row tid (from its largest scale), shared via LDS
-  if (FMT != FMT_NVFP4) {
-    const int gr = grow(tid);
-    float m = 0.f;
-    // 8 scale loads in flight per round trip (indices clamped to the last
-    // group: a repeated value does not change the max)
-    for (int g0 = 0; g0 < G; g0 += 8) {
-      float sv[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int g = min(g0 + u, G - 1);
-        sv[u] = FMT == FMT_INT4 ? (float)((const _Float16 *)a.scale)[((size_t)e * N + gr) * G + g]
-                                : ((const float *)a.scale)[((size_t)e * (N / 128) + gr / 128) * G + g];
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) m = fmaxf(m, fabsf(sv[u]));
-    }
-    float inv;
-    rowfs[tid] = row_pow2(m * (FMT == FMT_INT4 ? 8.f : 448.f), &inv);
-    colinv[tid] = inv;
-  } else {
-    colinv[tid] = 1.f;
-  }
-  // ---- B staging: rows 64 i + (tid >> 2), chunk c = tid & 3 (k 16 c .. 16 c + 16)
-  const int bc = tid & 3;
-  const uint8_t *wsrc[4];
-  const void *ssrc[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int gr = grow(64 * i + (tid >> 2));
-    wsrc[i] = a.w + ((size_t)e * N + gr) * rowbytes + (FMT == FMT_FP8 ? 16 : 8) * bc;
-    if (FMT == FMT_INT4)
-      ssrc[i] = (const _Float16 *)a.scale + ((size_t)e * N + gr) * G;
-    else if (FMT == FMT_FP8)
-      ssrc[i] = (const float *)a.scale + ((size_t)e * (N / 128) + gr / 128) * G;
-    else
-      ssrc[i] = (const uint8_t *)a.scale + ((size_t)e * N + gr) * (K / 16) + bc;
-  }
-
-  // ---- the wave's four 32-wide column tiles: B row of this lane in each
-  // (MFMA A operand) and the tile's first global weight row
-  const int j = lane & 31;
-  int tcol[4], bl[4];
-#pragma unroll
-  for (int tn = 0; tn < 4; ++tn) {
-    bl[tn] = wn * 128 + tn * 32 + j;
-    tcol[tn] = nb + wn * 128 + tn * 32;  // may reach past H in a half tile
-  }
-
-  auto gload = [&](PrefillRegs<FMT> &R, int ks) {
-    const int kb = ks * kBK;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) R.a[p] = *(const u4 *)(asrc[p] + kb);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (FMT == FMT_FP8) {
-        const u4 v = *(const u4 *)(wsrc[i] + kb);  // cached: every M tile of the expert reads it
-#pragma unroll
-        for (int q = 0; q < 4; ++q) R.b[i][q] = v[q];
-      } else {
-        typedef uint32_t u2 __attribute__((ext_vector_type(2)));
-        const u2 v = *(const u2 *)(wsrc[i] + kb / 2);
-        R.b[i][0] = v[0];
-        R.b[i][1] = v[1];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (FMT == FMT_INT4)
-        R.s[i] = ((const uint16_t *)ssrc[i])[kb >> 7];
-      else if (FMT == FMT_FP8)
-        R.s[i] = __builtin_bit_cast(uint32_t, ((const float *)ssrc[i])[kb >> 7]);
-      else
-        R.s[i] = ((const uint8_t *)ssrc[i])[kb / 16];
-    }
-  };
-  float rowf[4] = {1.f, 1.f, 1.f, 1.f};
-  auto stage = [&](const PrefillRegs<FMT> &R) {
-    _Float16 *As = (_Float16 *)smem;
-    _Float16 *Bs = As + kBM * kLD;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      u4 v = R.a[p];
-      if (FMT == FMT_INT4) v = perm_0415(v);  // h is stored in natural order
-      *(u4 *)(As + ((tid >> 3) + 32 * p) * kLD + (tid & 7) * 8) = v;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      h8 v[2];
-      if (FMT == FMT_INT4) {
-        v[0] = unpack_int4(R.b[i][0]);
-        v[1] = unpack_int4(R.b[i][1]);
-      } else if (FMT == FMT_FP8) {
-        v[0] = unpack_fp8(R.b[i][0], R.b[i][1]);
-        v[1] = unpack_fp8(R.b[i][2], R.b[i][3]);
-      } else {
-        const _Float16 sb = e4m3_to_f16(R.s[i]);
-        v[0] = unpack_nvfp4(R.b[i][0], sb);
-        v[1] = unpack_nvfp4(R.b[i][1], sb);
-      }
-      if (FMT != FMT_NVFP4) {
-        const float sv = FMT == FMT_INT4 ? (float)__builtin_bit_cast(_Float16, (uint16_t)R.s[i])
-                                         : __builtin_bit_cast(float, R.s[i]);
-        const _Float16 s16 = (_Float16)(sv * rowf[i]);
-        const h2 sc = {s16, s16};
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          u4 w = as_u4(v[h]);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) w[q] = as_u32(as_h2(w[q]) * sc);
-          v[h] = as_h8(w);
-        }
-      }
-      _Float16 *bdst = Bs + (64 * i + (tid >> 2)) * kLD + 16 * bc;
-      *(h8 *)bdst = v[0];
-      *(h8 *)(bdst + 8) = v[1];
-    }
-  };
-  __syncthreads();  // rowfs / colinv
-  if (FMT != FMT_NVFP4) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) rowf[i] = rowfs[64 * i + (tid >> 2)];
-  }
-
-  f16v acc[2][4];
-#pragma unroll
-  for (int tm = 0; tm < 2; ++tm)
-#pragma unroll
-    for (int tn = 0; tn < 4; ++tn)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[tm][tn][i] = 0.f;
-
-  // NV: the wave's 32-row M subtiles that hold grouped rows of the expert
-  // (the last M tile of an expert is often partly empty; MFMAs of empty
-  // subtiles are skipped, which frees the matrix unit for the other block)
-  auto compute = [&](auto nv_c) {
-    constexpr int NV = decltype(nv_c)::value;
-    const _Float16 *As = (const _Float16 *)smem;
-    const _Float16 *Bs = As + kBM * kLD;
-#pragma unroll
-    for (int s = 0; s < kBK / 16; ++s) {
-      const int kk = s * 16 + 8 * (lane >> 5);
-      h8 av[2], bv[4];
-#pragma unroll
-      for (int tm = 0; tm < NV; ++tm) av[tm] = *(const h8 *)(As + (wm * 64 + tm * 32 + j) * kLD + kk);
-#pragma unroll
-      for (int tn = 0; tn < 4; ++tn)
-        if (NV > 0) bv[tn] = *(const h8 *)(Bs + bl[tn] * kLD + kk);
-#pragma unroll
-      for (int tm = 0; tm < NV; ++tm)
-#pragma unroll
-        for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = mfma32(bv[tn], av[tm], acc[tm][tn]);
-    }
-  };
-  // every variant runs the same barriers: all waves take part in the staging
-  auto main_loop = [&](auto nv_c) {
-    PrefillRegs<FMT> R;
-    gload(R, 0);
-    for (int ks = 0; ks < nK; ++ks) {
-      __syncthreads();
-      stage(R);
-      __syncthreads();
-      if (ks + 1 < nK) gload(R, ks + 1);
-      compute(nv_c);
-    }
-  };
-  const int nv = min(2, max(0, (nrows - wm * 64 + 31) / 32));  // wave-uniform
-  if (nv == 2)
-    main_loop(std::integral_constant<int, 2>{});
-  else if (nv == 1)
-    main_loop(std::integral_constant<int, 1>{});
-  else
-    main_loop(std::integral_constant<int, 0>{});
-
-  // ---- epilogue.  The MFMA ran as C[n][m] (weights as its A operand), so
-  // lane l holds grouped row m = l % 32 of each M tile and, in register v,
-  // column 8 (v / 4) + 4 (l / 32) + v % 4 of the tile: four consecutive
-  // columns per group of four registers.
-  const float ginv = FMT == FMT_NVFP4 ? 1.0f / a.gscale[e] : 1.0f;
-  const int cl = 4 * (lane >> 5);
-  uint32_t sat = 0u;
-  float vmax = 0.f, vnan = 0.f;  // largest |value| before the FP16 clamp; NaN sentinel
-  typedef uint32_t u2 __attribute__((ext_vector_type(2)));
-  // The rows go to scattered slots of the partial buffer, so each
-  // 32-row half of the wave's tile is converted and transposed through LDS
-  // and every store writes 256 contiguous bytes of a row (16 per lane)
-  // instead of 8 bytes in each of 32 rows per instruction.
-  constexpr int kTL = 128 + 8;  // LDS row stride in halves
-  static_assert(4 * 32 * kTL * 2 <= (int)kPrefillStage, "transpose buffers fit the tile buffer");
-  _Float16 *tb = (_Float16 *)smem + wave * 32 * kTL;
-  const int ocol = tcol[0];  // first output column of the wave
-  __syncthreads();           // every wave is done reading the k-step tiles
-#pragma unroll
-  for (int tm = 0; tm < 2; ++tm) {
-    const int row = wm * 64 + tm * 32 + j;
-    float rsc = 0.f;  // rows past the expert's end: zeros, never stored
-    if (row < nrows) rsc = __builtin_bit_cast(float, a.rowinfo[rbeg + row].w) * ginv;
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int c4 = 8 * g4 + cl;
-#pragma unroll
-      for (int tn = 0; tn < 4; ++tn) {
-        const f4 ic = *(const f4 *)(colinv + bl[tn] - j + c4);
-        h2 o[2];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float v = acc[tm][tn][4 * g4 + i] * (rsc * ic[i]);
-          vmax = fmaxf(vmax, fabsf(v));
-          vnan = __builtin_fmaf(v, 0.f, vnan);  // stays 0 unless v is NaN or infinite
-          o[i >> 1][i & 1] = (_Float16)fminf(fmaxf(v, -65504.f), 65504.f);
-        }
-        *(u2 *)(tb + j * kTL + tn * 32 + c4) = u2{as_u32(o[0]), as_u32(o[1])};
-        __builtin_amdgcn_sched_barrier(0);  // column group by group (register pressure)
-      }
-    }
-    // the wave reads back what its own lanes wrote: its LDS operations run
-    // in order, and the compiler keeps them ordered (same buffer)
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    __builtin_amdgcn_wave_barrier();
-    const int ch = lane & 15;
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int rr = it * 4 + (lane >> 4);
-      const int orow = wm * 64 + tm * 32 + rr;
-      const u4 v = *(const u4 *)(tb + rr * kTL + ch * 8);
-      if (orow < nrows && ocol + ch * 8 < N)  // a half tile ends at H
-        *(u4 *)(a.partial + (size_t)a.rowinfo[rbeg + orow].x * a.H + ocol + ch * 8) = v;
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    __builtin_amdgcn_wave_barrier();
-  }
-  sat |= !(vmax <= 65504.f) || vnan != 0.f;  // NaN counts as saturated, as in to_f16_sat
-  if (__builtin_amdgcn_ballot_w64(sat != 0u) != 0ull && lane == 0) atomicOr(a.flags, 1u);
-}
-
-// ===========================================================================
-// Prefill gate/up path, weights in registers.  A block of 4 waves covers 128
-// grouped rows of one expert; each wave owns TN 32-column weight tiles and all
-// 128 rows, a TN x 4 grid of MFMA 32x32x16 tiles.  TN = 2 (the one launched):
+// Weights in registers.  A block of 4 waves covers 128 grouped rows of one
+// expert; each wave owns TN 32-column weight tiles and all 128 rows, a TN x 4
+// grid of MFMA 32x32x16 tiles.  TN = 2 (the one launched):
 // 128 accumulators per lane, two blocks per CU; TN = 4: 256 accumulators in
 // the accumulation registers, one block per CU.  Only the FP16 activation tile
 // goes through LDS (written once by the block, read by its 4 waves); every
 // wave streams the packed codes of its own columns into registers one k step
 // ahead and unpacks them straight into the MFMA A operand with the column's
-// scale folded in (the same FP16 values as the LDS-staged kernel above, so
-// the same error bound).
+// scale folded in.
 //
 // Per k step of 64 a lane holds 32 k values of its column: FP8 bytes
 // 16 h + [0, 16) and 32 + 16 h + [0, 16) of the step (h = lane / 32), INT4 and
@@ -726,11 +425,13 @@ void gemm_prefill_down(GemmArgs a) {
 // lane's 8 values s; the activation fragment of lane half h reads the same k
 // offsets (any k order works when both operands follow it).
 //
-// Wave w of column tile nt holds gate columns 64 TN nt + 16 TN w + [0, 16 TN)
-// in tiles [0, TN/2) and the matching up columns in the others, so SwiGLU runs
-// in registers.  A wave whose columns lie past I (I not a multiple of the
-// block width) stages activations and takes the barriers but multiplies and
-// stores nothing.
+// gate/up (STAGE 0): wave w of column tile nt holds gate columns
+// 64 TN nt + 16 TN w + [0, 16 TN) in tiles [0, TN/2) and the matching up
+// columns in the others, so SwiGLU runs in registers.  down (STAGE 1): wave w
+// holds output columns 128 TN nt + 32 TN w + [0, 32 TN); its rows go to
+// scattered partial slots through an LDS transpose.  A wave whose columns lie
+// past the end (I or H not a multiple of the block width) stages activations
+// and takes the barriers but multiplies and stores nothing.
 // ===========================================================================
 constexpr int kWK = 64;  // k step
 
@@ -757,7 +458,7 @@ __device__ __forceinline__ int wide_koff(int s, int hh) {
   return FMT == FMT_FP8 ? 16 * hh + 8 * (s & 1) + 32 * (s >> 1) : 32 * hh + 8 * s;
 }
 
-template <int FMT, int TN>
+template <int FMT, int TN, int STAGE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4 / TN, 4 / TN)))
 void gemm_prefill_wide(GemmArgs a) {
   constexpr int SPB = WideShape<TN>::SPB, LD = WideShape<TN>::LD, BC = WideShape<TN>::BC;
@@ -789,12 +490,13 @@ void gemm_prefill_wide(GemmArgs a) {
   const size_t rowbytes = FMT == FMT_FP8 ? (size_t)K : (size_t)K / 2;
 
   // ---- the wave's columns: global weight row of this lane in each tile
-  const int cb = nt * (BC / 2) + wave * (WC / 2);  // first gate (h) column of the wave
-  const bool wvalid = cb < a.I;                    // wave-uniform
+  // gate/up: first gate (h) column of the wave; down: first output column
+  const int cb = STAGE == 0 ? nt * (BC / 2) + wave * (WC / 2) : nt * BC + wave * WC;
+  const bool wvalid = cb < (STAGE == 0 ? a.I : N);  // wave-uniform
   int gr[TN];
 #pragma unroll
   for (int tn = 0; tn < TN; ++tn) {
-    const int c = (tn < TH ? cb : a.I + cb) + (tn % TH) * 32 + j;
+    const int c = STAGE == 0 ? (tn < TH ? cb : a.I + cb) + (tn % TH) * 32 + j : cb + tn * 32 + j;
     gr[tn] = wvalid ? c : j;  // a row that exists; never stored
   }
 
@@ -831,7 +533,8 @@ void gemm_prefill_wide(GemmArgs a) {
   for (int p = 0; p < 4; ++p) {
     const int rr = (tid >> 3) + 32 * p;
     const int r = rbeg + (rr < nrows ? rr : nrows - 1);
-    asrc[p] = a.a_src + (size_t)a.rowinfo[r].y * K + (tid & 7) * 8;
+    // gate/up: the token's x16 row; down: the grouped h row
+    asrc[p] = a.a_src + (STAGE == 0 ? (size_t)a.rowinfo[r].y : (size_t)r) * K + (tid & 7) * 8;
   }
   // ---- weight and scale streams of the lane's four columns
   const uint8_t *wsrc[TN];
@@ -855,7 +558,8 @@ void gemm_prefill_wide(GemmArgs a) {
     _Float16 *As = (_Float16 *)(smem + buf * ABUF) + sub * kWK;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      *(u4 *)(As + ((tid >> 3) + 32 * p) * LD + (tid & 7) * 8) = ar[p];  // INT4: x16 is stored INT4-ordered
+      // INT4: x16 is stored INT4-ordered, h in natural order
+      *(u4 *)(As + ((tid >> 3) + 32 * p) * LD + (tid & 7) * 8) = FMT == FMT_INT4 && STAGE == 1 ? perm_0415(ar[p]) : ar[p];
     }
   };
   auto load_w = [&](WideRegs<FMT, TN> &R, int ks) {
@@ -1026,7 +730,7 @@ void gemm_prefill_wide(GemmArgs a) {
   const float *cinv = colinv + wave * WC;
   uint32_t sat = 0u;
   typedef uint32_t u2 __attribute__((ext_vector_type(2)));
-  {
+  if constexpr (STAGE == 0) {
     if (wvalid) {
 #pragma unroll
       for (int tm = 0; tm < 4; ++tm) {
@@ -1056,6 +760,58 @@ void gemm_prefill_wide(GemmArgs a) {
         }
       }
     }
+  } else {
+    // down: the rows go to scattered slots of the partial buffer, so each
+    // 32-row slice of the wave's tile is converted and transposed through LDS
+    // and stored 16 bytes per lane, WC * 2 contiguous bytes per row
+    constexpr int TL = WC + 8;     // LDS row stride, halves
+    constexpr int LPR = WC / 8;    // lanes per row
+    constexpr int RPI = 64 / LPR;  // rows per store instruction
+    static_assert(4 * 32 * TL * 2 <= (int)(2 * ABUF), "transpose buffers fit the activation buffers");
+    _Float16 *tb = (_Float16 *)smem + wave * 32 * TL;
+    float vmax = 0.f, vnan = 0.f;  // largest |value| before the FP16 clamp; NaN sentinel
+    __syncthreads();               // every wave is done with the activation buffers
+    if (wvalid) {
+#pragma unroll
+      for (int tm = 0; tm < 4; ++tm) {
+        if (tm * 32 >= nrows) break;
+        const int row = tm * 32 + j;
+        float rsc = 0.f;  // rows past the expert's end: zeros, never stored
+        if (row < nrows) rsc = __builtin_bit_cast(float, a.rowinfo[rbeg + row].w) * ginv;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int c4 = 8 * g4 + cl;
+#pragma unroll
+          for (int tn = 0; tn < TN; ++tn) {
+            const f4 ic = *(const f4 *)(cinv + tn * 32 + c4);
+            h2 o[2];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float v = acc[tn][tm][4 * g4 + i] * (rsc * ic[i]);
+              vmax = fmaxf(vmax, fabsf(v));
+              vnan = __builtin_fmaf(v, 0.f, vnan);  // stays 0 unless v is NaN or infinite
+              o[i >> 1][i & 1] = (_Float16)fminf(fmaxf(v, -65504.f), 65504.f);
+            }
+            *(u2 *)(tb + j * TL + tn * 32 + c4) = u2{as_u32(o[0]), as_u32(o[1])};
+          }
+        }
+        // the wave reads back what its own lanes wrote (in-order LDS queue)
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        __builtin_amdgcn_wave_barrier();
+        const int ch = lane % LPR;
+#pragma unroll
+        for (int it = 0; it < 32 / RPI; ++it) {
+          const int rr = it * RPI + lane / LPR;
+          const int orow = tm * 32 + rr;
+          const u4 v = *(const u4 *)(tb + rr * TL + ch * 8);
+          if (orow < nrows)
+            *(u4 *)(a.partial + (size_t)a.rowinfo[rbeg + orow].x * a.H + cb + ch * 8) = v;
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_wave_barrier();
+      }
+    }
+    sat |= !(vmax <= 65504.f) || vnan != 0.f;  // NaN counts as saturated
   }
   if (__builtin_amdgcn_ballot_w64(sat != 0u) != 0ull && lane == 0) atomicOr(a.flags, 1u);
 }
@@ -1259,38 +1015,21 @@ static hipError_t run_decode_ks(GemmArgs a, int slots, const GemmLaunch &s) {
   }
 }
 
-template <int FMT>
-static hipError_t run_prefill_down(GemmArgs a, int64_t R, const GemmLaunch &s) {
-  a.tiles = (a.H + kBN - 1) / kBN;       // H need only be a multiple of 128
-  const int64_t max_mt = R / kBM + a.E;  // >= sum_e ceil(n_e / kBM)
-  const int64_t grid = 8 * ((max_mt * a.tiles + 7) / 8);
-  const size_t lds = kPrefillStage + 2 * kBN * sizeof(float);
-  static bool attr_set = false;
-  if (!attr_set) {
-    (void)hipFuncSetAttribute((const void *)gemm_prefill_down<FMT>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    attr_set = true;
-  }
-  hipExtLaunchKernelGGL((gemm_prefill_down<FMT>), dim3((unsigned)grid), dim3(256), (uint32_t)lds, s.stream,
-                        s.start, s.stop, 0u, a);
-  return hipGetLastError();
-}
-
-template <int FMT, int TN>
+template <int FMT, int TN, int STAGE>
 static hipError_t run_prefill_wide(GemmArgs a, int64_t R, const GemmLaunch &s) {
   constexpr int BC = WideShape<TN>::BC;
   if (a.K % (WideShape<TN>::SPB * kWK) != 0) return hipErrorInvalidValue;  // K fills whole LDS buffers
-  a.tiles = (a.I + BC / 2 - 1) / (BC / 2);
+  a.tiles = STAGE == 0 ? (a.I + BC / 2 - 1) / (BC / 2) : (a.H + BC - 1) / BC;
   const int64_t max_mt = R / kBM + a.E;  // >= sum_e ceil(n_e / kBM)
   const int64_t grid = 8 * ((max_mt * a.tiles + 7) / 8);
   constexpr size_t lds = WideShape<TN>::LDS;  // above the default limit
   static bool attr_set = false;
   if (!attr_set) {
-    (void)hipFuncSetAttribute((const void *)gemm_prefill_wide<FMT, TN>,
+    (void)hipFuncSetAttribute((const void *)gemm_prefill_wide<FMT, TN, STAGE>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     attr_set = true;
   }
-  hipExtLaunchKernelGGL((gemm_prefill_wide<FMT, TN>), dim3((unsigned)grid), dim3(256), (uint32_t)lds,
+  hipExtLaunchKernelGGL((gemm_prefill_wide<FMT, TN, STAGE>), dim3((unsigned)grid), dim3(256), (uint32_t)lds,
                         s.stream, s.start, s.stop, 0u, a);
   return hipGetLastError();
 }
@@ -1308,22 +1047,12 @@ static hipError_t dispatch(const LayerDims &L, const FwdPtrs &P, const Workspace
       default: return run_decode_ks<FMT_NVFP4, STAGE>(a, slots, s);
     }
   }
-  // gate/up runs the register-streamed kernel with two 32-column tiles per
-  // wave at two blocks per CU (equal to four tiles at one block per CU on FP8
-  // T=4096 gate/up, 271 us, and faster on NVFP4 Zipf T=16384, 887 against
-  // 897 us, and INT4 T=4096, 268 against 282 us); the down projection (K = I,
-  // scattered output rows) runs the LDS-staged kernel, measured faster there
-  if constexpr (STAGE == 0) {
-    switch (L.fmt) {
-      case FMT_INT4: return run_prefill_wide<FMT_INT4, 2>(a, R, s);
-      case FMT_FP8: return run_prefill_wide<FMT_FP8, 2>(a, R, s);
-      default: return run_prefill_wide<FMT_NVFP4, 2>(a, R, s);
-    }
-  }
+  // two 32-column tiles per wave at two blocks per CU (against four tiles at
+  // one block per CU: equal on FP8 T=4096 gate/up, faster on NVFP4 and INT4)
   switch (L.fmt) {
-    case FMT_INT4: return run_prefill_down<FMT_INT4>(a, R, s);
-    case FMT_FP8: return run_prefill_down<FMT_FP8>(a, R, s);
-    default: return run_prefill_down<FMT_NVFP4>(a, R, s);
+    case FMT_INT4: return run_prefill_wide<FMT_INT4, 2, STAGE>(a, R, s);
+    case FMT_FP8: return run_prefill_wide<FMT_FP8, 2, STAGE>(a, R, s);
+    default: return run_prefill_wide<FMT_NVFP4, 2, STAGE>(a, R, s);
   }
 }
 
