@@ -409,13 +409,13 @@ __device__ __forceinline__ float row_pow2(float m, float *inv) {
   return pow2f(sh);
 }
 
-// Weights in registers.  A block of 4 waves covers 128 grouped rows of one
+// Weights in registers.  A block of WPB waves covers 128 grouped rows of one
 // expert; each wave owns TN 32-column weight tiles and all 128 rows, a TN x 4
-// grid of MFMA 32x32x16 tiles.  TN = 2 (the one launched):
-// 128 accumulators per lane, two blocks per CU; TN = 4: 256 accumulators in
-// the accumulation registers, one block per CU.  Only the FP16 activation tile
-// goes through LDS (written once by the block, read by its 4 waves); every
-// wave streams the packed codes of its own columns into registers one k step
+// grid of MFMA 32x32x16 tiles.  TN = 2 (the one launched): 128 accumulators
+// per lane, two waves per SIMD (gate/up: one 8-wave block per CU; down: two
+// 4-wave blocks); TN = 4: 256 accumulators in the accumulation registers, one
+// wave per SIMD.  Only the FP16 activation tile goes through LDS (written
+// once by the block, read by all its waves); every wave streams the packed codes of its own columns into registers one k step
 // ahead and unpacks them straight into the MFMA A operand with the column's
 // scale folded in.
 //
@@ -426,25 +426,28 @@ __device__ __forceinline__ float row_pow2(float m, float *inv) {
 // offsets (any k order works when both operands follow it).
 //
 // gate/up (STAGE 0): wave w of column tile nt holds gate columns
-// 64 TN nt + 16 TN w + [0, 16 TN) in tiles [0, TN/2) and the matching up
+// 16 TN (WPB nt + w) + [0, 16 TN) in tiles [0, TN/2) and the matching up
 // columns in the others, so SwiGLU runs in registers.  down (STAGE 1): wave w
-// holds output columns 128 TN nt + 32 TN w + [0, 32 TN); its rows go to
+// holds output columns 32 TN (WPB nt + w) + [0, 32 TN); its rows go to
 // scattered partial slots through an LDS transpose.  A wave whose columns lie
 // past the end (I or H not a multiple of the block width) stages activations
 // and takes the barriers but multiplies and stores nothing.
 // ===========================================================================
 constexpr int kWK = 64;  // k step
 
-// Shape of a variant with TN 32-column tiles per wave: k steps per activation
-// buffer (one barrier each), LDS row stride in halves, bytes of one buffer,
-// weight columns per block, and dynamic LDS per block.
-template <int TN>
+// Shape of a variant with TN 32-column tiles per wave and WPB waves per block:
+// k steps per activation buffer (one barrier each), LDS row stride in halves,
+// bytes of one buffer, weight columns per block, dynamic LDS per block, and
+// the activation staging passes (each thread stages 16 bytes of one row per
+// pass; a pass covers 8 WPB rows).
+template <int TN, int WPB>
 struct WideShape {
   static constexpr int SPB = TN == 4 ? 4 : 2;
   static constexpr int LD = SPB * kWK + 8;
   static constexpr size_t ABUF = (size_t)kBM * LD * 2;
-  static constexpr int BC = 4 * 32 * TN;
+  static constexpr int BC = WPB * 32 * TN;
   static constexpr size_t LDS = 2 * ABUF + 2 * BC * sizeof(float);
+  static constexpr int AP = kBM / (8 * WPB);
 };
 
 template <int FMT, int TN>
@@ -458,12 +461,13 @@ __device__ __forceinline__ int wide_koff(int s, int hh) {
   return FMT == FMT_FP8 ? 16 * hh + 8 * (s & 1) + 32 * (s >> 1) : 32 * hh + 8 * s;
 }
 
-template <int FMT, int TN, int STAGE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4 / TN, 4 / TN)))
+template <int FMT, int TN, int WPB, int STAGE>
+__global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(4 / TN, 4 / TN)))
 void gemm_prefill_wide(GemmArgs a) {
-  constexpr int SPB = WideShape<TN>::SPB, LD = WideShape<TN>::LD, BC = WideShape<TN>::BC;
+  using Shape = WideShape<TN, WPB>;
+  constexpr int SPB = Shape::SPB, LD = Shape::LD, BC = Shape::BC, AP = Shape::AP;
   constexpr int WC = 32 * TN, TH = TN / 2;  // columns per wave; gate (and up) tiles per wave
-  constexpr size_t ABUF = WideShape<TN>::ABUF;
+  constexpr size_t ABUF = Shape::ABUF;
   extern __shared__ __align__(16) unsigned char smem[];
   float *colinv = (float *)(smem + 2 * ABUF);  // [BC]: 2^-p of each weight column
   float *rowfs = colinv + BC;                  // [BC]: 2^p
@@ -527,11 +531,11 @@ void gemm_prefill_wide(GemmArgs a) {
     for (int tn = 0; tn < TN; ++tn) colinv[wave * WC + tn * 32 + j] = 1.f;
   }
 
-  // ---- activation staging: row (tid >> 3) + 32 p, 16-byte chunk tid & 7
-  const _Float16 *asrc[4];
+  // ---- activation staging: row (tid >> 3) + 8 WPB p, 16-byte chunk tid & 7
+  const _Float16 *asrc[AP];
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int rr = (tid >> 3) + 32 * p;
+  for (int p = 0; p < AP; ++p) {
+    const int rr = (tid >> 3) + 8 * WPB * p;
     const int r = rbeg + (rr < nrows ? rr : nrows - 1);
     // gate/up: the token's x16 row; down: the grouped h row
     asrc[p] = a.a_src + (STAGE == 0 ? (size_t)a.rowinfo[r].y : (size_t)r) * K + (tid & 7) * 8;
@@ -550,16 +554,16 @@ void gemm_prefill_wide(GemmArgs a) {
       ssrc[tn] = (const uint8_t *)a.scale + ((size_t)e * N + gr[tn]) * (K / 16) + 2 * hh;
   }
 
-  auto load_a = [&](u4 (&ar)[4], int ks) {
+  auto load_a = [&](u4 (&ar)[AP], int ks) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) ar[p] = *(const u4 *)(asrc[p] + ks * kWK);
+    for (int p = 0; p < AP; ++p) ar[p] = *(const u4 *)(asrc[p] + ks * kWK);
   };
-  auto write_a = [&](const u4 (&ar)[4], int buf, int sub) {
+  auto write_a = [&](const u4 (&ar)[AP], int buf, int sub) {
     _Float16 *As = (_Float16 *)(smem + buf * ABUF) + sub * kWK;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
+    for (int p = 0; p < AP; ++p) {
       // INT4: x16 is stored INT4-ordered, h in natural order
-      *(u4 *)(As + ((tid >> 3) + 32 * p) * LD + (tid & 7) * 8) = FMT == FMT_INT4 && STAGE == 1 ? perm_0415(ar[p]) : ar[p];
+      *(u4 *)(As + ((tid >> 3) + 8 * WPB * p) * LD + (tid & 7) * 8) = FMT == FMT_INT4 && STAGE == 1 ? perm_0415(ar[p]) : ar[p];
     }
   };
   auto load_w = [&](WideRegs<FMT, TN> &R, int ks) {
@@ -684,7 +688,7 @@ void gemm_prefill_wide(GemmArgs a) {
   // Weights for k step t + 1 load while step t multiplies.
   auto main_loop = [&](auto nv_c) {
     WideRegs<FMT, TN> R[2];
-    u4 ar[4], a0[SPB][4];
+    u4 ar[AP], a0[SPB][AP];
     // same load order as in the loop (activations of a later step, then
     // weights), so that the loop's first LDS write waits for the activation
     // loads alone
@@ -767,7 +771,7 @@ void gemm_prefill_wide(GemmArgs a) {
     constexpr int TL = WC + 8;     // LDS row stride, halves
     constexpr int LPR = WC / 8;    // lanes per row
     constexpr int RPI = 64 / LPR;  // rows per store instruction
-    static_assert(4 * 32 * TL * 2 <= (int)(2 * ABUF), "transpose buffers fit the activation buffers");
+    static_assert(WPB * 32 * TL * 2 <= (int)(2 * ABUF), "transpose buffers fit the activation buffers");
     _Float16 *tb = (_Float16 *)smem + wave * 32 * TL;
     float vmax = 0.f, vnan = 0.f;  // largest |value| before the FP16 clamp; NaN sentinel
     __syncthreads();               // every wave is done with the activation buffers
@@ -1015,22 +1019,23 @@ static hipError_t run_decode_ks(GemmArgs a, int slots, const GemmLaunch &s) {
   }
 }
 
-template <int FMT, int TN, int STAGE>
+template <int FMT, int TN, int WPB, int STAGE>
 static hipError_t run_prefill_wide(GemmArgs a, int64_t R, const GemmLaunch &s) {
-  constexpr int BC = WideShape<TN>::BC;
-  if (a.K % (WideShape<TN>::SPB * kWK) != 0) return hipErrorInvalidValue;  // K fills whole LDS buffers
+  using Shape = WideShape<TN, WPB>;
+  constexpr int BC = Shape::BC;
+  if (a.K % (Shape::SPB * kWK) != 0) return hipErrorInvalidValue;  // K fills whole LDS buffers
   a.tiles = STAGE == 0 ? (a.I + BC / 2 - 1) / (BC / 2) : (a.H + BC - 1) / BC;
   const int64_t max_mt = R / kBM + a.E;  // >= sum_e ceil(n_e / kBM)
   const int64_t grid = 8 * ((max_mt * a.tiles + 7) / 8);
-  constexpr size_t lds = WideShape<TN>::LDS;  // above the default limit
+  constexpr size_t lds = Shape::LDS;  // above the default limit
   static bool attr_set = false;
   if (!attr_set) {
-    (void)hipFuncSetAttribute((const void *)gemm_prefill_wide<FMT, TN, STAGE>,
+    (void)hipFuncSetAttribute((const void *)gemm_prefill_wide<FMT, TN, WPB, STAGE>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     attr_set = true;
   }
-  hipExtLaunchKernelGGL((gemm_prefill_wide<FMT, TN, STAGE>), dim3((unsigned)grid), dim3(256), (uint32_t)lds,
-                        s.stream, s.start, s.stop, 0u, a);
+  hipExtLaunchKernelGGL((gemm_prefill_wide<FMT, TN, WPB, STAGE>), dim3((unsigned)grid), dim3(64 * WPB),
+                        (uint32_t)lds, s.stream, s.start, s.stop, 0u, a);
   return hipGetLastError();
 }
 
@@ -1047,12 +1052,16 @@ static hipError_t dispatch(const LayerDims &L, const FwdPtrs &P, const Workspace
       default: return run_decode_ks<FMT_NVFP4, STAGE>(a, slots, s);
     }
   }
-  // two 32-column tiles per wave at two blocks per CU (against four tiles at
-  // one block per CU: equal on FP8 T=4096 gate/up, faster on NVFP4 and INT4)
+  // Two 32-column tiles per wave, two waves per SIMD.  gate/up: 8 waves per
+  // block, so each staged activation tile feeds 512 weight columns (FP8
+  // T=4096 gate/up 260 -> 246 us, NVFP4 Zipf 834 -> 806 us against 4 waves);
+  // down (K = I = 768): 4 waves per block, two blocks per CU, whose prologue
+  // and epilogue overlap each other (8 waves measured slower there).
+  constexpr int WPB = STAGE == 0 ? 8 : 4;
   switch (L.fmt) {
-    case FMT_INT4: return run_prefill_wide<FMT_INT4, 2, STAGE>(a, R, s);
-    case FMT_FP8: return run_prefill_wide<FMT_FP8, 2, STAGE>(a, R, s);
-    default: return run_prefill_wide<FMT_NVFP4, 2, STAGE>(a, R, s);
+    case FMT_INT4: return run_prefill_wide<FMT_INT4, 2, WPB, STAGE>(a, R, s);
+    case FMT_FP8: return run_prefill_wide<FMT_FP8, 2, WPB, STAGE>(a, R, s);
+    default: return run_prefill_wide<FMT_NVFP4, 2, WPB, STAGE>(a, R, s);
   }
 }
 
