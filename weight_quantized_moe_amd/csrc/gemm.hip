@@ -823,8 +823,13 @@ void gemm_prefill_wide(GemmArgs a) {
 // ===========================================================================
 // Combine: out[t] = bf16(sum_j partial[t*k + j] (+ residual[t])), the FP16
 // partials widened to FP32 and added in order j = 0..k-1 so repeated runs are
-// bit-identical.
+// bit-identical.  kStream: non-temporal partial loads, for a partial buffer
+// larger than the 256 MiB last-level cache (NVFP4 Zipf T=16384, 537 MB:
+// 107 -> 88 us); a smaller one is still partly cached from the down GEMM's
+// writes, and plain loads read it faster (FP8 T=4096, 134 MB: 23.5 against
+// 24.7 us).
 // ===========================================================================
+template <bool kStream>
 __global__ __launch_bounds__(256) void combine_kernel(const _Float16 *__restrict__ partial,
                                                       const uint16_t *__restrict__ residual,
                                                       uint16_t *__restrict__ out, int T, int H,
@@ -841,7 +846,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const _Float16 *__restrict
     h8 x[8];
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj)
-      if (j0 + jj < k) x[jj] = as_h8(*(const u4 *)(partial + ((size_t)t * k + j0 + jj) * H + c));
+      if (j0 + jj < k) {
+        const u4 *src = (const u4 *)(partial + ((size_t)t * k + j0 + jj) * H + c);
+        x[jj] = as_h8(kStream ? __builtin_nontemporal_load(src) : *src);
+      }
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj)
       if (j0 + jj < k) {
@@ -1077,8 +1085,13 @@ hipError_t launch_down(const LayerDims &L, const FwdPtrs &P, const Workspace &W,
 
 hipError_t launch_combine(const LayerDims &L, const FwdPtrs &P, const Workspace &W, hipStream_t s) {
   const size_t items = (size_t)P.T * (L.H / 8);
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s,
-                     (const _Float16 *)(P.ws + W.partial), P.residual, P.out, P.T, L.H, L.k);
+  const bool stream = (size_t)P.T * L.k * L.H * sizeof(_Float16) > ((size_t)256 << 20);
+  const dim3 grid((unsigned)((items + 255) / 256)), block(256);
+  const _Float16 *partial = (const _Float16 *)(P.ws + W.partial);
+  if (stream)
+    hipLaunchKernelGGL(combine_kernel<true>, grid, block, 0, s, partial, P.residual, P.out, P.T, L.H, L.k);
+  else
+    hipLaunchKernelGGL(combine_kernel<false>, grid, block, 0, s, partial, P.residual, P.out, P.T, L.H, L.k);
   return hipGetLastError();
 }
 
