@@ -50,6 +50,23 @@ def silu(z: np.ndarray) -> np.ndarray:
     return out
 
 
+def router_logits(x_bf16_bits: np.ndarray, w_bf16_bits: np.ndarray) -> np.ndarray:
+    """Router logits [T, E] of the gate that stays in BF16 ("clef-omni-fp8" card,
+    section "What was quantized"; "clef-omni-NVFP4" card, section "How it was
+    made", where the router mlp.gate is copied unchanged).
+
+    Read as a linear layer without bias: logits[t, e] = sum_h x[t, h] w[e, h],
+    with ``x`` the BF16 hidden rows [T, H] and ``w`` the gate's BF16 weight
+    [E, H] (bit patterns).  BF16 values widen exactly to float64; each product
+    is exact there and the sum rounds in float64.
+    """
+    x = bf16_bits_to_f64(x_bf16_bits)
+    w = bf16_bits_to_f64(w_bf16_bits)
+    if x.ndim != 2 or w.ndim != 2 or x.shape[1] != w.shape[1]:
+        raise ValueError("need x [T, H] and w [E, H]")
+    return x @ w.T
+
+
 def route(logits: np.ndarray, k: int):
     """Top-k expert selection and routing weights for each token.
 

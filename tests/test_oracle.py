@@ -212,3 +212,50 @@ def test_workload_logit_skew():
     ids, _ = moe.route(lg, 8)
     counts = np.bincount(ids.ravel(), minlength=128)
     assert counts.max() > 2 * counts.mean()
+
+
+# ------------------------------------------------------------ router logits
+
+def _bf16_bits(v):
+    """float values that are exact in BF16 -> their bit patterns."""
+    a = np.asarray(v, dtype=np.float32)
+    b = a.view(np.uint32)
+    assert np.all((b & 0xFFFF) == 0), "value not exact in BF16"
+    return (b >> 16).astype(np.uint16)
+
+
+def test_router_logits_hand_example():
+    """x [[1, 2], [3, 4]], w [[1, 0], [1, 1], [0.5, -1]]: logits by hand."""
+    x = _bf16_bits([[1.0, 2.0], [3.0, 4.0]])
+    w = _bf16_bits([[1.0, 0.0], [1.0, 1.0], [0.5, -1.0]])
+    got = moe.router_logits(x, w)
+    assert np.array_equal(got, np.array([[1.0, 3.0, -1.5], [3.0, 7.0, -2.5]]))
+
+
+def test_router_logits_one_hot_rows_select_columns():
+    """w[e] = unit vector at column c(e): logits[:, e] is x[:, c(e)] exactly
+    (a transposed operand or a wrong index would pick other columns)."""
+    rng = np.random.default_rng(3)
+    T, H, E = 5, 16, 7
+    x = synth.to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    cols = rng.permutation(H)[:E]
+    w = np.zeros((E, H), dtype=np.float32)
+    w[np.arange(E), cols] = 1.0
+    got = moe.router_logits(x, _bf16_bits(w))
+    assert np.array_equal(got, moe.bf16_bits_to_f64(x)[:, cols])
+
+
+def test_router_logits_brute_force_tiny():
+    rng = np.random.default_rng(4)
+    T, H, E = 3, 8, 4
+    x = synth.to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    w = synth.to_bf16_bits(rng.standard_normal((E, H)).astype(np.float32))
+    xf, wf = moe.bf16_bits_to_f64(x), moe.bf16_bits_to_f64(w)
+    ref = np.zeros((T, E))
+    for t in range(T):
+        for e in range(E):
+            acc = 0.0
+            for h in range(H):
+                acc += xf[t, h] * wf[e, h]
+            ref[t, e] = acc
+    np.testing.assert_allclose(moe.router_logits(x, w), ref, rtol=1e-15, atol=1e-15)
