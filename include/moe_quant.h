@@ -208,6 +208,26 @@ mq_status moe_quant_check(const mq_layer *L, const void *workspace, struct ihipS
 mq_status moe_quant_dequantize(const mq_layer *L, int32_t which, int32_t expert, float *out,
                                struct ihipStream_t *stream);
 
+/*
+ * Router logits of the gate that stays in BF16 ("clef-omni-fp8" card, section
+ * "What was quantized"; "clef-omni-NVFP4" card, section "How it was made"),
+ * read as a linear layer without bias:
+ *   logits_f32[t, e] = sum_h hidden_bf16[t, h] * router_bf16[e, h]
+ *   hidden_bf16  [T, H] BF16 bits, row-major, 16-byte aligned
+ *   router_bf16  [E, H] BF16 bits, row-major (the gate's weight), 16-byte aligned
+ *   logits_f32   [T, E] float32, row-major, 16-byte aligned; written here, and
+ *                ready for moe_quant_forward with logits_dtype MQ_F32
+ * All three live in device memory owned by the caller; nothing is kept after
+ * the call.  Products are exact in FP32 and summed in FP32 by the matrix
+ * units (an order of their own).  hidden a positive multiple of 64 (at most
+ * 65536), 1 <= num_experts <= 65536, 0 <= num_tokens <= 2^22; num_tokens == 0
+ * returns MQ_OK without enqueuing anything.  No layer handle is needed.
+ * Errors: MQ_E_SHAPE, MQ_E_NULL, MQ_E_ALIGN, MQ_E_HIP (launch failed).
+ */
+mq_status moe_quant_router_logits(const uint16_t *hidden_bf16, const uint16_t *router_bf16,
+                                  int64_t num_tokens, int32_t hidden, int32_t num_experts,
+                                  float *logits_f32, struct ihipStream_t *stream);
+
 void moe_quant_destroy(mq_layer *L);
 
 /* Static strings; never NULL. */

@@ -151,3 +151,18 @@ def test_dequantize_rejects(lib):
     assert lib.moe_quant_dequantize(h, 0, 0, None, None) == MQ_E_NULL
     assert lib.moe_quant_dequantize(h, 0, 0, 0x1004, None) == MQ_E_ALIGN
     lib.moe_quant_destroy(h)
+
+
+def test_router_logits_rejects_before_any_launch(lib):
+    """Shape, NULL and alignment errors return before anything is enqueued."""
+    f = lib.moe_quant_router_logits
+    P = 0x100000
+    assert f(P, P + 0x10000, 0, 2048, 128, P + 0x20000, None) == MQ_OK     # T = 0: nothing to do
+    assert f(None, None, 0, 2048, 128, None, None) == MQ_OK
+    assert f(P, P + 0x10000, -1, 2048, 128, P + 0x20000, None) == MQ_E_SHAPE
+    assert f(P, P + 0x10000, 4, 2000, 128, P + 0x20000, None) == MQ_E_SHAPE  # H % 64
+    assert f(P, P + 0x10000, 4, 2048, 0, P + 0x20000, None) == MQ_E_SHAPE
+    assert f(None, P + 0x10000, 4, 2048, 128, P + 0x20000, None) == MQ_E_NULL
+    assert f(P, P + 0x10000, 4, 2048, 128, None, None) == MQ_E_NULL
+    assert f(P + 2, P + 0x10000, 4, 2048, 128, P + 0x20000, None) == MQ_E_ALIGN
+    assert f(P, P + 0x10000, 4, 2048, 128, P + 0x20004, None) == MQ_E_ALIGN

@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     MoeQuantError,
     library_path,
     load_library,
+    router_logits,
 )
 
-__all__ = ["FORMATS", "Layer", "MoeQuantError", "library_path", "load_library"]
+__all__ = ["FORMATS", "Layer", "MoeQuantError", "library_path", "load_library", "router_logits"]

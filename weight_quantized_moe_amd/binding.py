@@ -23,6 +23,7 @@ EXPORTED = (
     "moe_quant_forward",
     "moe_quant_check",
     "moe_quant_dequantize",
+    "moe_quant_router_logits",
     "moe_quant_destroy",
     "moe_quant_status_string",
     "moe_quant_last_error",
@@ -93,6 +94,8 @@ def load_library():
     lib.moe_quant_check.restype = i32
     lib.moe_quant_dequantize.argtypes = [vp, i32, i32, vp, vp]
     lib.moe_quant_dequantize.restype = i32
+    lib.moe_quant_router_logits.argtypes = [vp, vp, i64, i32, i32, vp, vp]
+    lib.moe_quant_router_logits.restype = i32
     lib.moe_quant_destroy.argtypes = [vp]
     lib.moe_quant_destroy.restype = None
     lib.moe_quant_status_string.argtypes = [i32]
@@ -121,6 +124,22 @@ def _stream(stream) -> Optional[int]:
     if stream is None:
         stream = torch.cuda.current_stream()
     return stream.cuda_stream
+
+
+def router_logits(hidden, router_w, out=None, stream=None):
+    """Router logits float32 [T, E] = hidden [T, H] . router_w [E, H]^T, both
+    bfloat16 on the GPU (moe_quant_router_logits)."""
+    import torch
+    lib = load_library()
+    t, h = hidden.shape
+    e = router_w.shape[0]
+    if router_w.shape[1] != h or hidden.dtype != torch.bfloat16 or router_w.dtype != torch.bfloat16:
+        raise ValueError("need bfloat16 hidden [T, H] and router weight [E, H]")
+    if out is None:
+        out = torch.empty((t, e), dtype=torch.float32, device=hidden.device)
+    _check(lib, lib.moe_quant_router_logits(_ptr(hidden), _ptr(router_w), t, h, e, _ptr(out),
+                                            _stream(stream)))
+    return out
 
 
 class Layer:

@@ -84,6 +84,8 @@ hipError_t launch_down(const LayerDims &L, const FwdPtrs &P, const Workspace &W,
                        const GemmLaunch &s);
 hipError_t launch_combine(const LayerDims &L, const FwdPtrs &P, const Workspace &W, hipStream_t s);
 hipError_t launch_dequantize(const LayerDims &L, int which, int expert, float *out, hipStream_t s);
+hipError_t launch_router_logits(const uint16_t *x, const uint16_t *w, float *out, int64_t T, int H,
+                                int E, hipStream_t s);
 
 // Rows per expert at or below which the decode (weight-streaming) GEMMs run.
 bool use_decode_path(int64_t T, int E, int k, int H, int I);

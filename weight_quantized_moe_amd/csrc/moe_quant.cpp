@@ -264,4 +264,29 @@ mq_status moe_quant_dequantize(const mq_layer *L, int32_t which, int32_t expert,
   return MQ_OK;
 }
 
+mq_status moe_quant_router_logits(const uint16_t *hidden_bf16, const uint16_t *router_bf16,
+                                  int64_t num_tokens, int32_t hidden, int32_t num_experts,
+                                  float *logits_f32, struct ihipStream_t *stream) {
+  if (num_tokens < 0 || num_tokens > kMaxTokens)
+    return fail(MQ_E_SHAPE, "router_logits: num_tokens %lld outside [0, %lld]", (long long)num_tokens,
+                (long long)kMaxTokens);
+  if (hidden <= 0 || hidden % 64 != 0 || hidden > 65536)
+    return fail(MQ_E_SHAPE, "router_logits: hidden %d must be a positive multiple of 64, at most 65536",
+                hidden);
+  if (num_experts <= 0 || num_experts > 65536)
+    return fail(MQ_E_SHAPE, "router_logits: num_experts %d outside [1, 65536]", num_experts);
+  if (num_tokens == 0) {
+    g_err[0] = 0;
+    return MQ_OK;
+  }
+  if (!hidden_bf16 || !router_bf16 || !logits_f32) return fail(MQ_E_NULL, "router_logits: NULL argument");
+  if (!aligned(hidden_bf16, 16) || !aligned(router_bf16, 16) || !aligned(logits_f32, 16))
+    return fail(MQ_E_ALIGN, "router_logits: pointers must be 16-byte aligned");
+  hipError_t e = mq::launch_router_logits(hidden_bf16, router_bf16, logits_f32, num_tokens, hidden,
+                                          num_experts, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(MQ_E_HIP, "router_logits: %s", hipGetErrorString(e));
+  g_err[0] = 0;
+  return MQ_OK;
+}
+
 }  // extern "C"
