@@ -118,6 +118,38 @@ def vendor_bmm(dev, steps):
     return out
 
 
+def router_bench(dev, steps):
+    """The router logits kernel alone (moe_quant_router_logits) at the layer's
+    shape, H 2048 and E 128, for the decode and prefill batch sizes.  It is
+    bound by HBM: x [T, H] and the gate [E, H] in BF16, logits [T, E] in FP32,
+    2 T H E FLOP on the BF16 matrix units."""
+    import torch
+    from weight_quantized_moe_amd import router_logits
+    H, E = 2048, 128
+    out = []
+    gen = torch.Generator(device=dev).manual_seed(7)
+    w = (torch.randn(E, H, device=dev, generator=gen) * 0.02).to(torch.bfloat16)
+    for T in (64, 4096, 16384):
+        x = torch.randn(T, H, device=dev, generator=gen).to(torch.bfloat16)
+        lg = torch.empty(T, E, device=dev, dtype=torch.float32)
+        for _ in range(5):
+            router_logits(x, w, out=lg)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            router_logits(x, w, out=lg)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        nbytes = T * H * 2 + E * H * 2 + T * E * 4
+        gbs = nbytes / us / 1e3
+        out.append({"tokens": T, "us": round(us, 2), "bytes": nbytes, "GB_s": round(gbs, 1),
+                    "frac_of_8TB_s": round(gbs / 8000.0, 4),
+                    "TFLOP_s": round(2.0 * T * H * E / us / 1e6, 1)})
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -127,6 +159,8 @@ def main():
     ap.add_argument("--tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true", help="also time every batch size of the workload")
+    ap.add_argument("--router", action="store_true",
+                    help="only time the router logits kernel (moe_quant_router_logits) at H 2048, E 128")
     ap.add_argument("--vendor-bmm", action="store_true",
                     help="only time torch.bmm (hipBLASLt) FP16 at the prefill expert-GEMM shapes, for reference")
     args = ap.parse_args()
@@ -140,6 +174,11 @@ def main():
     import torch
     from weight_quantized_moe_amd import Layer, load_library, synth
 
+    if args.router:
+        load_library()
+        print(json.dumps({"kernel": "router logits (moe_quant_router_logits), BF16 MFMA, FP32 out",
+                          "results": router_bench(torch.device("cuda:0"), max(args.steps, 20))}))
+        return
     if args.vendor_bmm:
         print(json.dumps({"reference": "torch.bmm FP16 (hipBLASLt), not this library",
                           "results": vendor_bmm(torch.device("cuda:0"), max(args.steps, 20))}))
