@@ -2,18 +2,17 @@
 // "What was quantized"; "clef-omni-NVFP4" card, section "How it was made"),
 // read as a linear layer without bias: logits[t, e] = sum_h x[t, h] w[e, h].
 //
-// BF16 MFMA 32x32x16 with FP32 accumulation: every product is exact in FP32
+// BF16 MFMA 16x16x32 with FP32 accumulation: every product is exact in FP32
 // and only the FP32 sums round.  A block of 8 waves covers 32 TG tokens x
 // 32 EG experts; each (token group, expert group) 32x32 tile is split over KS
 // = 8 / (TG EG) waves along H, and the KS partial tiles are added through LDS
 // in wave order (the same order every run).  Below 1024 tokens TG = EG = 1,
 // KS = 8, so a decode batch still spreads over many waves; above, TG = 1,
-// EG = 2, KS = 4.  In a wave, lane j = lane % 32 owns expert row
-// e0 + j (the MFMA A rows) and token row t0 + j (the B columns).  Per 64-wide
-// k chunk c a lane loads 32 values (64 bytes) of each row, k = c + 32 h +
-// [0, 32) with h = lane / 32; MFMA s of the chunk takes k = c + 32 h + 8 s +
-// [0, 8) on both operands (any k order works when both operands follow it).
-// Rows past T or E are clamped on load and never stored.
+// EG = 2, KS = 4.  A wave's 32x32 tile is 2 x 2 MFMA tiles of 16 rows: lane l
+// feeds row l % 16 of a tile with k = 8 (l / 16) + [0, 8) of each 32-wide
+// step, so the four lanes of a row read 64 contiguous bytes per load (the
+// gate rows are the MFMA A rows, the token rows the B columns).  Rows past T
+// or E are clamped on load and never stored.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -34,70 +33,95 @@ __global__ __launch_bounds__(64 * kRouterWaves) void router_logits_kernel(
   static_assert(KS * TG * EG == kRouterWaves, "8 waves per block");
   __shared__ f4 red[KS > 1 ? kRouterWaves : 1][4][64];  // partial tiles (16 floats per lane)
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int j = lane & 31, hh = lane >> 5;
   const int ks = wave % KS, tile = wave / KS;  // k slice; (token group, expert group) tile
   const int t0 = (blockIdx.x * TG + tile / EG) * 32, e0 = (blockIdx.y * EG + tile % EG) * 32;
   const bool live = t0 < T && e0 < E;  // a tile past both ends still takes the barrier
-  const uint16_t *xp = x + (size_t)min(t0 + j, T - 1) * H + 32 * hh;
-  const uint16_t *wp = w + (size_t)min(e0 + j, E - 1) * H + 32 * hh;
+  // MFMA 16x16x32: lane l feeds row l % 16 of a 16-row tile with k slice
+  // 8 (l / 16) + [0, 8) of each 32-wide step, so four lanes read 64 contiguous
+  // bytes of one row; the wave's 32x32 tile is 2 x 2 MFMA tiles
+  const int r16 = lane & 15, q16 = lane >> 4;
+  const uint16_t *xp[2], *wp[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    xp[i] = x + (size_t)min(t0 + 16 * i + r16, T - 1) * H + 8 * q16;
+    wp[i] = w + (size_t)min(e0 + 16 * i + r16, E - 1) * H + 8 * q16;
+  }
   const int nchunk = H / 64;
   const int cb = live ? (ks * nchunk) / KS : 0, ce = live ? ((ks + 1) * nchunk) / KS : 0;
-  f16v acc;
+  f4 acc[2][2];  // [expert tile][token tile]
 #pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 2
   for (int c = cb * 64; c < ce * 64; c += 64) {
-    u4 xa[4], wa[4];
+    u4 xa[2][2], wa[2][2];  // [tile][32-wide step]
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      xa[q] = *(const u4 *)(xp + c + 8 * q);
-      wa[q] = *(const u4 *)(wp + c + 8 * q);
-    }
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf8, wa[s]),
-                                                     __builtin_bit_cast(bf8, xa[s]), acc, 0, 0, 0);
+      for (int s2 = 0; s2 < 2; ++s2) {
+        xa[i][s2] = *(const u4 *)(xp[i] + c + 32 * s2);
+        wa[i][s2] = *(const u4 *)(wp[i] + c + 32 * s2);
+      }
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, wa[a][s2]),
+                                                              __builtin_bit_cast(bf8, xa[b][s2]),
+                                                              acc[a][b], 0, 0, 0);
   }
   if constexpr (KS > 1) {
     if (ks > 0) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        red[wave][g][lane] = f4{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) red[wave][2 * a + b][lane] = acc[a][b];
     }
     __syncthreads();
     if (ks != 0) return;
 #pragma unroll
     for (int p = 1; p < KS; ++p)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f4 v = red[wave + p][g][lane];
+      for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[4 * g + i] += v[i];
-      }
+        for (int b = 0; b < 2; ++b) {
+          const f4 v = red[wave + p][2 * a + b][lane];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[a][b][i] += v[i];
+        }
   }
-  // lane holds token t0 + j and, in register v, expert e0 + 8 (v / 4) + 4 h + v % 4
-  const int t = t0 + j;
-  if (!live || t >= T) return;
-  float *orow = out + (size_t)t * E;
+  // MFMA tile (a, b): lane holds token t0 + 16 b + l % 16 and experts
+  // e0 + 16 a + 4 (l / 16) + [0, 4)
+  if (!live) return;
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int e = e0 + 8 * g + 4 * hh;
-    if ((E & 3) == 0 && e + 3 < E) {
-      *(f4 *)(orow + e) = f4{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
-    } else {
+  for (int b = 0; b < 2; ++b) {
+    const int t = t0 + 16 * b + r16;
+    if (t >= T) continue;
+    float *orow = out + (size_t)t * E;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (e + i < E) orow[e + i] = acc[4 * g + i];
+    for (int a = 0; a < 2; ++a) {
+      const int e = e0 + 16 * a + 4 * q16;
+      if ((E & 3) == 0 && e + 3 < E) {
+        *(f4 *)(orow + e) = acc[a][b];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (e + i < E) orow[e + i] = acc[a][b][i];
+      }
     }
   }
 }
 
 hipError_t launch_router_logits(const uint16_t *x, const uint16_t *w, float *out, int64_t T, int H,
                                 int E, hipStream_t s) {
-  // Measured at H 2048, E 128 (us for T = 64 / 4096 / 16384): 32x32 tiles
-  // with 8 k slices 9.2 / 18.1 / 68.0; 32x64 with 4 slices - / 17.3 / 65.1;
-  // 32x128 and 64x64 with 2 slices - / 30.9 / 61.4 and - / 30.3 / 61.9;
-  // 64x128 unsplit 57.1 / 57.8 / 60.3.
+  // Measured at H 2048, E 128 with the 32x32x16 MFMA (us for T = 64 / 4096 /
+  // 16384): 32x32 tiles with 8 k slices 9.2 / 18.1 / 68.0; 32x64 with 4
+  // slices - / 17.3 / 65.1; 32x128 and 64x64 with 2 slices - / 30.9 / 61.4 and
+  // - / 30.3 / 61.9; 64x128 unsplit 57.1 / 57.8 / 60.3.  The 16x16x32 MFMA
+  // (64 contiguous bytes per row per load, against 32): 9.2 / 17.1 / 58.9.
   if (T < 1024) {
     const dim3 grid((unsigned)((T + 31) / 32), (unsigned)((E + 31) / 32));
     hipLaunchKernelGGL((router_logits_kernel<1, 1>), grid, dim3(64 * kRouterWaves), 0, s, x, w, out,
