@@ -505,7 +505,7 @@ void gemm_prefill_wide(GemmArgs a) {
   }
 
   // ---- power of two of each column (from its largest scale): lane half hh
-  // takes tiles 2 hh and 2 hh + 1, shared through LDS
+  // takes tiles TN/2 hh + [0, TN/2), shared through LDS
   if (FMT != FMT_NVFP4) {
 #pragma unroll
     for (int q = 0; q < TH; ++q) {
@@ -540,7 +540,7 @@ void gemm_prefill_wide(GemmArgs a) {
     // gate/up: the token's x16 row; down: the grouped h row
     asrc[p] = a.a_src + (STAGE == 0 ? (size_t)a.rowinfo[r].y : (size_t)r) * K + (tid & 7) * 8;
   }
-  // ---- weight and scale streams of the lane's four columns
+  // ---- weight and scale streams of the lane's TN columns
   const uint8_t *wsrc[TN];
   const uint8_t *ssrc[TN];
 #pragma unroll
@@ -630,8 +630,8 @@ void gemm_prefill_wide(GemmArgs a) {
       }
       // activation fragments of sub-step s + 1 are read while sub-step s
       // multiplies; each sub-step is its own scheduling region in which one
-      // MFMA alternates with a share of the unpack (one wave per SIMD has no
-      // other wave to fill the matrix unit's idle cycles)
+      // MFMA alternates with a share of the unpack (at one or two waves per
+      // SIMD few other waves are there to fill the matrix unit's idle cycles)
       constexpr int kValuPerTile = FMT == FMT_FP8 ? 8 : FMT == FMT_INT4 ? 13 : 10;
       constexpr int VP = (kValuPerTile + NV - 1) / NV;
       h8 afc[NV], afn[NV];
