@@ -1,6 +1,7 @@
 """Benchmark of the quantized MoE expert layer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode_int4] [--tokens T]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload nvfp4_zipf] [--tokens T]
+                    [--no-cpu-baseline] [--no-regimes] [--no-stack]
 
 A step is one full forward of the expert layer (routing, grouping, fused
 dequant gate/up GEMM + SwiGLU, down GEMM, combine) over one batch of synthetic
@@ -9,10 +10,22 @@ through several distinct layers' weights (>= 1.5 GiB in total, more than the
 256 MB last-level cache), so every step streams its expert weights from HBM as
 a real model's consecutive layers would.
 
-Prints one JSON line: whole-step tokens/s, the roofline position of the
-dominant kernel (timed live with HIP events on the stream it runs on, which
-the library has the runtime take at the kernel's own start and end), and the
-CPU oracle timed on a bounded sample of the same workload.
+The headline line is the largest batch: NVFP4 weights, 16384 tokens with
+Zipf-skewed routing (the prefill regime, bound by the matrix units).  Beside it:
+
+* ``regimes``: the decode layer (INT4, 1 / 8 / 64 tokens, bound by HBM) and
+  the FP8 prefill layer (4096 tokens), each with the median, p10 and p90 of
+  per-step times with the weights cycled through the sets, with one set
+  repeated (warm caches) and after a 1 GiB flush (cold caches), plus the
+  decode batches replayed from a captured HIP graph;
+* ``stack48``: the 48-layer stack (24 FP8 + 24 INT4 layers chained with
+  residual adds) at 64 and 2048 tokens, eager and graph-captured;
+* ``cpu_baseline``: the float64 oracle on a bounded sample of the headline
+  batch, on the host's cores.
+
+``roofline`` rates the dominant kernel of each line, timed live with HIP events
+that the runtime takes at the kernel's own start and end on the stream it runs
+on (``hipExtLaunchKernel``).
 """
 from __future__ import annotations
 
@@ -31,8 +44,9 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 PEAK_FP16_TFLOPS = 2500.0    # MI355X dense FP16/BF16 MFMA
 STAGES = ("route", "permute", "gate_up", "down", "combine")
-EVERY = 8  # bracket the dominant kernel with events in one step of every EVERY
-KERNEL_SRC = os.path.join(ROOT, "weight_quantized_moe_amd", "csrc", "gemm.hip")
+EVERY = 4  # bracket the dominant kernel with events in one step of every EVERY
+CSRC = os.path.join(ROOT, "weight_quantized_moe_amd", "csrc")
+METRIC = "MoE layer tokens/s + % roofline (HBM GB/s decode, MFMA util prefill)"
 
 
 def packed_bytes(fmt, n, k):
@@ -45,8 +59,8 @@ def packed_bytes(fmt, n, k):
 
 def source_hash() -> str:
     h = hashlib.sha256()
-    for name in sorted(os.listdir(os.path.dirname(KERNEL_SRC))):
-        with open(os.path.join(os.path.dirname(KERNEL_SRC), name), "rb") as f:
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
@@ -65,29 +79,430 @@ def counter_traffic(kernel_tag: str):
     return float(b.group(1))
 
 
-def cpu_baseline(layer_np, logits, x, budget_s=12.0):
-    """The oracle as it stands, on whole batches of the same workload, repeated
-    until ~budget_s of CPU work."""
+def kernel_work(fmt, E, H, I, k, T, touched):
+    """Algorithmic bytes and flops.  Bytes: the packed weights + scales of the
+    touched experts, the hidden rows read once (gate/up) and the output written
+    once (down); the intermediate h and the per-slot partials are the
+    implementation's own traffic and are not counted.  Flops: 6 H I per routed
+    row (4 H I gate/up, 2 H I down); no padding rows, no unpack, no SwiGLU."""
+    R = T * k
+    w13_b, w2_b = packed_bytes(fmt, 2 * I, H), packed_bytes(fmt, H, I)
+    return {
+        "bytes": {"gate_up": touched * w13_b + T * H * 2, "down": touched * w2_b + T * H * 2},
+        "flops": {"gate_up": 4 * H * I * R, "down": 2 * H * I * R},
+        "path_bytes": touched * (w13_b + w2_b) + 2 * T * H * 2 + T * E * 4,
+        "path_flops": 6 * H * I * R,
+    }
+
+
+def pct(vals, q):
+    s = sorted(vals)
+    return s[min(len(s) - 1, max(0, int(round(q * (len(s) - 1)))))]
+
+
+def new_events(n):
+    import torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for e in evs:          # torch creates the HIP event on first record
+        e.record()
+    return evs
+
+
+class LayerBench:
+    """One workload's layer: several weight sets (cycled so they stream from
+    HBM), its synthetic batch, workspace and output."""
+
+    def __init__(self, wl, T, dev, min_bytes=1.5 * 2 ** 30, seed0=1000, share=None):
+        import numpy as np
+        import torch
+        from weight_quantized_moe_amd import Layer, synth
+        self.wl, self.T, self.dev = wl, T, dev
+        E, H, I, k, fmt = wl.experts, wl.hidden, wl.inter, wl.top_k, wl.fmt
+        layer_bytes = E * (packed_bytes(fmt, 2 * I, H) + packed_bytes(fmt, H, I))
+        self.n_sets = max(2, math.ceil(min_bytes / layer_bytes))
+        self.layers, self.first_np = [], None
+        if share is not None:            # the same weight sets at another batch size
+            self.n_sets, self.layers, self.first_np = share.n_sets, share.layers, share.first_np
+        for li in range(len(self.layers), self.n_sets):
+            t13 = synth.random_packed_torch(fmt, E, 2 * I, H, seed0 + 2 * li, dev)
+            t2 = synth.random_packed_torch(fmt, E, H, I, seed0 + 1 + 2 * li, dev)
+            if li == 0:
+                self.first_np = tuple(None if a is None else a.cpu().numpy() for a in (*t13, *t2))
+            self.layers.append(Layer(fmt, t13[0], t13[1], t2[0], t2[1], k,
+                                     w13_gscale=t13[2], w2_gscale=t2[2]))
+        self.logits_np = synth.router_logits(wl.wid, 0, T, E, wl.logits)
+        self.x_np = synth.hidden_bf16(wl.wid, 0, T, H)
+        self.logits = torch.from_numpy(self.logits_np).to(dev)
+        self.x = torch.from_numpy(self.x_np.view(np.int16)).to(dev).view(torch.bfloat16)
+        self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        self.ws = self.layers[0].workspace(T, dev)
+        offs = torch.empty(E + 1, dtype=torch.int32, device=dev)
+        self.layers[0].forward(self.logits, self.x, out=self.out, workspace=self.ws,
+                               probe={"expert_offsets": offs})
+        torch.cuda.synchronize()
+        self.touched = int((torch.diff(offs) > 0).sum().item())
+        self.work = kernel_work(fmt, E, H, I, k, T, self.touched)
+
+    def fwd(self, i, events=None):
+        self.layers[i % self.n_sets].forward(self.logits, self.x, out=self.out, workspace=self.ws,
+                                             events=events)
+
+    def stages(self, n):
+        """Average per-stage time (ms) over n steps (its own run: ten event
+        records per step)."""
+        import torch
+        bev = [new_events(2 * len(STAGES)) for _ in range(n)]
+        for i in range(n):
+            self.fwd(i, bev[i])
+        torch.cuda.synchronize()
+        return {s: sum(e[2 * j].elapsed_time(e[2 * j + 1]) for e in bev) / n
+                for j, s in enumerate(STAGES)}
+
+    def timed(self, steps, warmup, dom):
+        """Exactly `steps` steps between two events (sets cycled); the dominant
+        kernel bracketed by runtime-taken kernel events in every EVERY-th step."""
+        import torch
+        for i in range(warmup):
+            self.fwd(i)
+        jd = STAGES.index(dom)
+        sampled = list(range(0, steps, EVERY))
+        dev_ev = {i: new_events(2) for i in sampled}
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record()
+        for i in range(steps):
+            ev = None
+            if i in dev_ev:
+                ev = [None] * (2 * len(STAGES))
+                ev[2 * jd], ev[2 * jd + 1] = dev_ev[i]
+            self.fwd(i, ev)
+        end.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        kern = [a.elapsed_time(b) for a, b in dev_ev.values()]
+        return dict(ms=start.elapsed_time(end) / steps, wall_ms=wall * 1e3 / steps,
+                    dom_ms=sum(kern) / len(kern), dom_med_ms=pct(kern, 0.5))
+
+    def per_step(self, iters, mode, flush=None):
+        """Per-step times (us), each step between its own event pair: `cycled`
+        (weight sets in turn), `warm` (set 0 every time) or `cold` (set 0 after
+        an untimed write of a 1 GiB buffer, which evicts L2 and the MALL)."""
+        import torch
+        evs = [new_events(2) for _ in range(iters)]
+        torch.cuda.synchronize()
+        for i in range(iters):
+            if mode == "cold":
+                flush.fill_(i & 0xFF)
+            evs[i][0].record()
+            self.fwd(i if mode == "cycled" else 0)
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) * 1e3 for a, b in evs]
+
+    def graph_us(self, reps):
+        """Per-step time (us) of the steps replayed from one captured HIP graph
+        that holds one forward per weight set, in turn."""
+        import torch
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for i in range(self.n_sets):
+                self.fwd(i)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(self.n_sets):
+                self.fwd(i)
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = new_events(2)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (reps * self.n_sets)
+
+
+def roofline(lb, dom, dom_ms, decode):
+    wl = lb.wl
+    secs = dom_ms * 1e-3
+    if decode:
+        algo = lb.work["bytes"][dom]
+        achieved = algo / secs / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    else:
+        algo = lb.work["flops"][dom]
+        achieved = algo / secs / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4)}
+    roof["traffic"] = counter_traffic(f"{dom}_{wl.fmt}_T{lb.T}")
+    roof["kernel"] = dom
+    roof["kernel_us"] = round(dom_ms * 1e3, 2)
+    roof["algorithmic_bytes" if decode else "algorithmic_flops"] = algo
+    return roof
+
+
+def is_decode(wl, T):
+    return T * wl.top_k <= 16 * wl.experts
+
+
+def regime_line(lb, iters, flush, graph):
+    """Distribution of per-step times for one workload and batch size."""
+    stage_ms = lb.stages(min(iters, 30))
+    dom = max(("gate_up", "down"), key=lambda s: stage_ms[s])
+    t = lb.timed(iters, 5, dom)
+    out = {"workload": lb.wl.name, "format": lb.wl.fmt, "tokens": lb.T, "touched_experts": lb.touched,
+           "tokens_per_s": round(lb.T / (t["ms"] * 1e-3), 1), "us_per_step": round(t["ms"] * 1e3, 2)}
+    for mode in ("cycled", "warm", "cold"):
+        v = lb.per_step(iters, mode, flush)
+        out[f"{mode}_us"] = {"median": round(pct(v, 0.5), 2), "p10": round(pct(v, 0.1), 2),
+                             "p90": round(pct(v, 0.9), 2)}
+    if graph:
+        out["graph_us_per_step"] = round(lb.graph_us(max(10, iters // lb.n_sets)), 2)
+    out["stage_us"] = {s: round(v * 1e3, 2) for s, v in stage_ms.items()}
+    out["roofline"] = roofline(lb, dom, t["dom_ms"], is_decode(lb.wl, lb.T))
+    return out
+
+
+def stack_bench(dev, reps):
+    """All 48 layers back to back (layers 0-23 FP8, 24-47 INT4, residual adds),
+    eager and replayed from one captured HIP graph, at 64 and 2048 tokens."""
     import numpy as np
-    from oracle import moe
+    import torch
+    from weight_quantized_moe_amd import Layer, synth
+    wl = synth.WORKLOADS["stack48"]
+    E, H, I, k, L = wl.experts, wl.hidden, wl.inter, wl.top_k, wl.layers
+    layers = []
+    for li in range(L):
+        fmt = synth.stack_layer_format(li)
+        t13 = synth.random_packed_torch(fmt, E, 2 * I, H, 5000 + 2 * li, dev)
+        t2 = synth.random_packed_torch(fmt, E, H, I, 5001 + 2 * li, dev)
+        layers.append((fmt, Layer(fmt, t13[0], t13[1], t2[0], t2[1], k)))
+    res = {"layers": L, "formats": "0-23 fp8_b128, 24-47 int4_g128"}
+    for T in wl.tokens:
+        lgs = [torch.from_numpy(synth.router_logits(wl.wid, li, T, E)).to(dev) for li in range(L)]
+        x0 = torch.from_numpy(synth.hidden_bf16(wl.wid, 0, T, H).view(np.int16)).to(dev).view(torch.bfloat16)
+        ws = max((lay.workspace(T, dev) for _, lay in layers[:1] + layers[-1:]), key=lambda w: w.numel())
+        bufs = [x0.clone(), torch.empty_like(x0)]
+        offs = torch.empty(E + 1, dtype=torch.int32, device=dev)
+        touched, roof_s, hbm_bytes, flops = [], 0.0, 0, 0
+        for li, (fmt, lay) in enumerate(layers):
+            lay.forward(lgs[li], x0, out=bufs[1], workspace=ws, probe={"expert_offsets": offs})
+            torch.cuda.synchronize()
+            n = int((torch.diff(offs) > 0).sum().item())
+            touched.append(n)
+            w = kernel_work(fmt, E, H, I, k, T, n)
+            hbm_bytes += w["path_bytes"]
+            flops += w["path_flops"]
+            roof_s += max(w["path_bytes"] / (PEAK_HBM_GBS * 1e9), w["path_flops"] / (PEAK_FP16_TFLOPS * 1e12))
+
+        def chain():
+            for li, (_, lay) in enumerate(layers):
+                src, dst = bufs[li & 1], bufs[(li + 1) & 1]
+                lay.forward(lgs[li], src, residual=src, out=dst, workspace=ws)
+
+        bufs[0].copy_(x0)
+        chain()
+        torch.cuda.synchronize()
+        evs = [new_events(2) for _ in range(reps)]
+        for r in range(reps):
+            evs[r][0].record()
+            chain()
+            evs[r][1].record()
+        torch.cuda.synchronize()
+        eager = [a.elapsed_time(b) for a, b in evs]
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            chain()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            chain()
+        g.replay()
+        torch.cuda.synchronize()
+        evs = [new_events(2) for _ in range(reps)]
+        for r in range(reps):
+            evs[r][0].record()
+            g.replay()
+            evs[r][1].record()
+        torch.cuda.synchronize()
+        graph = [a.elapsed_time(b) for a, b in evs]
+        med_e, med_g = pct(eager, 0.5), pct(graph, 0.5)
+        res[f"T{T}"] = {
+            "tokens": T, "touched_experts_mean": round(sum(touched) / L, 1),
+            "eager_ms": {"median": round(med_e, 4), "p10": round(pct(eager, 0.1), 4),
+                         "p90": round(pct(eager, 0.9), 4)},
+            "graph_ms": {"median": round(med_g, 4), "p10": round(pct(graph, 0.1), 4),
+                         "p90": round(pct(graph, 0.9), 4)},
+            "per_layer_us": {"eager": round(med_e * 1e3 / L, 2), "graph": round(med_g * 1e3 / L, 2)},
+            "tokens_per_s_graph": round(T / (med_g * 1e-3), 1),
+            "algorithmic_bytes": hbm_bytes, "algorithmic_flops": flops,
+            "roofline_ms": round(roof_s * 1e3, 4),
+            "frac_of_roofline_graph": round(roof_s * 1e3 / med_g, 4),
+            "hbm_GBps_graph": round(hbm_bytes / (med_g * 1e-3) / 1e9, 1),
+        }
+        del g
+    return res
+
+
+def cpu_baseline(lb, budget_s=10.0, max_tokens=4096):
+    """The oracle as it stands on a contiguous sample of the headline batch
+    (its first tokens, same layer and routing), repeated until ~budget_s."""
+    import numpy as np
+    from oracle import formats, moe
+    wl = lb.wl
+    E, H, I, k, fmt = wl.experts, wl.hidden, wl.inter, wl.top_k, wl.fmt
+    w, s, g, w_, s_, g_ = lb.first_np
+    lay = moe.Layer(formats.Packed(fmt, w, s, g, 2 * I, H), formats.Packed(fmt, w_, s_, g_, H, I), k)
+    info = {}
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()
-                       if p.get("user_api") == "blas"] or [1])
+        blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if blas:
+            info = {"blas": f"{blas[0].get('internal_api')} {blas[0].get('version')}",
+                    "threads": blas[0].get("num_threads")}
     except Exception:  # pragma: no cover
-        threads = 1
-    T = x.shape[0]
-    sample = np.arange(min(T, 64))
+        pass
+    model = "unknown"
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    sample = np.arange(min(lb.T, max_tokens))
     done, t0 = 0, time.perf_counter()
     while True:
-        moe.moe_forward(layer_np, logits, x, tokens=sample)
+        moe.moe_forward(lay, lb.logits_np, lb.x_np, tokens=sample)
         done += len(sample)
         el = time.perf_counter() - t0
         if el >= budget_s:
             break
-    return {"value": done / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} tokens ({len(sample)}-token batches of the same layer, "
-                      f"float64 NumPy per-expert loop incl. dequantization), {el:.1f} s"}
+    # the GEMM-only part of the same sample: both projections over the
+    # already dequantized weights of the experts it routes to
+    ids, _ = moe.route(lb.logits_np[sample], k)
+    perm = moe.permute(ids, E)
+    x = moe.bf16_bits_to_f64(lb.x_np[sample])
+    deq = {e: (formats.dequantize_expert(lay.w13, e), formats.dequantize_expert(lay.w2, e))
+           for e in range(E) if perm.offsets[e + 1] > perm.offsets[e]}
+    t1 = time.perf_counter()
+    for e, (d13, d2) in deq.items():
+        rows = x[perm.sorted_token_ids[perm.offsets[e]:perm.offsets[e + 1]]]
+        gu = rows @ d13.T
+        (gu[:, :I] * gu[:, I:]) @ d2.T
+    gemm_s = time.perf_counter() - t1
+    return {"value": round(done / el, 2), "unit": "tokens/s", "cores": info.get("threads", 1),
+            "kind": "oracle", "cpu_model": model, "host_cpus": len(os.sched_getaffinity(0)),
+            "blas": info.get("blas", "unknown"),
+            "gemm_only_tokens_per_s": round(len(sample) / gemm_s, 1),
+            "sample": f"{done} tokens: the first {len(sample)} tokens of the {lb.T}-token batch "
+                      f"({fmt}, {wl.logits} logits), float64 NumPy per-expert loop incl. "
+                      f"dequantization, routing and combine, {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="nvfp4_zipf")
+    ap.add_argument("--tokens", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-regimes", action="store_true", help="skip the decode / FP8 prefill lines")
+    ap.add_argument("--no-stack", action="store_true", help="skip the 48-layer stack")
+    ap.add_argument("--iters", type=int, default=100, help="per-step samples of each regime line")
+    ap.add_argument("--router", action="store_true",
+                    help="only time the router logits kernel (moe_quant_router_logits) at H 2048, E 128")
+    ap.add_argument("--vendor-bmm", action="store_true",
+                    help="only time torch.bmm (hipBLASLt) FP16 at the prefill expert-GEMM shapes, for reference")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the layer is data parallel over tokens; DESIGN.md describes how it would shard)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from weight_quantized_moe_amd import load_library, synth
+
+    dev = torch.device("cuda:0")
+    if args.router:
+        load_library()
+        print(json.dumps({"kernel": "router logits (moe_quant_router_logits), BF16 MFMA, FP32 out",
+                          "results": router_bench(dev, max(args.steps, 20))}))
+        return
+    if args.vendor_bmm:
+        print(json.dumps({"reference": "torch.bmm FP16 (hipBLASLt), not this library",
+                          "results": vendor_bmm(dev, max(args.steps, 20))}))
+        return
+    load_library()
+    wl = synth.WORKLOADS[args.workload]
+    if wl.fmt == "stack":
+        raise SystemExit("the 48-layer stack is timed in the 'stack48' part of the default run")
+    T = args.tokens or max(wl.tokens)
+    lb = LayerBench(wl, T, dev)
+    decode = is_decode(wl, T)
+    stage_ms = lb.stages(min(args.steps, 20))
+    dom = max(("gate_up", "down"), key=lambda s: stage_ms[s])
+    r = lb.timed(args.steps, args.warmup, dom)
+    print(f"# headline {wl.name} T={T}: {r['ms'] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+    res = {
+        "metric": METRIC,
+        "value": round(T / (r["ms"] * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16-mfma/fp32-acc, bf16 io",
+        "data": "synthetic (seeded packed codes, N(0,1) activations and logits)",
+        "config": {"workload": wl.name, "format": wl.fmt, "tokens": T, "hidden": wl.hidden,
+                   "intermediate": wl.inter, "experts": wl.experts, "top_k": wl.top_k,
+                   "logits": wl.logits, "touched_experts": lb.touched, "weight_sets_cycled": lb.n_sets},
+        "roofline": roofline(lb, dom, r["dom_ms"], decode),
+        "path_roofline": {"bytes": lb.work["path_bytes"], "flops": lb.work["path_flops"],
+                          "hbm_GBps": round(lb.work["path_bytes"] / (r["ms"] * 1e-3) / 1e9, 1),
+                          "tflops": round(lb.work["path_flops"] / (r["ms"] * 1e-3) / 1e12, 2),
+                          "frac_of_mfma_peak": round(lb.work["path_flops"] / (r["ms"] * 1e-3) / 1e12
+                                                     / PEAK_FP16_TFLOPS, 4)},
+        "stage_us": {s: round(v * 1e3, 2) for s, v in stage_ms.items()},
+        "wall_ms_per_step": round(r["wall_ms"], 4),
+    }
+    flush = torch.empty(2 ** 30, dtype=torch.uint8, device=dev)
+    if not args.no_regimes:
+        res["regimes"] = []
+        prev = None
+        for name, T2 in (("decode_int4", 1), ("decode_int4", 8), ("decode_int4", 64),
+                         ("prefill_fp8", 4096)):
+            share = prev if prev is not None and prev.wl.name == name else None
+            other = LayerBench(synth.WORKLOADS[name], T2, dev, share=share)
+            line = regime_line(other, args.iters, flush, graph=is_decode(other.wl, T2))
+            res["regimes"].append(line)
+            print(f"# {name} T={T2}: {line['us_per_step']} us/step", file=sys.stderr, flush=True)
+            prev = other
+        del prev, other
+    if not args.no_stack:
+        res["stack48"] = stack_bench(dev, max(5, args.steps // 2))
+        print("# stack48 done", file=sys.stderr, flush=True)
+    del flush
+    # plain copy of known size: reference reading for HBM byte counters
+    src = torch.empty(256 * 2 ** 20, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(lb)
+    print(json.dumps(res))
 
 
 def vendor_bmm(dev, steps):
@@ -148,190 +563,6 @@ def router_bench(dev, steps):
                     "frac_of_8TB_s": round(gbs / 8000.0, 4),
                     "TFLOP_s": round(2.0 * T * H * E / us / 1e6, 1)})
     return out
-
-
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode_int4")
-    ap.add_argument("--tokens", type=int, default=0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--sweep", action="store_true", help="also time every batch size of the workload")
-    ap.add_argument("--router", action="store_true",
-                    help="only time the router logits kernel (moe_quant_router_logits) at H 2048, E 128")
-    ap.add_argument("--vendor-bmm", action="store_true",
-                    help="only time torch.bmm (hipBLASLt) FP16 at the prefill expert-GEMM shapes, for reference")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the layer is data parallel over tokens; see DESIGN.md for how it would shard)",
-              file=sys.stderr)
-        sys.exit(2)
-
-    import numpy as np
-    import torch
-    from weight_quantized_moe_amd import Layer, load_library, synth
-
-    if args.router:
-        load_library()
-        print(json.dumps({"kernel": "router logits (moe_quant_router_logits), BF16 MFMA, FP32 out",
-                          "results": router_bench(torch.device("cuda:0"), max(args.steps, 20))}))
-        return
-    if args.vendor_bmm:
-        print(json.dumps({"reference": "torch.bmm FP16 (hipBLASLt), not this library",
-                          "results": vendor_bmm(torch.device("cuda:0"), max(args.steps, 20))}))
-        return
-    load_library()
-    wl = synth.WORKLOADS[args.workload]
-    if wl.fmt == "stack":
-        raise SystemExit("use --workload decode_int4 | prefill_fp8 | nvfp4_zipf")
-    E, H, I, k, fmt = wl.experts, wl.hidden, wl.inter, wl.top_k, wl.fmt
-    T = args.tokens or max(wl.tokens)
-    dev = torch.device("cuda:0")
-
-    w13_b = packed_bytes(fmt, 2 * I, H)
-    w2_b = packed_bytes(fmt, H, I)
-    layer_bytes = E * (w13_b + w2_b)
-    n_layers = max(2, math.ceil(1.5 * 2 ** 30 / layer_bytes))
-    layers, np_layers = [], []
-    for li in range(n_layers):
-        t13, ts13, tg13 = synth.random_packed_torch(fmt, E, 2 * I, H, 1000 + 2 * li, dev)
-        t2, ts2, tg2 = synth.random_packed_torch(fmt, E, H, I, 1001 + 2 * li, dev)
-        if li == 0 and not args.no_cpu_baseline:
-            to_np = lambda a: None if a is None else a.cpu().numpy()  # noqa: E731
-            np_layers = tuple(map(to_np, (t13, ts13, tg13, t2, ts2, tg2)))
-        layers.append(Layer(fmt, t13, ts13, t2, ts2, k, w13_gscale=tg13, w2_gscale=tg2))
-
-    def run_config(T, steps, warmup):
-        logits_np = synth.router_logits(wl.wid, 0, T, E, wl.logits)
-        x_np = synth.hidden_bf16(wl.wid, 0, T, H)
-        logits = torch.from_numpy(logits_np).to(dev)
-        x = torch.from_numpy(x_np.view(np.int16)).to(dev).view(torch.bfloat16)
-        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-        ws = layers[0].workspace(T, dev)
-        offs = torch.empty(E + 1, dtype=torch.int32, device=dev)
-        layers[0].forward(logits, x, out=out, workspace=ws, probe={"expert_offsets": offs})
-        torch.cuda.synchronize()
-        touched = int((torch.diff(offs) > 0).sum().item())
-        for i in range(warmup):
-            layers[i % n_layers].forward(logits, x, out=out, workspace=ws)
-
-        def new_events(n):
-            evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-            for e in evs:          # torch creates the HIP event on first record
-                e.record()
-            return evs
-
-        # stage breakdown (its own run: ten event records per step)
-        nb = min(steps, 50)
-        bev = [new_events(2 * len(STAGES)) for _ in range(nb)]
-        for i in range(nb):
-            layers[i % n_layers].forward(logits, x, out=out, workspace=ws, events=bev[i])
-        torch.cuda.synchronize()
-        stage_ms = {s: sum(e[2 * j].elapsed_time(e[2 * j + 1]) for e in bev) / nb
-                    for j, s in enumerate(STAGES)}
-        dom = max(("gate_up", "down"), key=lambda s: stage_ms[s])
-        jd = STAGES.index(dom)
-        # timed region: K steps.  HIP events on the layer's stream bracket the
-        # dominant kernel in every EVERY-th step (an event pair costs a few
-        # microseconds of GPU time, so bracketing every launch would inflate
-        # the step time it is part of).
-        sampled = list(range(0, steps, EVERY))
-        dev_ev = {i: new_events(2) for i in sampled}
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        start.record()
-        for i in range(steps):
-            ev = None
-            if i in dev_ev:
-                ev = [None] * (2 * len(STAGES))
-                ev[2 * jd], ev[2 * jd + 1] = dev_ev[i]
-            layers[i % n_layers].forward(logits, x, out=out, workspace=ws, events=ev)
-        end.record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        ms = start.elapsed_time(end) / steps
-        dom_ms = sum(a.elapsed_time(b) for a, b in dev_ev.values()) / len(dev_ev)
-        return dict(T=T, ms=ms, wall_ms=wall * 1e3 / steps, stage_ms=stage_ms, touched=touched,
-                    dom=dom, dom_ms=dom_ms, logits=logits_np, x=x_np)
-
-    r = run_config(T, args.steps, args.warmup)
-    R = T * k
-    touched = r["touched"]
-    # algorithmic work (SURVEY/DESIGN definitions)
-    path_bytes = touched * (w13_b + w2_b) + T * H * 2 * 2 + T * E * 4
-    flops = 6 * H * I * R
-    kern_bytes = {
-        "gate_up": touched * w13_b + T * H * 2 + R * I * 2,
-        "down": touched * w2_b + R * I * 2 + R * H * 4,
-    }
-    kern_flops = {"gate_up": 4 * H * I * R, "down": 2 * H * I * R}
-    dom = r["dom"]
-    dom_s = r["dom_ms"] * 1e-3
-    decode = R <= 16 * E
-    if decode:
-        achieved = kern_bytes[dom] / dom_s / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
-    else:
-        achieved = kern_flops[dom] / dom_s / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4)}
-    tag = f"{dom}_{fmt}_T{T}"
-    traffic = counter_traffic(tag)
-    roof["traffic"] = traffic
-    roof["kernel"] = dom
-    roof["kernel_us"] = round(r["dom_ms"] * 1e3, 2)
-    roof["algorithmic_bytes" if decode else "algorithmic_flops"] = \
-        kern_bytes[dom] if decode else kern_flops[dom]
-
-    res = {
-        "metric": "MoE layer tokens/s + % roofline (HBM GB/s decode, MFMA util prefill)",
-        "value": round(T / (r["ms"] * 1e-3), 1),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(r["ms"], 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "fp16-mfma/fp32-acc, bf16 io",
-        "data": "synthetic (seeded packed codes, N(0,1) activations and logits)",
-        "config": {"workload": wl.name, "format": fmt, "tokens": T, "hidden": H,
-                   "intermediate": I, "experts": E, "top_k": k, "logits": wl.logits,
-                   "touched_experts": touched, "weight_sets_cycled": n_layers},
-        "roofline": roof,
-        "path_roofline": {"bytes": path_bytes, "flops": flops,
-                          "hbm_GBps": round(path_bytes / (r["ms"] * 1e-3) / 1e9, 1),
-                          "tflops": round(flops / (r["ms"] * 1e-3) / 1e12, 2)},
-        "stage_us": {s: round(v * 1e3, 2) for s, v in r["stage_ms"].items()},
-        "wall_ms_per_step": round(r["wall_ms"], 4),
-    }
-    if args.sweep:
-        res["sweep"] = []
-        for t in wl.tokens:
-            rr = run_config(t, args.steps, args.warmup)
-            res["sweep"].append({"tokens": t, "us_per_step": round(rr["ms"] * 1e3, 2),
-                                 "tokens_per_s": round(t / (rr["ms"] * 1e-3), 1),
-                                 "touched": rr["touched"],
-                                 "stage_us": {s: round(v * 1e3, 2) for s, v in rr["stage_ms"].items()}})
-    # plain copy of known size: reference reading for HBM byte counters
-    src = torch.empty(256 * 2 ** 20, dtype=torch.uint8, device=dev)
-    dst = torch.empty_like(src)
-    dst.copy_(src)
-    torch.cuda.synchronize()
-    if not args.no_cpu_baseline:
-        from oracle import formats, moe
-        w, s, g, w_, s_, g_ = np_layers
-        lay = moe.Layer(formats.Packed(fmt, w, s, g, 2 * I, H), formats.Packed(fmt, w_, s_, g_, H, I), k)
-        res["cpu_baseline"] = cpu_baseline(lay, r["logits"], r["x"])
-    else:
-        res["cpu_baseline"] = None
-    print(json.dumps(res))
 
 
 if __name__ == "__main__":

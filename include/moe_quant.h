@@ -34,8 +34,9 @@
  *    Nothing is printed and no exception crosses the ABI.
  *  - Work is enqueued asynchronously on the caller's HIP stream (a
  *    hipStream_t, passed as struct ihipStream_t *; NULL is the default stream).
- *  - A handle is immutable after init: concurrent forward calls on different
- *    streams are safe as long as each uses its own workspace.
+ *  - A handle is immutable after init: concurrent forward calls, from any host
+ *    threads, on different streams are safe as long as each uses its own
+ *    workspace (the library's launch-shape caches are guarded by a lock).
  */
 #ifndef MOE_QUANT_H
 #define MOE_QUANT_H
@@ -94,8 +95,13 @@ typedef enum {
  *     gscale float32 [E]            global scale g = 448*6/amax
  *     weight = e2m1(c) * e4m3(scale[n, k/16]) / gscale[e]
  *
- * Dimension limits of this version: H and I multiples of 128 for every format
- * (the NVFP4 format itself only needs 16), 1 <= k <= E <= 512.
+ * Dimension limits of this version: H and I multiples of 128 for every format,
+ * 128 <= H, I <= 4608 (the decode GEMM stages 16 whole input rows of a
+ * projection in the 160 KiB LDS of one workgroup), 1 <= k <= E <= 512, k <= 64.
+ * The NVFP4 format itself only needs multiples of 16; this version's GEMM
+ * tiles (128-wide k blocks and 128-row weight tiles) take multiples of 128
+ * for NVFP4 too, which every Clef shape satisfies (hidden 2048, intermediate
+ * 768).
  */
 typedef enum { MQ_W_INT4_G128 = 1, MQ_W_FP8_B128 = 2, MQ_W_NVFP4_G16 = 3 } mq_wformat;
 
@@ -159,7 +165,8 @@ typedef struct {
  * Validate a layer descriptor and create a handle.  Host only: no HIP call is
  * made.  On MQ_OK *out holds a handle to release with moe_quant_destroy.
  * Errors: MQ_E_NULL (d, out or a weight pointer NULL; gscale NULL for NVFP4),
- * MQ_E_ABI, MQ_E_FORMAT, MQ_E_SHAPE, MQ_E_ALIGN.
+ * MQ_E_ABI, MQ_E_FORMAT, MQ_E_SHAPE (a dimension outside the limits above),
+ * MQ_E_ALIGN.
  */
 mq_status moe_quant_init(const mq_layer_desc *d, mq_layer **out);
 

@@ -176,7 +176,6 @@ def moe_forward(layer: Layer, logits: np.ndarray, x_bf16_bits: np.ndarray,
     tokens = np.asarray(tokens, dtype=np.int64)
     ids, w = route(logits[tokens], layer.top_k)
     x = bf16_bits_to_f64(np.asarray(x_bf16_bits)[tokens])
-    y = np.zeros((len(tokens), layer.hidden), dtype=np.float64)
     perm = permute(ids, layer.num_experts)
     # per-expert FP64 loop over the dequantized weights
     expert_out = np.empty((len(tokens) * layer.top_k, layer.hidden), dtype=np.float64)
@@ -188,10 +187,22 @@ def moe_forward(layer: Layer, logits: np.ndarray, x_bf16_bits: np.ndarray,
         w13 = formats.dequantize_expert(layer.w13, e)
         w2 = formats.dequantize_expert(layer.w2, e)
         expert_out[lo:hi] = expert_mlp(x[rows], w13, w2)
-    # combine in slot order
-    for j in range(layer.top_k):
-        rows = perm.inv_pos[np.arange(len(tokens)) * layer.top_k + j]
-        y += w[:, j:j + 1] * expert_out[rows]
+    y = combine(perm, w, expert_out)
     if residual_bf16_bits is not None:
         y = y + bf16_bits_to_f64(np.asarray(residual_bf16_bits)[tokens])
     return y, ids, w
+
+
+def combine(perm: Permutation, w: np.ndarray, expert_out: np.ndarray) -> np.ndarray:
+    """Routing-weighted sum of the k expert outputs of every token, in slot order.
+
+    ``expert_out`` [T*k, H] holds the expert outputs in grouped row order (row
+    ``perm.inv_pos[t*k + j]`` is slot j of token t); ``w`` [T, k] the routing
+    weights.  Returns y [T, H] = sum_j w[t, j] * expert_out[row(t, j)].
+    """
+    t, k = w.shape
+    y = np.zeros((t, expert_out.shape[1]), dtype=np.float64)
+    for j in range(k):
+        rows = perm.inv_pos[np.arange(t) * k + j]
+        y += w[:, j:j + 1] * expert_out[rows]
+    return y

@@ -50,6 +50,59 @@ def quantized_layer(fmt, wid, layer, E, H, I, workers=None):
     return out[0], out[1]
 
 
+def quantize_expert_job(args):
+    """Worker job: oracle-quantized N(0, 0.02) weights of one expert of one
+    layer.  Returns ((w, scale, gscale) of w13, (w, scale, gscale) of w2)."""
+    fmt, wid, layer, e, H, I = args
+    out = []
+    for which, n, k in (("w13", 2 * I, H), ("w2", H, I)):
+        w = synth.expert_weight(wid, layer, which, e, n, k).astype(np.float64)
+        out.append(formats.quantize_expert(fmt, w))
+    return tuple(out)
+
+
+def expert_outputs_job(args):
+    """Worker job: the oracle's SwiGLU expert (float64, exact dequantization)
+    on each of several row sets.  ``q`` is quantize_expert_job's result;
+    ``row_sets`` a list of float64 [n, H] arrays (or None)."""
+    fmt, H, I, q, row_sets = args
+    (w13, s13, g13), (w2, s2, g2) = q
+    one = lambda a: None if a is None else np.asarray(a)[None]  # noqa: E731
+    p13 = formats.Packed(fmt, one(w13), one(s13), one(g13), 2 * I, H)
+    p2 = formats.Packed(fmt, one(w2), one(s2), one(g2), H, I)
+    d13 = formats.dequantize_expert(p13, 0)
+    d2 = formats.dequantize_expert(p2, 0)
+    return [None if x is None or len(x) == 0 else moe.expert_mlp(x, d13, d2) for x in row_sets]
+
+
+def oracle_forward_pool(pool, p13, p2, top_k, logits, x_bits):
+    """The oracle's layer output for every token, with the per-expert step
+    (dequantize + SwiGLU expert, float64) farmed to ``pool``: route, permute
+    and combine are the oracle's own functions, in the order moe_forward runs
+    them, so the result equals moe.moe_forward's (checked on the CPU)."""
+    fmt, H, I, E = p13.fmt, p13.k, p13.n // 2, p13.num_experts
+    ids, w = moe.route(logits, top_k)
+    perm = moe.permute(ids, E)
+    x = moe.bf16_bits_to_f64(x_bits)
+    g = lambda p, e: None if p.gscale is None else p.gscale[e]  # noqa: E731
+    futs = {}
+    for e in range(E):
+        lo, hi = perm.offsets[e], perm.offsets[e + 1]
+        if hi > lo:
+            q = ((p13.w[e], p13.scale[e], g(p13, e)), (p2.w[e], p2.scale[e], g(p2, e)))
+            futs[e] = pool.submit(expert_outputs_job,
+                                  (fmt, H, I, q, [x[perm.sorted_token_ids[lo:hi]]]))
+    expert_out = np.empty((len(ids) * top_k, H), dtype=np.float64)
+    for e, f in futs.items():
+        expert_out[perm.offsets[e]:perm.offsets[e + 1]] = f.result()[0]
+    return moe.combine(perm, w, expert_out), ids, w
+
+
+def spawn_pool(workers=None):
+    nproc = workers or min(16, len(os.sched_getaffinity(0)))
+    return ProcessPoolExecutor(nproc, mp_context=multiprocessing.get_context("spawn"))
+
+
 def random_layer(fmt, seed, E, H, I):
     """Packed weights drawn directly (codes and scales with the spread of
     quantized N(0, 0.02) weights)."""

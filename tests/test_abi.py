@@ -75,6 +75,9 @@ def test_init_accepts_valid_descriptors(lib):
     (dict(h=200), MQ_E_SHAPE),
     (dict(i=64), MQ_E_SHAPE),
     (dict(fmt=3, h=272), MQ_E_SHAPE),
+    (dict(h=4736), MQ_E_SHAPE),           # decode rows of 4736 values exceed 160 KiB of LDS
+    (dict(i=4736), MQ_E_SHAPE),
+    (dict(fmt=2, h=65536, i=128), MQ_E_SHAPE),
     (dict(base=0x10008), MQ_E_ALIGN),
     (dict(fmt=1, gscale=True), MQ_E_NULL),
 ])
@@ -83,6 +86,13 @@ def test_init_rejects(lib, change, expect):
     assert st == expect, (change, st, lib.moe_quant_last_error())
     assert h.value is None
     assert lib.moe_quant_last_error()
+
+
+def test_init_accepts_the_largest_dimensions(lib):
+    for fmt in (1, 2, 3):
+        st, h = _init(lib, _desc(fmt, h=4608, i=4608))
+        assert st == MQ_OK, lib.moe_quant_last_error()
+        lib.moe_quant_destroy(h)
 
 
 def test_init_null_and_missing_pointers(lib):

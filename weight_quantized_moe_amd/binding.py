@@ -126,17 +126,53 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream
 
 
+def _need(t, name, shape, dtypes, device=None):
+    """Raise ValueError unless tensor ``t`` is contiguous, of the given shape
+    (None entries match any size) and one of ``dtypes``.  Checked before any
+    launch: a wrong shape or a strided view would otherwise become
+    out-of-bounds device accesses.  (``device`` is checked by _on_gpu.)"""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if t.dim() != len(shape) or any(s is not None and s != d for s, d in zip(shape, t.shape)):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _on_gpu(device, **tensors):
+    """Raise ValueError unless every given tensor is a GPU tensor on ``device``
+    (the first one's device if ``device`` is None)."""
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        device = device if device is not None else t.device
+        if t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
 def router_logits(hidden, router_w, out=None, stream=None):
     """Router logits float32 [T, E] = hidden [T, H] . router_w [E, H]^T, both
     bfloat16 on the GPU (moe_quant_router_logits)."""
     import torch
     lib = load_library()
+    if hidden.dim() != 2 or router_w.dim() != 2:
+        raise ValueError("need hidden [T, H] and router weight [E, H]")
     t, h = hidden.shape
     e = router_w.shape[0]
-    if router_w.shape[1] != h or hidden.dtype != torch.bfloat16 or router_w.dtype != torch.bfloat16:
-        raise ValueError("need bfloat16 hidden [T, H] and router weight [E, H]")
+    _need(hidden, "hidden", (t, h), (torch.bfloat16,))
+    _need(router_w, "router_w", (e, h), (torch.bfloat16,))
     if out is None:
         out = torch.empty((t, e), dtype=torch.float32, device=hidden.device)
+    _need(out, "out", (t, e), (torch.float32,))
+    _on_gpu(None, hidden=hidden, router_w=router_w, out=out)
     _check(lib, lib.moe_quant_router_logits(_ptr(hidden), _ptr(router_w), t, h, e, _ptr(out),
                                             _stream(stream)))
     return out
@@ -157,10 +193,32 @@ class Layer:
         if fmt not in FORMATS:
             raise ValueError(f"unknown format {fmt!r}")
         self.fmt = fmt
+        import torch
+        if w13.dim() != 3 or w2.dim() != 3:
+            raise ValueError("w13 and w2 must be [E, N, K-bytes] tensors")
         e, n13, kb = w13.shape
         e2, h, _ = w2.shape
         if e2 != e:
             raise ValueError("w13 and w2 disagree on the number of experts")
+        i = n13 // 2
+        kdiv = 1 if fmt == "fp8_b128" else 2
+        u8 = (torch.uint8,)
+        _need(w13, "w13", (e, 2 * i, h // kdiv), u8)
+        _need(w2, "w2", (e, h, i // kdiv), u8)
+        if fmt == "int4_g128":
+            _need(w13_scale, "w13_scale", (e, 2 * i, h // 128), (torch.float16,))
+            _need(w2_scale, "w2_scale", (e, h, i // 128), (torch.float16,))
+        elif fmt == "fp8_b128":
+            _need(w13_scale, "w13_scale", (e, 2 * i // 128, h // 128), (torch.float32,))
+            _need(w2_scale, "w2_scale", (e, h // 128, i // 128), (torch.float32,))
+        else:
+            _need(w13_scale, "w13_scale", (e, 2 * i, h // 16), u8)
+            _need(w2_scale, "w2_scale", (e, h, i // 16), u8)
+            _need(w13_gscale, "w13_gscale", (e,), (torch.float32,))
+            _need(w2_gscale, "w2_gscale", (e,), (torch.float32,))
+        _on_gpu(None, w13=w13, w13_scale=w13_scale, w2=w2, w2_scale=w2_scale,
+                w13_gscale=w13_gscale, w2_gscale=w2_gscale)
+        self.device = w13.device
         self.num_experts, self.hidden, self.inter, self.top_k = e, h, n13 // 2, top_k
         self._keep = (w13, w13_scale, w2, w2_scale, w13_gscale, w2_gscale)
         d = LayerDesc(ABI_VERSION, e, h, n13 // 2, top_k, FORMATS[fmt],
@@ -184,23 +242,44 @@ class Layer:
     def workspace(self, num_tokens: int, device=None):
         import torch
         return torch.empty(max(self.workspace_size(num_tokens), 256), dtype=torch.uint8,
-                           device=device or "cuda")
+                           device=device or self.device)
 
     def forward(self, logits, hidden, residual=None, out=None, workspace=None,
                 probe: Optional[Dict] = None, events=None, stream=None):
         """Enqueue one forward; returns ``out`` (bfloat16 [T, H])."""
         import torch
+        if hidden.dim() != 2:
+            raise ValueError("hidden must be [T, H]")
         t = hidden.shape[0]
+        dev = self.device
+        bf16 = (torch.bfloat16,)
+        _need(hidden, "hidden", (t, self.hidden), bf16)
+        _need(logits, "logits", (t, self.num_experts), (torch.float32, torch.bfloat16))
+        if residual is not None:
+            _need(residual, "residual", (t, self.hidden), bf16)
         if out is None:
-            out = torch.empty((t, self.hidden), dtype=torch.bfloat16, device=hidden.device)
+            out = torch.empty((t, self.hidden), dtype=torch.bfloat16, device=dev)
+        _need(out, "out", (t, self.hidden), bf16)
+        shapes = {"topk_ids": ((t, self.top_k), torch.int32), "topk_w": ((t, self.top_k), torch.float32),
+                  "expert_offsets": ((self.num_experts + 1,), torch.int32),
+                  "sorted_token_ids": ((t * self.top_k,), torch.int32),
+                  "inv_pos": ((t * self.top_k,), torch.int32),
+                  "h": ((t * self.top_k, self.inter), torch.float16)}
+        for name, v in (probe or {}).items():
+            if name not in shapes:
+                raise ValueError(f"unknown probe output {name!r}")
+            if v is not None:
+                _need(v, f"probe[{name!r}]", shapes[name][0], (shapes[name][1],))
+        if workspace is not None and not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous")
+        _on_gpu(dev, hidden=hidden, logits=logits, residual=residual, out=out, workspace=workspace,
+                **{f"probe[{n!r}]": v for n, v in (probe or {}).items()})
         if workspace is None:
-            workspace = self.workspace(t, hidden.device)
-        if logits.dtype == torch.float32:
-            ldt = MQ_F32
-        elif logits.dtype == torch.bfloat16:
-            ldt = MQ_BF16
-        else:
-            raise ValueError("router logits must be float32 or bfloat16")
+            workspace = self.workspace(t, dev)
+        if t > 0 and _nbytes(workspace) < self.workspace_size(t):   # T = 0 enqueues nothing
+            raise ValueError(f"workspace holds {_nbytes(workspace)} bytes, "
+                             f"{self.workspace_size(t)} needed for {t} tokens")
+        ldt = MQ_F32 if logits.dtype == torch.float32 else MQ_BF16
         pr = None
         if probe is not None or events is not None:
             pr = Probe()
@@ -212,7 +291,7 @@ class Layer:
                     pr.events[i] = None if ev is None else ev.cuda_event
         st = self._lib.moe_quant_forward(
             self._h, _ptr(logits), ldt, _ptr(hidden), _ptr(residual), t, _ptr(out),
-            _ptr(workspace), workspace.numel(), ctypes.byref(pr) if pr is not None else None,
+            _ptr(workspace), _nbytes(workspace), ctypes.byref(pr) if pr is not None else None,
             _stream(stream))
         _check(self._lib, st)
         return out
@@ -228,7 +307,7 @@ class Layer:
     def dequantize(self, which: int, expert: int, stream=None):
         import torch
         n, k = (2 * self.inter, self.hidden) if which == 0 else (self.hidden, self.inter)
-        out = torch.empty((n, k), dtype=torch.float32, device="cuda")
+        out = torch.empty((n, k), dtype=torch.float32, device=self.device)
         _check(self._lib, self._lib.moe_quant_dequantize(self._h, which, expert, _ptr(out),
                                                           _stream(stream)))
         return out

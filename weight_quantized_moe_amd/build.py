@@ -1,6 +1,9 @@
 """Build libmoe_quant.so for gfx950 with hipcc (in-tree, next to this file).
 
     python -m weight_quantized_moe_amd.build
+
+Each source compiles to its own object in ``_build/`` (in parallel), then one
+hipcc call links the shared library.
 """
 from __future__ import annotations
 
@@ -9,17 +12,18 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_quant.so")
+OBJ_DIR = os.path.join(HERE, "..", "_build")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-Wall",
     "-Wno-unused-function",
     # never emit packed FP32 VALU ops
@@ -38,22 +42,46 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP/C++ source into libmoe_quant.so; returns its path."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(HERE, "..", "include"), *sources(), "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
+    return res
+
+
+def build(verbose: bool = False, extra_flags=(), out: str = LIB) -> str:
+    """Compile every HIP/C++ source into ``out`` (libmoe_quant.so); returns its path.
+
+    ``extra_flags`` are added to every compile and to the link (for instance a
+    host-only sanitizer build: ``-Xarch_host -fsanitize=address``).
+    """
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    tag = "" if out == LIB else "_" + os.path.splitext(os.path.basename(out))[0]
+    inc = ["-I", os.path.join(HERE, "..", "include")]
+    jobs = []
+    for src in sources():
+        obj = os.path.join(OBJ_DIR, os.path.basename(src) + tag + ".o")
+        jobs.append((src, obj, [hipcc(), *HIPCC_FLAGS, *extra_flags, *inc, "-c", src, "-o", obj]))
+    workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", "8"))))
+    with ThreadPoolExecutor(workers) as ex:
+        results = list(ex.map(lambda j: _run(j[2], verbose), jobs))
+    warn = []
+    for (src, _, _), res in zip(jobs, results):
+        text = res.stdout + res.stderr
+        if res.returncode != 0:
+            sys.stderr.write(text)
+            raise RuntimeError(f"hipcc failed compiling {os.path.basename(src)}")
+        warn += [ln for ln in text.splitlines() if "warning" in ln and "packed-fp32-ops" not in ln]
+    tmp = out + ".tmp"
+    res = _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *extra_flags,
+                *[j[1] for j in jobs], "-o", tmp], verbose)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building libmoe_quant.so")
-    warn = [ln for ln in (res.stdout + res.stderr).splitlines()
-            if "warning" in ln and "packed-fp32-ops" not in ln]
+        raise RuntimeError("hipcc failed linking libmoe_quant.so")
     if verbose and warn:
         print("\n".join(warn))
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

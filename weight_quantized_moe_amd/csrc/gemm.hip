@@ -15,6 +15,10 @@
 // lane therefore owns one output column, so a per-column scale is one scalar
 // per lane.
 #include <algorithm>
+#include <map>
+#include <mutex>
+#include <set>
+#include <tuple>
 #include <type_traits>
 
 #include <hip/hip_ext.h>
@@ -937,39 +941,68 @@ static GemmArgs make_args(const LayerDims &L, const FwdPtrs &P, const Workspace 
   return a;
 }
 
-static int g_num_cus = 0;
+// Launch-shape caches, shared by every host thread that launches: compute
+// units per device, resident blocks per CU per (kernel, device, LDS bytes),
+// and the (kernel, device) pairs whose dynamic-LDS limit has been raised.
+static std::mutex g_launch_mu;
+static std::map<int, int> g_num_cus;
+static std::map<std::tuple<const void *, int, size_t>, int> g_per_cu;
+static std::set<std::pair<const void *, int>> g_lds_raised;
+
+static int current_device() {
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  return dev;
+}
 
 static int num_cus() {
-  if (g_num_cus == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-      g_num_cus = n;
-    else
-      g_num_cus = 256;
+  const int dev = current_device();
+  std::lock_guard<std::mutex> lk(g_launch_mu);
+  auto it = g_num_cus.find(dev);
+  if (it != g_num_cus.end()) return it->second;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    n = 256;
+  g_num_cus[dev] = n;
+  return n;
+}
+
+// Allow up to 160 KiB of dynamic LDS for kernel f on the current device (once).
+static void raise_lds_limit(const void *f) {
+  const int dev = current_device();
+  std::lock_guard<std::mutex> lk(g_launch_mu);
+  if (g_lds_raised.insert({f, dev}).second)
+    (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLdsBytes);
+}
+
+// Workgroups of kernel f resident per CU at `threads` threads and `lds` bytes.
+template <typename F>
+static int blocks_per_cu(F f, int threads, size_t lds) {
+  raise_lds_limit((const void *)f);
+  const int dev = current_device();
+  const auto key = std::make_tuple((const void *)f, dev, lds);
+  {
+    std::lock_guard<std::mutex> lk(g_launch_mu);
+    auto it = g_per_cu.find(key);
+    if (it != g_per_cu.end()) return it->second;
   }
-  return g_num_cus;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, threads, lds) != hipSuccess || n < 1) n = 1;
+  std::lock_guard<std::mutex> lk(g_launch_mu);
+  g_per_cu[key] = n;
+  return n;
 }
 
 template <int FMT, int STAGE, int KSPLIT, int GCT, int TPW>
 static hipError_t run_decode_t(GemmArgs a, int slots, const GemmLaunch &s) {
   constexpr int CG = kDecodeWaves / KSPLIT;
   a.tiles = STAGE == 0 ? a.I / (16 * CG * TPW) : a.H / (32 * CG * TPW);
-  const size_t lds = (size_t)16 * (a.K + 8) * 2 + 48 * 4 + (size_t)(KSPLIT - 1) * CG * 512 * 4;
+  const size_t lds = decode_lds_bytes(a.K, KSPLIT);
+  static_assert(CG == 8 / KSPLIT && kDecodeWaves == 8, "decode_lds_bytes assumes 8 waves");
+  if (lds > kMaxLdsBytes) return hipErrorInvalidValue;  // init rejects such shapes
   // persistent grid: as many blocks as are resident at once (from the
   // kernel's registers and LDS), never more than the number of units
-  static int per_cu = 0;
-  static size_t per_cu_lds = 0;
-  if (per_cu == 0 || per_cu_lds != lds) {
-    (void)hipFuncSetAttribute((const void *)gemm_decode<FMT, STAGE, KSPLIT, GCT, TPW>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_decode<FMT, STAGE, KSPLIT, GCT, TPW>,
-                                                     64 * kDecodeWaves, lds) != hipSuccess || n < 1)
-      n = 1;
-    per_cu = n;
-    per_cu_lds = lds;
-  }
+  const int per_cu = blocks_per_cu(gemm_decode<FMT, STAGE, KSPLIT, GCT, TPW>, 64 * kDecodeWaves, lds);
   const long units = (long)slots * a.tiles;
   const long grid = std::min<long>(units, (long)num_cus() * per_cu);
   hipExtLaunchKernelGGL((gemm_decode<FMT, STAGE, KSPLIT, GCT, TPW>), dim3((unsigned)grid),
@@ -1036,12 +1069,8 @@ static hipError_t run_prefill_wide(GemmArgs a, int64_t R, const GemmLaunch &s) {
   const int64_t max_mt = R / kBM + a.E;  // >= sum_e ceil(n_e / kBM)
   const int64_t grid = 8 * ((max_mt * a.tiles + 7) / 8);
   constexpr size_t lds = Shape::LDS;  // above the default limit
-  static bool attr_set = false;
-  if (!attr_set) {
-    (void)hipFuncSetAttribute((const void *)gemm_prefill_wide<FMT, TN, WPB, STAGE>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    attr_set = true;
-  }
+  static_assert(lds <= kMaxLdsBytes, "prefill tile fits in LDS");
+  raise_lds_limit((const void *)gemm_prefill_wide<FMT, TN, WPB, STAGE>);
   hipExtLaunchKernelGGL((gemm_prefill_wide<FMT, TN, WPB, STAGE>), dim3((unsigned)grid), dim3(64 * WPB),
                         (uint32_t)lds, s.stream, s.start, s.stop, 0u, a);
   return hipGetLastError();

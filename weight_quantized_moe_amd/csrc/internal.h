@@ -15,6 +15,27 @@ constexpr int kMaxChunks = 256;  // token chunks of the grouping for T > 64
 // GEMM that stages them (decode) or in two passes (prefill).
 constexpr int kRowRegsMaxH = 2048;
 
+// LDS of one workgroup on gfx950 (bytes).
+constexpr size_t kMaxLdsBytes = 160 * 1024;
+constexpr int kDecodeRows = 16;  // rows of one decode unit staged in LDS
+
+// Dynamic LDS of the decode GEMM for input dimension K and k split ks: the
+// unit's FP16 rows [16][K + 8], row scales, and the k-split reduction tiles.
+constexpr size_t decode_lds_bytes(int K, int ks) {
+  return (size_t)kDecodeRows * (K + 8) * 2 + 48 * 4 + (size_t)(ks - 1) * (8 / ks) * 512 * 4;
+}
+// Whether the decode GEMM's LDS fits for input dimension K at every k split.
+constexpr bool decode_fits(int K) {
+  for (int ks = 1; ks <= 8; ks *= 2)
+    if (decode_lds_bytes(K, ks) > kMaxLdsBytes) return false;
+  return true;
+}
+
+constexpr int kMaxGemmK = 4608;
+static_assert(decode_lds_bytes(kMaxGemmK, 8) <= kMaxLdsBytes &&
+                  decode_lds_bytes(kMaxGemmK + 128, 8) > kMaxLdsBytes,
+              "kMaxGemmK is the largest multiple of 128 the decode GEMM can stage");
+
 // Chunks of the grouping: at most kMaxChunks, each a multiple of 256 tokens.
 inline void permute_chunks(int64_t T, int *nc, int *chunk) {
   int64_t n = (T + 255) / 256;

@@ -104,8 +104,11 @@ mq_status moe_quant_init(const mq_layer_desc *d, mq_layer **out) {
                 "init: hidden %d and intermediate %d must be positive multiples of 128 "
                 "(block sizes of INT4 g128 / FP8 128x128; this version's tiles for NVFP4)",
                 H, I);
-  if ((int64_t)H > 65536 || (int64_t)I > 65536)
-    return fail(MQ_E_SHAPE, "init: hidden/intermediate above 65536");
+  if (!mq::decode_fits(H) || !mq::decode_fits(I))
+    return fail(MQ_E_SHAPE,
+                "init: hidden %d / intermediate %d above %d: the decode GEMM stages 16 whole "
+                "rows of the input dimension in LDS (160 KiB per workgroup)",
+                H, I, mq::kMaxGemmK);
   if (!d->w13 || !d->w13_scale || !d->w2 || !d->w2_scale)
     return fail(MQ_E_NULL, "init: weight and scale pointers must be non-NULL");
   if (d->format == MQ_W_NVFP4_G16 && (!d->w13_gscale || !d->w2_gscale))
