@@ -306,6 +306,16 @@ def stack_bench(dev, reps):
                 src, dst = bufs[li & 1], bufs[(li + 1) & 1]
                 lay.forward(lgs[li], src, residual=src, out=dst, workspace=ws)
 
+        # one checked pass: which layers saturate an FP16 intermediate, and the
+        # size of the residual stream at the end
+        bufs[0].copy_(x0)
+        saturated = []
+        for li, (_, lay) in enumerate(layers):
+            src, dst = bufs[li & 1], bufs[(li + 1) & 1]
+            lay.forward(lgs[li], src, residual=src, out=dst, workspace=ws)
+            if lay.check(ws):
+                saturated.append(li)
+        final_rms = bufs[L & 1].float().square().mean().sqrt().item()
         bufs[0].copy_(x0)
         chain()
         torch.cuda.synchronize()
@@ -347,6 +357,7 @@ def stack_bench(dev, reps):
             "roofline_ms": round(roof_s * 1e3, 4),
             "frac_of_roofline_graph": round(roof_s * 1e3 / med_g, 4),
             "hbm_GBps_graph": round(hbm_bytes / (med_g * 1e-3) / 1e9, 1),
+            "saturated_layers": saturated, "final_residual_rms": round(final_rms, 4),
         }
         del g
     return res

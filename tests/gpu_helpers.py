@@ -98,9 +98,20 @@ def oracle_forward_pool(pool, p13, p2, top_k, logits, x_bits):
     return moe.combine(perm, w, expert_out), ids, w
 
 
+def _single_threaded_blas():
+    """Pool initializer: one BLAS thread per worker (the pool supplies the
+    parallelism; nested BLAS threads would oversubscribe the cores)."""
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:  # pragma: no cover
+        pass
+
+
 def spawn_pool(workers=None):
     nproc = workers or min(16, len(os.sched_getaffinity(0)))
-    return ProcessPoolExecutor(nproc, mp_context=multiprocessing.get_context("spawn"))
+    return ProcessPoolExecutor(nproc, mp_context=multiprocessing.get_context("spawn"),
+                               initializer=_single_threaded_blas)
 
 
 def random_layer(fmt, seed, E, H, I):

@@ -52,13 +52,17 @@ __device__ __forceinline__ _Float16 to_f16_sat(float v, uint32_t &sat) {
   return (_Float16)c;
 }
 
-__device__ __forceinline__ void store_h(const GemmArgs &a, int r, int col, float g, float u) {
-  float hv = silu(g) * u;
-  if (fabsf(hv) > 65504.f) {
-    atomicOr(a.flags, 1u);
-    hv = hv > 0.f ? 65504.f : -65504.f;
-  }
-  a.h_out[(size_t)r * a.I + col] = (_Float16)hv;
+// SwiGLU of one (gate, up) pair into the FP16 intermediate; `sat` remembers a
+// clamp (the caller sets the flag word once per wave).
+__device__ __forceinline__ void store_h(const GemmArgs &a, int r, int col, float g, float u,
+                                        uint32_t &sat) {
+  a.h_out[(size_t)r * a.I + col] = to_f16_sat(silu(g) * u, sat);
+}
+
+// One flag-word update per wave that saw a saturated value (every lane of the
+// wave must reach this call).
+__device__ __forceinline__ void flag_saturation(const GemmArgs &a, uint32_t sat) {
+  if (__builtin_amdgcn_ballot_w64(sat != 0u) != 0ull && (threadIdx.x & 63) == 0) atomicOr(a.flags, 1u);
 }
 
 // ===========================================================================
@@ -363,8 +367,9 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode(GemmArgs a) {
           }
         }
       }
-      if (kp == 0) {
+      if (kp == 0) {  // wave-uniform
         const float ginv = FMT == FMT_NVFP4 ? 1.0f / a.gscale[e] : 1.0f;
+        uint32_t sat = 0u;
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
           const int m = 4 * q + ii;
@@ -373,18 +378,17 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode(GemmArgs a) {
           const int slot = rinf[ii].x;
           if (STAGE == 0) {
             const float sc = sm_rscale[m] * ginv;
-            store_h(a, r, row[0][0], acc[0][0][ii] * sc, acc[0][1][ii] * sc);
+            store_h(a, r, row[0][0], acc[0][0][ii] * sc, acc[0][1][ii] * sc, sat);
           } else {
             const float wt = __builtin_bit_cast(float, rinf[ii].w) * ginv;
-            uint32_t sat = 0u;
 #pragma unroll
             for (int p = 0; p < TPW; ++p) {
               a.partial[(size_t)slot * a.H + row[p][0]] = to_f16_sat(acc[p][0][ii] * wt, sat);
               a.partial[(size_t)slot * a.H + row[p][1]] = to_f16_sat(acc[p][1][ii] * wt, sat);
             }
-            if (sat) atomicOr(a.flags, 1u);
           }
         }
+        flag_saturation(a, sat);
       }
     }
   }
@@ -821,7 +825,7 @@ void gemm_prefill_wide(GemmArgs a) {
     }
     sat |= !(vmax <= 65504.f) || vnan != 0.f;  // NaN counts as saturated
   }
-  if (__builtin_amdgcn_ballot_w64(sat != 0u) != 0ull && lane == 0) atomicOr(a.flags, 1u);
+  flag_saturation(a, sat);
 }
 
 // ===========================================================================
@@ -936,7 +940,7 @@ static GemmArgs make_args(const LayerDims &L, const FwdPtrs &P, const Workspace 
   a.mtile = (const int32_t *)(ws + W.mtile);
   a.h_out = (_Float16 *)(ws + W.h);
   a.partial = (_Float16 *)(ws + W.partial);
-  a.flags = (uint32_t *)(ws + W.flags);
+  a.flags = P.flags;
   a.tiles = 0;
   return a;
 }
