@@ -235,6 +235,34 @@ mq_status moe_quant_router_logits(const uint16_t *hidden_bf16, const uint16_t *r
                                   int64_t num_tokens, int32_t hidden, int32_t num_experts,
                                   float *logits_f32, struct ihipStream_t *stream);
 
+/*
+ * Allocation-free variant of moe_quant_forward, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  It runs the same kernels; their scratch
+ * (routing tables, the FP16 intermediate and the per-slot partials) lives in
+ * a static device array inside the library, MOE_QUANT_NOALLOC_SCRATCH_BYTES
+ * per GPU, held by each GPU the library runs on until the process ends.  No
+ * hipMalloc, hipFree or allocating library routine is called.
+ *   router_logits, hidden_bf16, residual_bf16, num_tokens, out_bf16, stream:
+ *                  as for moe_quant_forward
+ *   overflow_flag  NULL, or a caller-owned device uint32 (4-byte aligned):
+ *                  set to 0 at the start of the call and to 1 if an FP16
+ *                  intermediate saturated (read it after the stream syncs)
+ * Every call on one GPU shares that GPU's array and leaves its contents
+ * behind: calls that overlap on one GPU (different streams, or host threads
+ * without ordering between them) race on it and must not be issued.
+ * Errors: as moe_quant_forward, plus MQ_E_WORKSPACE when the batch needs more
+ * scratch than the array holds (moe_quant_workspace_size(L, T) above
+ * MOE_QUANT_NOALLOC_SCRATCH_BYTES; about 1350 tokens at hidden 2048,
+ * intermediate 768, 128 experts, top-8), checked before anything is enqueued.
+ */
+#define MOE_QUANT_NOALLOC_SCRATCH_BYTES (64u << 20)
+mq_status moe_quant_forward_noalloc(const mq_layer *L, const void *router_logits,
+                                    int32_t logits_dtype, const uint16_t *hidden_bf16,
+                                    const uint16_t *residual_bf16, int64_t num_tokens,
+                                    uint16_t *out_bf16, uint32_t *overflow_flag,
+                                    struct ihipStream_t *stream);
+
 void moe_quant_destroy(mq_layer *L);
 
 /* Static strings; never NULL. */

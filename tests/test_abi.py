@@ -153,6 +153,28 @@ def test_forward_rejects_before_any_launch(lib):
     lib.moe_quant_destroy(h)
 
 
+def test_forward_noalloc_rejects_before_any_launch(lib):
+    """The allocation-free forward checks its arguments and the scratch bound
+    on the host before it touches the GPU."""
+    st, h = _init(lib, _desc(1, e=128, h=2048, i=768, k=8))
+    assert st == MQ_OK
+    P = 0x100000
+    f = lib.moe_quant_forward_noalloc
+    assert f(None, P, 0, P, None, 64, P, None, None) == MQ_E_NULL
+    assert f(h, P, 0, P, None, -1, P, None, None) == MQ_E_SHAPE
+    assert f(h, None, 0, None, None, 0, None, None, None) == MQ_OK        # T = 0: nothing to do
+    assert f(h, P, 0, P, None, 64, P, P + 2, None) == MQ_E_ALIGN         # overflow flag
+    # 4096 tokens need ~200 MiB of scratch, above the static 64 MiB
+    assert f(h, P, 0, P, None, 4096, P, None, None) == MQ_E_WORKSPACE
+    assert b"64" in lib.moe_quant_last_error() or b"scratch" in lib.moe_quant_last_error()
+    n = ctypes.c_size_t()
+    assert lib.moe_quant_workspace_size(h, 1300, ctypes.byref(n)) == MQ_OK
+    assert n.value <= 64 << 20          # the documented capacity: ~1350 tokens at this shape
+    assert lib.moe_quant_workspace_size(h, 1400, ctypes.byref(n)) == MQ_OK
+    assert n.value > 64 << 20
+    lib.moe_quant_destroy(h)
+
+
 def test_dequantize_rejects(lib):
     st, h = _init(lib, _desc(2))
     assert st == MQ_OK

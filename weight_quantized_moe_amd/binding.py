@@ -21,6 +21,7 @@ EXPORTED = (
     "moe_quant_init",
     "moe_quant_workspace_size",
     "moe_quant_forward",
+    "moe_quant_forward_noalloc",
     "moe_quant_check",
     "moe_quant_dequantize",
     "moe_quant_router_logits",
@@ -90,6 +91,8 @@ def load_library():
     lib.moe_quant_forward.argtypes = [vp, vp, i32, vp, vp, i64, vp, vp, sz,
                                       ctypes.POINTER(Probe), vp]
     lib.moe_quant_forward.restype = i32
+    lib.moe_quant_forward_noalloc.argtypes = [vp, vp, i32, vp, vp, i64, vp, vp, vp]
+    lib.moe_quant_forward_noalloc.restype = i32
     lib.moe_quant_check.argtypes = [vp, vp, vp]
     lib.moe_quant_check.restype = i32
     lib.moe_quant_dequantize.argtypes = [vp, i32, i32, vp, vp]
@@ -293,6 +296,35 @@ class Layer:
             self._h, _ptr(logits), ldt, _ptr(hidden), _ptr(residual), t, _ptr(out),
             _ptr(workspace), _nbytes(workspace), ctypes.byref(pr) if pr is not None else None,
             _stream(stream))
+        _check(self._lib, st)
+        return out
+
+    def forward_noalloc(self, logits, hidden, residual=None, out=None, overflow_flag=None,
+                        stream=None):
+        """Enqueue one forward whose scratch is the library's static device
+        array (moe_quant_forward_noalloc); ``overflow_flag``: None or an int32
+        tensor of one element that receives the saturation flag."""
+        import torch
+        if hidden.dim() != 2:
+            raise ValueError("hidden must be [T, H]")
+        t = hidden.shape[0]
+        dev = self.device
+        bf16 = (torch.bfloat16,)
+        _need(hidden, "hidden", (t, self.hidden), bf16)
+        _need(logits, "logits", (t, self.num_experts), (torch.float32, torch.bfloat16))
+        if residual is not None:
+            _need(residual, "residual", (t, self.hidden), bf16)
+        if out is None:
+            out = torch.empty((t, self.hidden), dtype=torch.bfloat16, device=dev)
+        _need(out, "out", (t, self.hidden), bf16)
+        if overflow_flag is not None:
+            _need(overflow_flag, "overflow_flag", (1,), (torch.int32,))
+        _on_gpu(dev, hidden=hidden, logits=logits, residual=residual, out=out,
+                overflow_flag=overflow_flag)
+        ldt = MQ_F32 if logits.dtype == torch.float32 else MQ_BF16
+        st = self._lib.moe_quant_forward_noalloc(
+            self._h, _ptr(logits), ldt, _ptr(hidden), _ptr(residual), t, _ptr(out),
+            _ptr(overflow_flag), _stream(stream))
         _check(self._lib, st)
         return out
 

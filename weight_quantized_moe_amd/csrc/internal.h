@@ -1,6 +1,8 @@
 // Internal declarations shared by the host ABI and the kernel launchers.
 #pragma once
 #include <hip/hip_runtime.h>
+
+#include "../../include/moe_quant.h"
 #include <stddef.h>
 #include <stdint.h>
 
@@ -81,6 +83,7 @@ struct FwdPtrs {
   const uint16_t *residual;
   uint16_t *out;
   char *ws;
+  uint32_t *flags;  // saturation flag word (the workspace's first word, or the caller's)
   int T;
   // probe outputs (may be null)
   int32_t *p_ids, *p_offsets, *p_sorted_tok, *p_inv;
@@ -107,6 +110,21 @@ hipError_t launch_combine(const LayerDims &L, const FwdPtrs &P, const Workspace 
 hipError_t launch_dequantize(const LayerDims &L, int which, int expert, float *out, hipStream_t s);
 hipError_t launch_router_logits(const uint16_t *x, const uint16_t *w, float *out, int64_t T, int H,
                                 int E, hipStream_t s);
+
+// The forward path behind moe_quant_forward and its allocation-free variant:
+// host checks, then the launch sequence on `stream`.  `flags` (nullable) is
+// the saturation word to use instead of the workspace's first word.
+mq_status forward_impl(const mq_layer *L, const void *router_logits, int32_t logits_dtype,
+                       const uint16_t *hidden_bf16, const uint16_t *residual_bf16,
+                       int64_t num_tokens, uint16_t *out_bf16, void *workspace,
+                       size_t workspace_bytes, const mq_probe *probe, uint32_t *flags,
+                       hipStream_t stream);
+// Record a status and its one-line explanation for moe_quant_last_error().
+mq_status fail(mq_status s, const char *fmt, ...);
+void clear_error();
+// Bytes of workspace one forward over T tokens needs for layer L.
+size_t workspace_bytes(const mq_layer *L, int64_t T);
+constexpr int64_t kMaxTokens = 1 << 22;
 
 // Rows per expert at or below which the decode (weight-streaming) GEMMs run.
 bool use_decode_path(int64_t T, int E, int k, int H, int I);

@@ -18,6 +18,14 @@ namespace {
 
 thread_local char g_err[512] = "";
 
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+namespace mq {
+
 mq_status fail(mq_status s, const char *fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
@@ -26,15 +34,7 @@ mq_status fail(mq_status s, const char *fmt, ...) {
   return s;
 }
 
-bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
-
-size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-constexpr int64_t kMaxTokens = 1 << 22;
-
-}  // namespace
-
-namespace mq {
+void clear_error() { g_err[0] = 0; }
 
 Workspace workspace_layout(int64_t T, int E, int H, int I, int k) {
   Workspace w{};
@@ -63,7 +63,15 @@ Workspace workspace_layout(int64_t T, int E, int H, int I, int k) {
   return w;
 }
 
+size_t workspace_bytes(const mq_layer *L, int64_t T) {
+  const mq_layer_desc &d = L->d;
+  return workspace_layout(T, d.num_experts, d.hidden, d.intermediate, d.top_k).total;
+}
+
 }  // namespace mq
+
+using mq::fail;
+using mq::kMaxTokens;
 
 extern "C" {
 
@@ -135,8 +143,7 @@ mq_status moe_quant_workspace_size(const mq_layer *L, int64_t num_tokens, size_t
   if (num_tokens < 0 || num_tokens > kMaxTokens)
     return fail(MQ_E_SHAPE, "workspace_size: num_tokens %lld outside [0, %lld]",
                 (long long)num_tokens, (long long)kMaxTokens);
-  const mq_layer_desc &d = L->d;
-  *bytes = mq::workspace_layout(num_tokens, d.num_experts, d.hidden, d.intermediate, d.top_k).total;
+  *bytes = mq::workspace_bytes(L, num_tokens);
   return MQ_OK;
 }
 
@@ -155,6 +162,17 @@ mq_status moe_quant_forward(const mq_layer *L, const void *router_logits, int32_
                             int64_t num_tokens, uint16_t *out_bf16, void *workspace,
                             size_t workspace_bytes, const mq_probe *probe,
                             struct ihipStream_t *stream) {
+  return mq::forward_impl(L, router_logits, logits_dtype, hidden_bf16, residual_bf16, num_tokens,
+                          out_bf16, workspace, workspace_bytes, probe, nullptr, (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+mq_status mq::forward_impl(const mq_layer *L, const void *router_logits, int32_t logits_dtype,
+                           const uint16_t *hidden_bf16, const uint16_t *residual_bf16,
+                           int64_t num_tokens, uint16_t *out_bf16, void *workspace,
+                           size_t workspace_bytes, const mq_probe *probe, uint32_t *flags,
+                           hipStream_t stream) {
   if (!L) return fail(MQ_E_NULL, "forward: NULL layer handle");
   if (num_tokens < 0 || num_tokens > kMaxTokens)
     return fail(MQ_E_SHAPE, "forward: num_tokens %lld outside [0, %lld]", (long long)num_tokens,
@@ -190,6 +208,7 @@ mq_status moe_quant_forward(const mq_layer *L, const void *router_logits, int32_
   P.residual = residual_bf16;
   P.out = out_bf16;
   P.ws = (char *)workspace;
+  P.flags = flags ? flags : (uint32_t *)(P.ws + W.flags);
   P.T = (int)num_tokens;
   if (probe) {
     P.p_ids = probe->topk_ids;
@@ -199,7 +218,7 @@ mq_status moe_quant_forward(const mq_layer *L, const void *router_logits, int32_
     P.p_inv = probe->inv_pos;
     P.p_h = probe->h;
   }
-  hipStream_t s = (hipStream_t)stream;
+  hipStream_t s = stream;
   const bool decode = mq::use_decode_path(num_tokens, D.E, D.k, D.H, D.I);
   auto ev = [&](int stage, int after) {
     if (probe && probe->events[2 * stage + after])
@@ -240,6 +259,8 @@ mq_status moe_quant_forward(const mq_layer *L, const void *router_logits, int32_
   g_err[0] = 0;
   return MQ_OK;
 }
+
+extern "C" {
 
 mq_status moe_quant_check(const mq_layer *L, const void *workspace, struct ihipStream_t *stream) {
   if (!L || !workspace) return fail(MQ_E_NULL, "check: NULL argument");

@@ -494,7 +494,7 @@ static hipError_t route_dispatch(const LayerDims &L, const FwdPtrs &P, const Wor
   hipLaunchKernelGGL((route_kernel<kPer, kBf16, kPerm>), dim3((P.T + tpb - 1) / tpb), dim3(threads), 0, s,
                      P.logits, P.hidden, P.T, L.E, L.H, L.k, (int32_t *)(ws + W.topk_ids),
                      (float *)(ws + W.topk_w), (_Float16 *)(ws + W.x16), (float *)(ws + W.rowscale),
-                     (uint32_t *)(ws + W.flags), P.p_ids, P.p_w, stage_rows);
+                     P.flags, P.p_ids, P.p_w, stage_rows);
   return hipGetLastError();
 }
 
