@@ -18,6 +18,9 @@ Zipf-skewed routing (the prefill regime, bound by the matrix units).  Beside it:
   per-step times with the weights cycled through the sets, with one set
   repeated (warm caches) and after a 1 GiB flush (cold caches), plus the
   decode batches replayed from a captured HIP graph;
+* ``with_router``: the decode (64 tokens) and FP8 prefill layers driven from the
+  BF16 gate's weight, router GEMM and top-k fused in one kernel, against the
+  router-logits kernel followed by the logits-driven forward;
 * ``stack48``: the 48-layer stack (24 FP8 + 24 INT4 layers chained with
   residual adds) at 64 and 2048 tokens, eager and graph-captured;
 * ``cpu_baseline``: the float64 oracle on a bounded sample of the headline
@@ -269,6 +272,56 @@ def regime_line(lb, iters, flush, graph):
     return out
 
 
+def router_line(lb, iters):
+    """The layer driven from the BF16 gate's weight: moe_quant_forward_with_router
+    (router GEMM and top-k in one kernel) against the two-kernel pipeline
+    moe_quant_router_logits + moe_quant_forward, same layer, batch and weight
+    sets.  The fused routing kernel is rated against HBM: the hidden rows read
+    once, the gate read once, the top-k ids and weights written (prefill also
+    writes the FP16 rows it stages for the GEMM)."""
+    import torch
+    from weight_quantized_moe_amd import router_logits, synth
+    wl, T, dev = lb.wl, lb.T, lb.dev
+    gen = torch.Generator(device=dev).manual_seed(11)
+    gate = (torch.randn(wl.experts, wl.hidden, device=dev, generator=gen) * 0.02).to(torch.bfloat16)
+    lg = torch.empty((T, wl.experts), dtype=torch.float32, device=dev)
+
+    def fused(i, events=None):
+        lb.layers[i % lb.n_sets].forward_with_router(gate, lb.x, out=lb.out, workspace=lb.ws,
+                                                     events=events)
+
+    def unfused(i):
+        router_logits(lb.x, gate, out=lg)
+        lb.layers[i % lb.n_sets].forward(lg, lb.x, out=lb.out, workspace=lb.ws)
+
+    res = {"workload": wl.name, "tokens": T}
+    for name, fn in (("fused_us_per_step", fused), ("logits_kernel_then_forward_us_per_step", unfused)):
+        for i in range(5):
+            fn(i)
+        e0, e1 = new_events(2)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(iters):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = round(e0.elapsed_time(e1) * 1e3 / iters, 2)
+    n = min(iters, 30)
+    bev = [new_events(2 * len(STAGES)) for _ in range(n)]
+    for i in range(n):
+        fused(i, bev[i])
+    torch.cuda.synchronize()
+    route_us = sum(e[0].elapsed_time(e[1]) for e in bev) / n * 1e3
+    nbytes = T * wl.hidden * 2 + wl.experts * wl.hidden * 2 + T * wl.top_k * 8
+    if not is_decode(wl, T):
+        nbytes += T * wl.hidden * 2 + T * 4
+    res["fused_route_stage_us"] = round(route_us, 2)
+    res["fused_route_roofline"] = {"bound": "hbm", "algorithmic_bytes": nbytes,
+                                   "achieved": round(nbytes / route_us / 1e3, 1), "peak": PEAK_HBM_GBS,
+                                   "unit": "GB/s", "frac": round(nbytes / route_us / 1e3 / PEAK_HBM_GBS, 4)}
+    return res
+
+
 def stack_bench(dev, reps):
     """All 48 layers back to back (layers 0-23 FP8, 24-47 INT4, residual adds),
     eager and replayed from one captured HIP graph, at 64 and 2048 tokens."""
@@ -501,6 +554,8 @@ def main():
             line = regime_line(other, args.iters, flush, graph=is_decode(other.wl, T2))
             res["regimes"].append(line)
             print(f"# {name} T={T2}: {line['us_per_step']} us/step", file=sys.stderr, flush=True)
+            if T2 in (64, 4096):
+                res.setdefault("with_router", []).append(router_line(other, args.iters))
             prev = other
         del prev, other
     if not args.no_stack:

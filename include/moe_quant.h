@@ -20,8 +20,10 @@
  * W13[e] is [2I, H], W2[e] is [H, I]; both are stored per expert, stacked over
  * experts, row major with the input dimension K contiguous, in one of three
  * packed formats (see mq_wformat).  The router itself is not part of the
- * library: it stays a BF16 linear layer on every card ("clef-omni-int4" card,
- * section "Recipe": ignore_layers=mlp.gate); its logits are an input.
+ * path: it stays a BF16 linear layer on every card ("clef-omni-int4" card,
+ * section "Recipe": ignore_layers=mlp.gate); moe_quant_forward takes its
+ * logits as an input, and moe_quant_forward_with_router computes them from
+ * the gate's weight in the same kernel as the top-k.
  *
  * Conventions shared by every entry point:
  *  - All tensor pointers are DEVICE pointers, owned by the caller, row major
@@ -194,6 +196,35 @@ mq_status moe_quant_forward(const mq_layer *L, const void *router_logits, int32_
                             int64_t num_tokens, uint16_t *out_bf16, void *workspace,
                             size_t workspace_bytes, const mq_probe *probe,
                             struct ihipStream_t *stream);
+
+/*
+ * moe_quant_forward with the router in the library: the logits of the BF16
+ * gate that stays unquantized on every card ("clef-omni-int4" card, section
+ * "Recipe": ignore_layers=mlp.gate; "clef-omni-NVFP4" card, section "How it
+ * was made": the router is copied unchanged), read as a linear layer without
+ * bias, logits[t, e] = sum_h hidden[t, h] * router[e, h], are computed and
+ * selected in one kernel from 4096 tokens up: each block of 16 or 32 tokens
+ * keeps its FP32 logits on chip and runs the top-k there (same order, ties
+ * and weights as moe_quant_forward).  Smaller batches run the router logits
+ * kernel into the workspace and then the logits-driven routing kernel, which
+ * is faster there.  The rest of the path is moe_quant_forward's.
+ *   hidden_bf16   [T, H] BF16 bits, 16-byte aligned
+ *   router_bf16   [E, H] BF16 bits (the gate's weight), 16-byte aligned
+ *   residual_bf16, num_tokens, out_bf16, workspace, workspace_bytes, probe,
+ *   stream        as for moe_quant_forward (same workspace size)
+ *   logits_out    NULL, or float [T, E] (4-byte aligned): receives the FP32
+ *                 logits the top-k decided on (for tests)
+ * Products are exact in FP32 and summed in FP32 by the matrix units in a fixed
+ * order, so repeated calls are bit-identical.  E at most 256.
+ * Errors: as moe_quant_forward (MQ_E_NULL when router_bf16 is NULL,
+ * MQ_E_SHAPE when E > 256).
+ */
+mq_status moe_quant_forward_with_router(const mq_layer *L, const uint16_t *hidden_bf16,
+                                        const uint16_t *router_bf16,
+                                        const uint16_t *residual_bf16, int64_t num_tokens,
+                                        uint16_t *out_bf16, void *workspace,
+                                        size_t workspace_bytes, float *logits_out,
+                                        const mq_probe *probe, struct ihipStream_t *stream);
 
 /*
  * Synchronize `stream` and report whether the last forward that used

@@ -175,6 +175,26 @@ def test_forward_noalloc_rejects_before_any_launch(lib):
     lib.moe_quant_destroy(h)
 
 
+def test_forward_with_router_rejects_before_any_launch(lib):
+    P = 0x100000
+    f = lib.moe_quant_forward_with_router
+    st, h = _init(lib, _desc(1, e=128, h=2048, i=768, k=8))
+    assert st == MQ_OK
+    n = ctypes.c_size_t()
+    lib.moe_quant_workspace_size(h, 64, ctypes.byref(n))
+    ws = n.value
+    assert f(h, P, None, None, 64, P, P + 0x100000, ws, None, None, None) == MQ_E_NULL   # no router
+    assert f(h, P, P + 8, None, 64, P, P + 0x100000, ws, None, None, None) == MQ_E_ALIGN
+    assert f(h, P, P, None, 64, P, P + 0x100000, ws - 1, None, None, None) == MQ_E_WORKSPACE
+    assert f(h, P, P, None, 64, P, P + 0x100000, ws, P + 2, None, None) == MQ_E_ALIGN    # logits_out
+    assert f(h, P, P, None, 0, P, None, 0, None, None, None) == MQ_OK                     # T = 0
+    lib.moe_quant_destroy(h)
+    st, h = _init(lib, _desc(1, e=300, k=8))          # more experts than the fused router holds
+    assert st == MQ_OK
+    assert f(h, P, P, None, 4, P, P + 0x100000, 1 << 30, None, None, None) == MQ_E_SHAPE
+    lib.moe_quant_destroy(h)
+
+
 def test_dequantize_rejects(lib):
     st, h = _init(lib, _desc(2))
     assert st == MQ_OK

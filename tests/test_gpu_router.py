@@ -93,3 +93,77 @@ def test_router_feeds_the_layer():
     out, pr, ovf = g.run(lg, x, probe=True)
     check_routing(pr, lg, k, E)
     assert not ovf
+
+
+# ------------------------------------------------------------ router fused with the top-k
+
+def _fused(g, x_bits, w_bits, res_bits=None):
+    """moe_quant_forward_with_router with every probe output."""
+    import torch
+    lay = g.layer
+    T, E, k, I = x_bits.shape[0], lay.num_experts, lay.top_k, lay.inter
+    x = dev(x_bits.view(np.int16)).view(torch.bfloat16)
+    w = dev(w_bits.view(np.int16)).view(torch.bfloat16)
+    res = dev(res_bits.view(np.int16)).view(torch.bfloat16) if res_bits is not None else None
+    lg = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    pr = dict(topk_ids=torch.empty((T, k), dtype=torch.int32, device="cuda"),
+              topk_w=torch.empty((T, k), dtype=torch.float32, device="cuda"),
+              expert_offsets=torch.empty(E + 1, dtype=torch.int32, device="cuda"),
+              sorted_token_ids=torch.empty(T * k, dtype=torch.int32, device="cuda"),
+              inv_pos=torch.empty(T * k, dtype=torch.int32, device="cuda"))
+    ws = lay.workspace(T)
+    out = lay.forward_with_router(w, x, residual=res, workspace=ws, logits_out=lg, probe=pr)
+    torch.cuda.synchronize()
+    assert not lay.check(ws)
+    return (out.view(torch.int16).cpu().numpy().view(np.uint16), lg.cpu().numpy(),
+            {n: v.cpu().numpy() for n, v in pr.items()})
+
+
+def _check_fused(g, x, w, tag, res=None):
+    from gpu_helpers import ATOL_MAX, RTOL_L2, errors
+    out, lg, pr = _fused(g, x, w, res)
+    # the logits the top-k decided on: within the FP32 summation bound
+    H = x.shape[1]
+    u = 2.0 ** -23
+    gamma = H * u / (1 - H * u)
+    ref_lg = moe.router_logits(x, w)
+    bound = gamma * (np.abs(moe.bf16_bits_to_f64(x)) @ np.abs(moe.bf16_bits_to_f64(w)).T)
+    assert np.all(np.abs(lg.astype(np.float64) - ref_lg) <= bound), tag
+    # routing and grouping bit-exact against the oracle's top-k of those logits
+    check_routing(pr, lg, g.top_k, g.layer.num_experts)
+    y, _, _ = moe.moe_forward(g.oracle, lg, x, res)
+    rel, mx = errors(out, y)
+    log(f"    {tag}: rel_l2={rel:.3e} max_abs={mx:.3e}")
+    assert rel <= RTOL_L2 and mx <= ATOL_MAX, tag
+    return out, lg
+
+
+@pytest.mark.parametrize("T,E,k,fmt", [
+    # below 4096 tokens: router logits kernel into the workspace, then routing
+    (1, 128, 8, "int4_g128"), (37, 128, 8, "fp8_b128"), (64, 128, 8, "nvfp4_g16"),
+    (300, 8, 2, "int4_g128"), (700, 200, 6, "fp8_b128"),
+    # the fused router + top-k kernel: 16-token blocks up to 8192 tokens, 32
+    # above; ragged token blocks and expert groups, E from 8 to 256
+    (4096, 128, 8, "int4_g128"), (4099, 200, 6, "fp8_b128"), (4111, 40, 5, "nvfp4_g16"),
+    (5000, 8, 2, "int4_g128"), (8193, 256, 8, "nvfp4_g16"), (9000, 32, 4, "fp8_b128")])
+def test_forward_with_router(T, E, k, fmt):
+    """Routing from the gate's weight on the decode (T*k <= 16 E) and the
+    prefill paths, with ragged token blocks (T not a multiple of 16 or 32) and
+    expert groups (E not a multiple of 32)."""
+    log(f"[router+topk] T={T} E={E} k={k} {fmt}")
+    H, I = 256, 128
+    g = GpuLayer(*quantized_layer(fmt, 35, E, E, H, I), k)
+    x = synth.hidden_bf16(36, T, T, H)
+    res = synth.residual_bf16(36, T, T, H) if T % 2 else None
+    out, lg = _check_fused(g, x, _gate(37 + E, E, H), f"T={T} E={E}", res)
+    out2, lg2, _ = _fused(g, x, _gate(37 + E, E, H), res)
+    assert np.array_equal(out, out2) and np.array_equal(lg, lg2), "repeat run differs"
+
+
+def test_forward_with_router_full_shape():
+    """The prefill workload's shape (hidden 2048, intermediate 768, 128
+    experts, top-8, FP8, 4096 tokens), every token compared."""
+    log("[router+topk] full shape T=4096 fp8")
+    E, H, I, k, T = 128, 2048, 768, 8, 4096
+    g = GpuLayer(*quantized_layer("fp8_b128", 3, 0, E, H, I), k)
+    _check_fused(g, synth.hidden_bf16(38, 0, T, H), _gate(39, E, H), "full shape")

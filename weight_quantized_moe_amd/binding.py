@@ -22,6 +22,7 @@ EXPORTED = (
     "moe_quant_workspace_size",
     "moe_quant_forward",
     "moe_quant_forward_noalloc",
+    "moe_quant_forward_with_router",
     "moe_quant_check",
     "moe_quant_dequantize",
     "moe_quant_router_logits",
@@ -93,6 +94,9 @@ def load_library():
     lib.moe_quant_forward.restype = i32
     lib.moe_quant_forward_noalloc.argtypes = [vp, vp, i32, vp, vp, i64, vp, vp, vp]
     lib.moe_quant_forward_noalloc.restype = i32
+    lib.moe_quant_forward_with_router.argtypes = [vp, vp, vp, vp, i64, vp, vp, sz, vp,
+                                                  ctypes.POINTER(Probe), vp]
+    lib.moe_quant_forward_with_router.restype = i32
     lib.moe_quant_check.argtypes = [vp, vp, vp]
     lib.moe_quant_check.restype = i32
     lib.moe_quant_dequantize.argtypes = [vp, i32, i32, vp, vp]
@@ -249,7 +253,21 @@ class Layer:
 
     def forward(self, logits, hidden, residual=None, out=None, workspace=None,
                 probe: Optional[Dict] = None, events=None, stream=None):
-        """Enqueue one forward; returns ``out`` (bfloat16 [T, H])."""
+        """Enqueue one forward from router logits; returns ``out`` (bfloat16 [T, H])."""
+        return self._forward(logits, None, hidden, residual, out, workspace, probe, events,
+                             stream, None)
+
+    def forward_with_router(self, router_w, hidden, residual=None, out=None, workspace=None,
+                            logits_out=None, probe: Optional[Dict] = None, events=None,
+                            stream=None):
+        """Enqueue one forward whose router logits (BF16 gate ``router_w`` [E, H])
+        are computed in the same kernel as the top-k; ``logits_out`` (float32
+        [T, E]) optionally receives them."""
+        return self._forward(None, router_w, hidden, residual, out, workspace, probe, events,
+                             stream, logits_out)
+
+    def _forward(self, logits, router_w, hidden, residual, out, workspace, probe, events, stream,
+                 logits_out):
         import torch
         if hidden.dim() != 2:
             raise ValueError("hidden must be [T, H]")
@@ -257,7 +275,12 @@ class Layer:
         dev = self.device
         bf16 = (torch.bfloat16,)
         _need(hidden, "hidden", (t, self.hidden), bf16)
-        _need(logits, "logits", (t, self.num_experts), (torch.float32, torch.bfloat16))
+        if router_w is None:
+            _need(logits, "logits", (t, self.num_experts), (torch.float32, torch.bfloat16))
+        else:
+            _need(router_w, "router_w", (self.num_experts, self.hidden), bf16)
+            if logits_out is not None:
+                _need(logits_out, "logits_out", (t, self.num_experts), (torch.float32,))
         if residual is not None:
             _need(residual, "residual", (t, self.hidden), bf16)
         if out is None:
@@ -275,14 +298,14 @@ class Layer:
                 _need(v, f"probe[{name!r}]", shapes[name][0], (shapes[name][1],))
         if workspace is not None and not workspace.is_contiguous():
             raise ValueError("workspace must be contiguous")
-        _on_gpu(dev, hidden=hidden, logits=logits, residual=residual, out=out, workspace=workspace,
+        _on_gpu(dev, hidden=hidden, logits=logits, router_w=router_w, residual=residual, out=out,
+                workspace=workspace, logits_out=logits_out,
                 **{f"probe[{n!r}]": v for n, v in (probe or {}).items()})
         if workspace is None:
             workspace = self.workspace(t, dev)
         if t > 0 and _nbytes(workspace) < self.workspace_size(t):   # T = 0 enqueues nothing
             raise ValueError(f"workspace holds {_nbytes(workspace)} bytes, "
                              f"{self.workspace_size(t)} needed for {t} tokens")
-        ldt = MQ_F32 if logits.dtype == torch.float32 else MQ_BF16
         pr = None
         if probe is not None or events is not None:
             pr = Probe()
@@ -292,10 +315,16 @@ class Layer:
             if events is not None:
                 for i, ev in enumerate(events):
                     pr.events[i] = None if ev is None else ev.cuda_event
-        st = self._lib.moe_quant_forward(
-            self._h, _ptr(logits), ldt, _ptr(hidden), _ptr(residual), t, _ptr(out),
-            _ptr(workspace), _nbytes(workspace), ctypes.byref(pr) if pr is not None else None,
-            _stream(stream))
+        prp = ctypes.byref(pr) if pr is not None else None
+        if router_w is None:
+            ldt = MQ_F32 if logits.dtype == torch.float32 else MQ_BF16
+            st = self._lib.moe_quant_forward(
+                self._h, _ptr(logits), ldt, _ptr(hidden), _ptr(residual), t, _ptr(out),
+                _ptr(workspace), _nbytes(workspace), prp, _stream(stream))
+        else:
+            st = self._lib.moe_quant_forward_with_router(
+                self._h, _ptr(hidden), _ptr(router_w), _ptr(residual), t, _ptr(out),
+                _ptr(workspace), _nbytes(workspace), _ptr(logits_out), prp, _stream(stream))
         _check(self._lib, st)
         return out
 

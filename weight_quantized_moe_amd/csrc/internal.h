@@ -9,6 +9,12 @@
 namespace mq {
 
 constexpr int kMaxExperts = 512;
+constexpr int kMaxGateExperts = 256;  // experts the fused router + top-k kernel holds in LDS
+// Batches of at least this many tokens route from the gate's weight with the
+// fused router + top-k kernel; smaller ones run the router-logits kernel into
+// the workspace, then the routing kernel (measured faster there: the fused
+// kernel's block runs its GEMM, top-k and row staging back to back).
+constexpr int64_t kGateFusedMinT = 4096;
 constexpr int kPrefillBM = 128;  // token rows per prefill M-tile
 constexpr int kMaxChunks = 256;  // token chunks of the grouping for T > 64
 // Hidden rows of at most this many values are read whole into the registers
@@ -60,6 +66,7 @@ struct Workspace {
   size_t inv_pos;              // int32 [R]
   size_t x16;                  // fp16 [T, H]: hidden rows scaled by 2^-s_t (INT4: k order of the unpack)
   size_t rowscale;             // float [T]: 2^s_t
+  size_t logits;               // float [T, E]: router logits computed in-library (small batches)
   size_t h;                    // fp16 [R, I]
   size_t partial;              // fp16 [R, H]: routing-weighted expert outputs per slot
   size_t chunks;               // int32 [kMaxChunks, E]: per-chunk expert counts, then bases
@@ -79,6 +86,8 @@ struct LayerDims {
 struct FwdPtrs {
   const void *logits;
   int logits_bf16;
+  const uint16_t *gate_w;  // BF16 router weight [E, H]: logits computed in-library (else null)
+  float *p_logits;         // probe: the in-library logits [T, E] (may be null)
   const uint16_t *hidden;
   const uint16_t *residual;
   uint16_t *out;
@@ -118,7 +127,8 @@ mq_status forward_impl(const mq_layer *L, const void *router_logits, int32_t log
                        const uint16_t *hidden_bf16, const uint16_t *residual_bf16,
                        int64_t num_tokens, uint16_t *out_bf16, void *workspace,
                        size_t workspace_bytes, const mq_probe *probe, uint32_t *flags,
-                       hipStream_t stream);
+                       hipStream_t stream, const uint16_t *gate_w = nullptr,
+                       float *logits_out = nullptr);
 // Record a status and its one-line explanation for moe_quant_last_error().
 mq_status fail(mq_status s, const char *fmt, ...);
 void clear_error();

@@ -57,6 +57,7 @@ Workspace workspace_layout(int64_t T, int E, int H, int I, int k) {
   w.chunks = take((size_t)mq::kMaxChunks * E * 4);
   w.x16 = take((size_t)T * H * 2);
   w.rowscale = take((size_t)T * 4);
+  w.logits = take((size_t)T * E * 4);
   w.h = take(R * (size_t)I * 2);
   w.partial = take(R * (size_t)H * 2);
   w.total = o;
@@ -172,22 +173,26 @@ mq_status mq::forward_impl(const mq_layer *L, const void *router_logits, int32_t
                            const uint16_t *hidden_bf16, const uint16_t *residual_bf16,
                            int64_t num_tokens, uint16_t *out_bf16, void *workspace,
                            size_t workspace_bytes, const mq_probe *probe, uint32_t *flags,
-                           hipStream_t stream) {
+                           hipStream_t stream, const uint16_t *gate_w, float *logits_out) {
   if (!L) return fail(MQ_E_NULL, "forward: NULL layer handle");
   if (num_tokens < 0 || num_tokens > kMaxTokens)
     return fail(MQ_E_SHAPE, "forward: num_tokens %lld outside [0, %lld]", (long long)num_tokens,
                 (long long)kMaxTokens);
-  if (logits_dtype != MQ_F32 && logits_dtype != MQ_BF16)
+  if (!gate_w && logits_dtype != MQ_F32 && logits_dtype != MQ_BF16)
     return fail(MQ_E_DTYPE, "forward: unknown logits dtype %d", logits_dtype);
+  if (gate_w && L->d.num_experts > mq::kMaxGateExperts)
+    return fail(MQ_E_SHAPE, "forward_with_router: %d experts, the fused router holds at most %d",
+                L->d.num_experts, mq::kMaxGateExperts);
   if (num_tokens == 0) {
     g_err[0] = 0;
     return MQ_OK;
   }
-  if (!router_logits || !hidden_bf16 || !out_bf16)
-    return fail(MQ_E_NULL, "forward: logits, hidden and out must be non-NULL");
-  if (!aligned(router_logits, 16) || !aligned(hidden_bf16, 16) || !aligned(out_bf16, 16) ||
-      (residual_bf16 && !aligned(residual_bf16, 16)))
-    return fail(MQ_E_ALIGN, "forward: logits/hidden/residual/out must be 16-byte aligned");
+  if ((!gate_w && !router_logits) || !hidden_bf16 || !out_bf16)
+    return fail(MQ_E_NULL, "forward: logits (or the router weight), hidden and out must be non-NULL");
+  if ((!gate_w && !aligned(router_logits, 16)) || (gate_w && !aligned(gate_w, 16)) ||
+      !aligned(hidden_bf16, 16) || !aligned(out_bf16, 16) ||
+      (residual_bf16 && !aligned(residual_bf16, 16)) || (logits_out && !aligned(logits_out, 4)))
+    return fail(MQ_E_ALIGN, "forward: logits/router/hidden/residual/out must be 16-byte aligned");
   const mq::LayerDims D = dims_of(L);
   const mq::Workspace W = mq::workspace_layout(num_tokens, D.E, D.H, D.I, D.k);
   if (!workspace) return fail(MQ_E_WORKSPACE, "forward: workspace is NULL");
@@ -204,6 +209,8 @@ mq_status mq::forward_impl(const mq_layer *L, const void *router_logits, int32_t
   mq::FwdPtrs P{};
   P.logits = router_logits;
   P.logits_bf16 = logits_dtype == MQ_BF16;
+  P.gate_w = gate_w;
+  P.p_logits = logits_out;
   P.hidden = hidden_bf16;
   P.residual = residual_bf16;
   P.out = out_bf16;
@@ -261,6 +268,18 @@ mq_status mq::forward_impl(const mq_layer *L, const void *router_logits, int32_t
 }
 
 extern "C" {
+
+mq_status moe_quant_forward_with_router(const mq_layer *L, const uint16_t *hidden_bf16,
+                                        const uint16_t *router_bf16,
+                                        const uint16_t *residual_bf16, int64_t num_tokens,
+                                        uint16_t *out_bf16, void *workspace,
+                                        size_t workspace_bytes, float *logits_out,
+                                        const mq_probe *probe, struct ihipStream_t *stream) {
+  if (!router_bf16) return fail(MQ_E_NULL, "forward_with_router: router weight is NULL");
+  return mq::forward_impl(L, nullptr, MQ_F32, hidden_bf16, residual_bf16, num_tokens, out_bf16,
+                          workspace, workspace_bytes, probe, nullptr, (hipStream_t)stream,
+                          router_bf16, logits_out);
+}
 
 mq_status moe_quant_check(const mq_layer *L, const void *workspace, struct ihipStream_t *stream) {
   if (!L || !workspace) return fail(MQ_E_NULL, "check: NULL argument");

@@ -11,6 +11,7 @@
 // holds E/16 keys, and each of the k rounds is a local maximum plus a 4-step
 // DPP all-reduce inside the 16-lane row.
 #include "device.h"
+#include "gate.h"
 #include "internal.h"
 
 namespace mq {
@@ -147,7 +148,7 @@ __device__ __forceinline__ void topk16(const void *__restrict__ logits, int t, i
 // values are stored in the k order of the INT4 unpack ({0,4,1,5,2,6,3,7}, see
 // unpack_int4), so INT4 GEMMs use the rows as they are.  Loads of the 4 rows
 // are issued together (kChunk per row per round trip).
-template <bool kPermInt4>
+template <bool kPermInt4, bool kWriteRows = true>
 __device__ __forceinline__ void rows_to_f16(const uint16_t *__restrict__ hidden, int t0, int T,
                                             int H, int lane, _Float16 *__restrict__ x16,
                                             float *__restrict__ rowscale) {
@@ -180,6 +181,7 @@ __device__ __forceinline__ void rows_to_f16(const uint16_t *__restrict__ hidden,
     down[r] = pow2f(-sh);
     if (lane == 0 && t0 + r < T) rowscale[t0 + r] = pow2f(sh);
   }
+  if (!kWriteRows) return;  // the power of two only (decode)
   for (int c0 = lane * 8; c0 < H; c0 += 512 * kChunk) {
     u4 v[4][kChunk];
 #pragma unroll
@@ -273,6 +275,97 @@ __global__ __launch_bounds__(256) void route_kernel(const void *__restrict__ log
   }
   if (t < T) topk16<kPer, kBf16Logits>(logits, t, E, k, li, ids, wts, p_ids, p_w);
   if (stage_rows) rows_to_f16<kPermInt4>(hidden, t0, T, H, lane, x16, rowscale);
+}
+
+// ---------------------------------------------------------------------------
+// Router GEMM fused with the top-k: the logits of the BF16 gate (read as a
+// linear layer without bias, logits[t, e] = sum_h x[t, h] w[e, h]; the router
+// stays unquantized on every card: "clef-omni-int4" card, section "Recipe";
+// "clef-omni-NVFP4" card, section "How it was made") are computed for a block
+// of 16 or 32 tokens and all E <= 32 EG experts, kept in LDS, and selected there by
+// the same 16-lanes-per-token top-k as route_kernel, while the other half of
+// the block stages the tokens' hidden rows as route_kernel does.  The logits
+// reach HBM only when the caller asks for them (p_logits).
+//   GEMM: 16 waves = EG expert groups of 32 x KS = 16 / EG slices of H; each
+//   wave computes a 32x32 partial tile (gate_tile, BF16 MFMA, FP32 sums, the
+//   next 64-wide chunk loading while one multiplies) and the KS partials of a tile are
+//   added through LDS in wave order, so repeated runs are bit-identical.  The
+//   16 waves keep enough loads in flight to stream the whole gate through
+//   each block (512 KB at 128 experts x 2048).
+// ---------------------------------------------------------------------------
+constexpr int kGateWaves = 16;
+
+template <int EG, bool kPermInt4, int TB>
+__global__ __launch_bounds__(64 * kGateWaves) void gate_route_kernel(
+    const uint16_t *__restrict__ hidden, const uint16_t *__restrict__ gate_w, int T, int E, int H,
+    int k, int32_t *__restrict__ ids, float *__restrict__ wts, _Float16 *__restrict__ x16,
+    float *__restrict__ rowscale, uint32_t *__restrict__ flags, int32_t *__restrict__ p_ids,
+    float *__restrict__ p_w, float *__restrict__ p_logits, int stage_rows) {
+  constexpr int KS = kGateWaves / EG, kPer = 2 * EG, EP = 32 * EG + 4, NB = TB / 16;
+  static_assert(KS >= 2 && (TB == 16 || TB == 32), "H slices per expert group; 16 or 32 tokens");
+  __shared__ f4 red[kGateWaves][4][64];  // partial tiles (16 floats per lane)
+  __shared__ float lg[TB][EP];           // the block's logits [token][expert]
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int ks = wave % KS, eg = wave / KS;
+  const int t0 = blockIdx.x * TB, e0 = eg * 32;
+  if (blockIdx.x == 0 && threadIdx.x == 0) flags[0] = 0u;
+  const bool live = e0 < E;  // an expert group past E still takes the barriers
+  const int nchunk = H / 64;
+  const int cb = live ? (ks * nchunk) / KS : 0, ce = live ? ((ks + 1) * nchunk) / KS : 0;
+  f4 acc[2][2];
+  gate_tile<NB>(hidden, gate_w, T, H, E, t0, e0, cb, ce, lane, acc);
+  if (ks > 0) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) red[wave][2 * a + b][lane] = acc[a][b];
+  }
+  __syncthreads();
+  if (ks == 0 && live) {
+#pragma unroll
+    for (int p = 1; p < KS; ++p)
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const f4 v = red[wave + p][2 * a + b][lane];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[a][b][i] += v[i];
+        }
+    // MFMA tile (a, b): token 16 b + l % 16, experts e0 + 16 a + 4 (l / 16) + [0, 4)
+    const int r16 = lane & 15, q16 = lane >> 4;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lg[16 * b + r16][e0 + 16 * a + 4 * q16 + i] = acc[a][b][i];
+  }
+  __syncthreads();
+  if (wave < TB / 4) {
+    // top-k of token t0 + tl on the 16 lanes of one DPP row
+    const int tl = threadIdx.x >> 4, li = threadIdx.x & 15, t = t0 + tl;
+    if (t < T) {
+      uint64_t key[kPer];
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int e = li + 16 * i;
+        key[i] = e < E ? ((uint64_t)ordered_key(lg[tl][e]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e) : 0;
+      }
+      topk16_select<kPer>(key, t, k, li, ids, wts, p_ids, p_w);
+      if (p_logits)
+        for (int e = li; e < E; e += 16) p_logits[(size_t)t * E + e] = lg[tl][e];
+    }
+  } else if (wave < TB / 2) {
+    // hidden rows of 4 tokens per wave: FP16 rows and their powers of two
+    // (prefill), the powers of two alone (decode), or nothing (decode with
+    // rows longer than kRowRegsMaxH: the GEMM scans them itself)
+    const int tr = t0 + 4 * (wave - TB / 4);
+    if (stage_rows == 1)
+      rows_to_f16<kPermInt4>(hidden, tr, T, H, lane, x16, rowscale);
+    else if (stage_rows == 2)
+      rows_to_f16<kPermInt4, false>(hidden, tr, T, H, lane, x16, rowscale);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -509,12 +602,55 @@ static hipError_t route_dispatch2(const LayerDims &L, const FwdPtrs &P, const Wo
               : route_dispatch<kPer, false, false>(L, P, W, stage_rows, s);
 }
 
+template <int EG, bool kPerm>
+static hipError_t gate_route_launch(const LayerDims &L, const FwdPtrs &P, const Workspace &W,
+                                    int stage_rows, hipStream_t s) {
+  char *ws = P.ws;
+  // 16 tokens per block up to 8192 tokens (twice the blocks: the batch then
+  // spreads over more CUs), 32 above (half the gate reads from L2)
+  if (P.T <= 8192) {
+    hipLaunchKernelGGL((gate_route_kernel<EG, kPerm, 16>), dim3((P.T + 15) / 16), dim3(64 * kGateWaves), 0, s,
+                       P.hidden, P.gate_w, P.T, L.E, L.H, L.k, (int32_t *)(ws + W.topk_ids),
+                       (float *)(ws + W.topk_w), (_Float16 *)(ws + W.x16), (float *)(ws + W.rowscale),
+                       P.flags, P.p_ids, P.p_w, P.p_logits, stage_rows);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((gate_route_kernel<EG, kPerm, 32>), dim3((P.T + 31) / 32), dim3(64 * kGateWaves), 0, s, P.hidden,
+                     P.gate_w, P.T, L.E, L.H, L.k, (int32_t *)(ws + W.topk_ids), (float *)(ws + W.topk_w),
+                     (_Float16 *)(ws + W.x16), (float *)(ws + W.rowscale), P.flags, P.p_ids, P.p_w,
+                     P.p_logits, stage_rows);
+  return hipGetLastError();
+}
+
+template <bool kPerm>
+static hipError_t gate_route_dispatch(const LayerDims &L, const FwdPtrs &P, const Workspace &W,
+                                      int stage_rows, hipStream_t s) {
+  if (L.E <= 32) return gate_route_launch<1, kPerm>(L, P, W, stage_rows, s);
+  if (L.E <= 64) return gate_route_launch<2, kPerm>(L, P, W, stage_rows, s);
+  if (L.E <= 128) return gate_route_launch<4, kPerm>(L, P, W, stage_rows, s);
+  return gate_route_launch<8, kPerm>(L, P, W, stage_rows, s);  // E <= kMaxGateExperts
+}
+
 hipError_t launch_route(const LayerDims &L, const FwdPtrs &P, const Workspace &W, bool decode,
                         hipStream_t s) {
   // prefill: FP16 rows and their scales (1); decode with H <= 2048: the
   // scales only (2), the decode gate/up GEMM converts the rows it stages;
   // larger decode rows: the GEMM finds the scales too (0)
   const int stage_rows = !decode ? 1 : L.H <= kRowRegsMaxH ? 2 : 0;
+  if (P.gate_w && P.T >= kGateFusedMinT)  // router GEMM fused with the top-k
+    return L.fmt == FMT_INT4 ? gate_route_dispatch<true>(L, P, W, stage_rows, s)
+                             : gate_route_dispatch<false>(L, P, W, stage_rows, s);
+  if (P.gate_w) {
+    // small batch: the router logits kernel, then route_kernel on its logits
+    FwdPtrs Q = P;
+    float *lg = P.p_logits ? P.p_logits : (float *)(P.ws + W.logits);
+    hipError_t e = launch_router_logits(P.hidden, P.gate_w, lg, P.T, L.H, L.E, s);
+    if (e != hipSuccess) return e;
+    Q.logits = lg;
+    Q.logits_bf16 = 0;
+    Q.gate_w = nullptr;
+    return launch_route(L, Q, W, decode, s);
+  }
   if (L.E <= 128) return route_dispatch2<8>(L, P, W, stage_rows, s);
   if (L.E <= 256) return route_dispatch2<16>(L, P, W, stage_rows, s);
   return route_dispatch2<32>(L, P, W, stage_rows, s);

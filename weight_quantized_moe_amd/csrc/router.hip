@@ -2,26 +2,20 @@
 // "What was quantized"; "clef-omni-NVFP4" card, section "How it was made"),
 // read as a linear layer without bias: logits[t, e] = sum_h x[t, h] w[e, h].
 //
-// BF16 MFMA 16x16x32 with FP32 accumulation: every product is exact in FP32
-// and only the FP32 sums round.  A block of 8 waves covers 32 TG tokens x
-// 32 EG experts; each (token group, expert group) 32x32 tile is split over KS
-// = 8 / (TG EG) waves along H, and the KS partial tiles are added through LDS
-// in wave order (the same order every run).  Below 1024 tokens TG = EG = 1,
-// KS = 8, so a decode batch still spreads over many waves; above, TG = 1,
-// EG = 2, KS = 4.  A wave's 32x32 tile is 2 x 2 MFMA tiles of 16 rows: lane l
-// feeds row l % 16 of a tile with k = 8 (l / 16) + [0, 8) of each 32-wide
-// step, so the four lanes of a row read 64 contiguous bytes per load (the
-// gate rows are the MFMA A rows, the token rows the B columns).  Rows past T
-// or E are clamped on load and never stored.
+// A block of 8 waves covers 32 TG tokens x 32 EG experts; each (token group,
+// expert group) 32x32 tile (gate_tile, BF16 MFMA with FP32 accumulation) is
+// split over KS = 8 / (TG EG) waves along H, and the KS partial tiles are
+// added through LDS in wave order (the same order every run).  Below 1024
+// tokens TG = EG = 1, KS = 8, so a decode batch still spreads over many waves;
+// above, TG = 1, EG = 2, KS = 4.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "device.h"
+#include "gate.h"
 #include "internal.h"
 
 namespace mq {
-
-typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
 
 constexpr int kRouterWaves = 8;
 
@@ -36,43 +30,11 @@ __global__ __launch_bounds__(64 * kRouterWaves) void router_logits_kernel(
   const int ks = wave % KS, tile = wave / KS;  // k slice; (token group, expert group) tile
   const int t0 = (blockIdx.x * TG + tile / EG) * 32, e0 = (blockIdx.y * EG + tile % EG) * 32;
   const bool live = t0 < T && e0 < E;  // a tile past both ends still takes the barrier
-  // MFMA 16x16x32: lane l feeds row l % 16 of a 16-row tile with k slice
-  // 8 (l / 16) + [0, 8) of each 32-wide step, so four lanes read 64 contiguous
-  // bytes of one row; the wave's 32x32 tile is 2 x 2 MFMA tiles
   const int r16 = lane & 15, q16 = lane >> 4;
-  const uint16_t *xp[2], *wp[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    xp[i] = x + (size_t)min(t0 + 16 * i + r16, T - 1) * H + 8 * q16;
-    wp[i] = w + (size_t)min(e0 + 16 * i + r16, E - 1) * H + 8 * q16;
-  }
   const int nchunk = H / 64;
   const int cb = live ? (ks * nchunk) / KS : 0, ce = live ? ((ks + 1) * nchunk) / KS : 0;
   f4 acc[2][2];  // [expert tile][token tile]
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-  for (int c = cb * 64; c < ce * 64; c += 64) {
-    u4 xa[2][2], wa[2][2];  // [tile][32-wide step]
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        xa[i][s2] = *(const u4 *)(xp[i] + c + 32 * s2);
-        wa[i][s2] = *(const u4 *)(wp[i] + c + 32 * s2);
-      }
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8, wa[a][s2]),
-                                                              __builtin_bit_cast(bf8, xa[b][s2]),
-                                                              acc[a][b], 0, 0, 0);
-  }
+  gate_tile(x, w, T, H, E, t0, e0, cb, ce, lane, acc);
   if constexpr (KS > 1) {
     if (ks > 0) {
 #pragma unroll
