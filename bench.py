@@ -21,6 +21,8 @@ Zipf-skewed routing (the prefill regime, bound by the matrix units).  Beside it:
 * ``with_router``: the decode (64 tokens) and FP8 prefill layers driven from the
   BF16 gate's weight, router GEMM and top-k fused in one kernel, against the
   router-logits kernel followed by the logits-driven forward;
+* ``import``: checkpoint import of one layer per format (FineGrainedFP8,
+  auto_gptq INT4, compressed-tensors NVFP4 source layouts), against HBM;
 * ``stack48``: the 48-layer stack (24 FP8 + 24 INT4 layers chained with
   residual adds) at 64 and 2048 tokens, eager and graph-captured;
 * ``cpu_baseline``: the float64 oracle on a bounded sample of the headline
@@ -322,6 +324,63 @@ def router_line(lb, iters):
     return res
 
 
+def import_bench(dev, reps=3):
+    """Checkpoint import of a whole layer at the Clef shape (128 experts,
+    moe_quant_import_expert per expert) from synthetic source tensors of each
+    format's checkpoint layout, rated against HBM: the source bytes read plus
+    the packed bytes written."""
+    import torch
+    from weight_quantized_moe_amd import import_expert
+    E, H, I = 128, 2048, 768
+    out = []
+    g = torch.Generator(device=dev).manual_seed(13)
+    u8 = lambda *s: torch.randint(0, 256, s, dtype=torch.uint8, device=dev, generator=g)  # noqa: E731
+    for fmt in ("fp8_b128", "int4_g128", "nvfp4_g16"):
+        kd = 1 if fmt == "fp8_b128" else 2
+        if fmt == "int4_g128":
+            dst = (u8(E, 2 * I, H // 2), torch.zeros(E, 2 * I, H // 128, dtype=torch.float16, device=dev),
+                   u8(E, H, I // 2), torch.zeros(E, H, I // 128, dtype=torch.float16, device=dev), None, None)
+
+            def src(n, k):
+                qw = u8(k // 8, n, 4).view(torch.int32).view(k // 8, n)
+                qz = torch.full((k // 128, n // 8), 0x77777777, dtype=torch.int32, device=dev)
+                return qw, qz, torch.rand(k // 128, n, device=dev, generator=g).to(torch.float16)
+        elif fmt == "fp8_b128":
+            dst = (u8(E, 2 * I, H), torch.zeros(E, 2 * I // 128, H // 128, device=dev), u8(E, H, I),
+                   torch.zeros(E, H // 128, I // 128, device=dev), None, None)
+
+            def src(n, k):
+                return u8(n, k), torch.rand(n // 128, k // 128, device=dev, generator=g)
+        else:
+            dst = (u8(E, 2 * I, H // 2), u8(E, 2 * I, H // 16), u8(E, H, I // 2), u8(E, H, I // 16),
+                   torch.ones(E, device=dev), torch.ones(E, device=dev))
+
+            def src(n, k):
+                return u8(n, k // 2), u8(n, k // 16), 2.5
+        srcs = [(src(I, H), src(I, H), src(H, I)) for _ in range(8)]   # 8 distinct source experts
+        nbytes = 2 * E * (packed_bytes(fmt, 2 * I, H) + packed_bytes(fmt, H, I))   # read + write
+        if fmt == "int4_g128":   # the zero points are read as well
+            nbytes += E * 4 * ((H // 128) * (2 * I) // 8 + (I // 128) * H // 8)
+        times = []
+        for r in range(reps + 1):
+            e0, e1 = new_events(2)
+            torch.cuda.synchronize()
+            e0.record()
+            for e in range(E):
+                sg, su, sd = srcs[e % 8]
+                import_expert(fmt, dst, e, sg, su, sd)
+            e1.record()
+            torch.cuda.synchronize()
+            if r:
+                times.append(e0.elapsed_time(e1) * 1e3)
+        us = pct(times, 0.5)
+        out.append({"format": fmt, "experts": E, "us_per_layer": round(us, 1), "bytes": nbytes,
+                    "GB_s": round(nbytes / us / 1e3, 1), "frac_of_8TB_s": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4),
+                    "launches_per_expert": 9 if fmt == "int4_g128" else (7 if fmt == "nvfp4_g16" else 6)})
+        del dst, srcs
+    return out
+
+
 def stack_bench(dev, reps):
     """All 48 layers back to back (layers 0-23 FP8, 24-47 INT4, residual adds),
     eager and replayed from one captured HIP graph, at 64 and 2048 tokens."""
@@ -558,6 +617,8 @@ def main():
                 res.setdefault("with_router", []).append(router_line(other, args.iters))
             prev = other
         del prev, other
+    res["import"] = import_bench(dev)
+    print("# import done", file=sys.stderr, flush=True)
     if not args.no_stack:
         res["stack48"] = stack_bench(dev, max(5, args.steps // 2))
         print("# stack48 done", file=sys.stderr, flush=True)

@@ -294,6 +294,53 @@ mq_status moe_quant_forward_noalloc(const mq_layer *L, const void *router_logits
                                     uint16_t *out_bf16, uint32_t *overflow_flag,
                                     struct ihipStream_t *stream);
 
+/*
+ * Checkpoint import: one expert's gate_proj, up_proj and down_proj, each in
+ * the tensor layout of the checkpoint format the model cards name for the
+ * layer's weight format, written into the packed layouts above (gate and up
+ * fused into W13, gate rows first).  Source and destination tensors are
+ * device memory owned by the caller.  Per projection (N = out_features, K =
+ * in_features: gate and up N = I, K = H; down N = H, K = I):
+ *   MQ_W_FP8_B128   FineGrainedFP8 ("clef-omni-fp8" card, section "Recipe"):
+ *                   weight = E4M3 [N, K], scale = weight_scale_inv float
+ *                   [N/128, K/128]; copied into place (the same bytes).
+ *   MQ_W_INT4_G128  auto_gptq packing ("clef-omni-int4" card, section "What
+ *                   was quantized"): weight = qweight int32 [K/8, N] (word
+ *                   [i, n] holds k = 8 i + j at bits 4 j), qzeros = int32
+ *                   [K/128, N/8] (word [g, c] holds column 8 c + j at bits
+ *                   4 j), scale = scales fp16 [K/128, N].  The stored zero
+ *                   point plus gptq_zero_offset (1 in the auto_gptq
+ *                   convention) must be 8 in every group (symmetric INT4);
+ *                   weights and scales are transposed into place.
+ *   MQ_W_NVFP4_G16  compressed-tensors NVFP4 ("clef-omni-NVFP4" card, section
+ *                   "How it was made"): weight = weight_packed uint8 [N, K/2],
+ *                   scale = weight_scale E4M3 [N, K/16], global_scale =
+ *                   weight_global_scale (host float); copied into place, and
+ *                   the global scales into w13_gscale[expert] (gate and up
+ *                   must be equal: the card's quantizer fuses them) and
+ *                   w2_gscale[expert].
+ * dst: a descriptor of the destination layer (the same checks as
+ * moe_quant_init); its weight and scale buffers are written.
+ * bad_zero_points: INT4 only, NULL or a device uint32 that is set to 1 when
+ * a group's zero point is not 8 (read it after the stream syncs; the weights
+ * of such a group cannot be represented and the import must be discarded).
+ * Asynchronous on `stream`.  Errors: the moe_quant_init errors for dst,
+ * MQ_E_NULL (a source tensor NULL), MQ_E_SHAPE (expert out of range),
+ * MQ_E_ALIGN (a source tensor not 16-byte aligned), MQ_E_FORMAT (NVFP4 gate
+ * and up global scales differ), MQ_E_HIP.
+ */
+typedef struct {
+  const void *weight;  /* see above, per format                            */
+  const void *scale;
+  const void *qzeros;  /* INT4 only; NULL for the other formats            */
+  float global_scale;  /* NVFP4 only                                        */
+} mq_src_proj;
+
+mq_status moe_quant_import_expert(const mq_layer_desc *dst, int32_t expert, const mq_src_proj *gate,
+                                  const mq_src_proj *up, const mq_src_proj *down,
+                                  int32_t gptq_zero_offset, uint32_t *bad_zero_points,
+                                  struct ihipStream_t *stream);
+
 void moe_quant_destroy(mq_layer *L);
 
 /* Static strings; never NULL. */

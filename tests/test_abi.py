@@ -195,6 +195,31 @@ def test_forward_with_router_rejects_before_any_launch(lib):
     lib.moe_quant_destroy(h)
 
 
+def test_import_expert_rejects_before_any_launch(lib):
+    from weight_quantized_moe_amd.binding import SrcProj
+    f = lib.moe_quant_import_expert
+    P = 0x100000
+    ok = SrcProj(P, P + 0x1000, P + 0x2000, 1.0)
+    for fmt in (1, 2, 3):
+        d = _desc(fmt)
+        assert f(ctypes.byref(d), 8, ctypes.byref(ok), ctypes.byref(ok), ctypes.byref(ok), 1, None, None) == MQ_E_SHAPE
+        assert f(ctypes.byref(d), -1, ctypes.byref(ok), ctypes.byref(ok), ctypes.byref(ok), 1, None, None) == MQ_E_SHAPE
+        nul = SrcProj(None, P, P, 1.0)
+        assert f(ctypes.byref(d), 0, ctypes.byref(ok), ctypes.byref(nul), ctypes.byref(ok), 1, None, None) == MQ_E_NULL
+        mis = SrcProj(P + 8, P, P, 1.0)
+        assert f(ctypes.byref(d), 0, ctypes.byref(mis), ctypes.byref(ok), ctypes.byref(ok), 1, None, None) == MQ_E_ALIGN
+        bad_desc = _desc(fmt, h=200)
+        assert f(ctypes.byref(bad_desc), 0, ctypes.byref(ok), ctypes.byref(ok), ctypes.byref(ok), 1, None, None) == MQ_E_SHAPE
+    # INT4 needs qzeros
+    noz = SrcProj(P, P, None, 0.0)
+    d = _desc(1)
+    assert f(ctypes.byref(d), 0, ctypes.byref(noz), ctypes.byref(ok), ctypes.byref(ok), 1, None, None) == MQ_E_NULL
+    # NVFP4: gate and up share W13's global scale
+    d = _desc(3)
+    g1, g2 = SrcProj(P, P, None, 2.0), SrcProj(P, P, None, 3.0)
+    assert f(ctypes.byref(d), 0, ctypes.byref(g1), ctypes.byref(g2), ctypes.byref(g1), 1, None, None) == MQ_E_FORMAT
+
+
 def test_dequantize_rejects(lib):
     st, h = _init(lib, _desc(2))
     assert st == MQ_OK

@@ -9,9 +9,11 @@ from .binding import (  # noqa: F401
     FORMATS,
     Layer,
     MoeQuantError,
+    import_expert,
     library_path,
     load_library,
     router_logits,
 )
 
-__all__ = ["FORMATS", "Layer", "MoeQuantError", "library_path", "load_library", "router_logits"]
+__all__ = ["FORMATS", "Layer", "MoeQuantError", "import_expert", "library_path", "load_library",
+           "router_logits"]

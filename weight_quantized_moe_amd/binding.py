@@ -23,6 +23,7 @@ EXPORTED = (
     "moe_quant_forward",
     "moe_quant_forward_noalloc",
     "moe_quant_forward_with_router",
+    "moe_quant_import_expert",
     "moe_quant_check",
     "moe_quant_dequantize",
     "moe_quant_router_logits",
@@ -53,6 +54,15 @@ class LayerDesc(ctypes.Structure):
         ("w2", ctypes.c_void_p),
         ("w2_scale", ctypes.c_void_p),
         ("w2_gscale", ctypes.c_void_p),
+    ]
+
+
+class SrcProj(ctypes.Structure):
+    _fields_ = [
+        ("weight", ctypes.c_void_p),
+        ("scale", ctypes.c_void_p),
+        ("qzeros", ctypes.c_void_p),
+        ("global_scale", ctypes.c_float),
     ]
 
 
@@ -97,6 +107,9 @@ def load_library():
     lib.moe_quant_forward_with_router.argtypes = [vp, vp, vp, vp, i64, vp, vp, sz, vp,
                                                   ctypes.POINTER(Probe), vp]
     lib.moe_quant_forward_with_router.restype = i32
+    lib.moe_quant_import_expert.argtypes = [ctypes.POINTER(LayerDesc), i32, ctypes.POINTER(SrcProj),
+                                            ctypes.POINTER(SrcProj), ctypes.POINTER(SrcProj), i32, vp, vp]
+    lib.moe_quant_import_expert.restype = i32
     lib.moe_quant_check.argtypes = [vp, vp, vp]
     lib.moe_quant_check.restype = i32
     lib.moe_quant_dequantize.argtypes = [vp, i32, i32, vp, vp]
@@ -183,6 +196,56 @@ def router_logits(hidden, router_w, out=None, stream=None):
     _check(lib, lib.moe_quant_router_logits(_ptr(hidden), _ptr(router_w), t, h, e, _ptr(out),
                                             _stream(stream)))
     return out
+
+
+def import_expert(fmt: str, dst, expert: int, gate, up, down, gptq_zero_offset: int = 1,
+                  bad_zero_points=None, stream=None):
+    """Write one expert's checkpoint tensors into packed layer buffers
+    (moe_quant_import_expert).  ``dst`` = (w13, w13_scale, w2, w2_scale,
+    w13_gscale, w2_gscale) GPU tensors in the library layouts (gscales None
+    except for NVFP4).  ``gate``/``up``/``down`` per format: FP8 (weight uint8
+    [N, K], weight_scale_inv float32 [N/128, K/128]); INT4 auto_gptq (qweight
+    int32 [K/8, N], qzeros int32 [K/128, N/8], scales float16 [K/128, N]);
+    NVFP4 compressed-tensors (weight_packed uint8 [N, K/2], weight_scale
+    uint8 [N, K/16], weight_global_scale float)."""
+    import torch
+    lib = load_library()
+    w13, s13, w2, s2, g13, g2 = dst
+    e, n13, _ = w13.shape
+    h = w2.shape[1]
+    i = n13 // 2
+    kdiv = 1 if fmt == "fp8_b128" else 2
+    _need(w13, "w13", (e, 2 * i, h // kdiv), (torch.uint8,))
+    _need(w2, "w2", (e, h, i // kdiv), (torch.uint8,))
+
+    def src(p, n, k, name):
+        if fmt == "fp8_b128":
+            w, s = p
+            _need(w, f"{name}.weight", (n, k), (torch.uint8,))
+            _need(s, f"{name}.weight_scale_inv", (n // 128, k // 128), (torch.float32,))
+            _on_gpu(w13.device, w=w, s=s)
+            return SrcProj(w.data_ptr(), s.data_ptr(), None, 0.0)
+        if fmt == "int4_g128":
+            qw, qz, sc = p
+            _need(qw, f"{name}.qweight", (k // 8, n), (torch.int32,))
+            _need(qz, f"{name}.qzeros", (k // 128, n // 8), (torch.int32,))
+            _need(sc, f"{name}.scales", (k // 128, n), (torch.float16,))
+            _on_gpu(w13.device, qw=qw, qz=qz, sc=sc)
+            return SrcProj(qw.data_ptr(), sc.data_ptr(), qz.data_ptr(), 0.0)
+        wp, ws, g = p
+        _need(wp, f"{name}.weight_packed", (n, k // 2), (torch.uint8,))
+        _need(ws, f"{name}.weight_scale", (n, k // 16), (torch.uint8,))
+        _on_gpu(w13.device, wp=wp, ws=ws)
+        return SrcProj(wp.data_ptr(), ws.data_ptr(), None, float(g))
+
+    sg, su, sd = src(gate, i, h, "gate_proj"), src(up, i, h, "up_proj"), src(down, h, i, "down_proj")
+    d = LayerDesc(ABI_VERSION, e, h, i, 1, FORMATS[fmt], _ptr(w13), _ptr(s13), _ptr(g13),
+                  _ptr(w2), _ptr(s2), _ptr(g2))
+    if bad_zero_points is not None:
+        _need(bad_zero_points, "bad_zero_points", (1,), (torch.int32,))
+    _check(lib, lib.moe_quant_import_expert(ctypes.byref(d), expert, ctypes.byref(sg), ctypes.byref(su),
+                                            ctypes.byref(sd), gptq_zero_offset, _ptr(bad_zero_points),
+                                            _stream(stream)))
 
 
 class Layer:

@@ -117,6 +117,9 @@ hipError_t launch_down(const LayerDims &L, const FwdPtrs &P, const Workspace &W,
                        const GemmLaunch &s);
 hipError_t launch_combine(const LayerDims &L, const FwdPtrs &P, const Workspace &W, hipStream_t s);
 hipError_t launch_dequantize(const LayerDims &L, int which, int expert, float *out, hipStream_t s);
+hipError_t launch_import_expert(const LayerDims &L, int e, const mq_src_proj &gate,
+                                const mq_src_proj &up, const mq_src_proj &down, int gptq_offset,
+                                uint32_t *bad, hipStream_t st);
 hipError_t launch_router_logits(const uint16_t *x, const uint16_t *w, float *out, int64_t T, int H,
                                 int E, hipStream_t s);
 

@@ -96,39 +96,43 @@ const char *moe_quant_status_string(mq_status s) {
   return "unknown mq_status";
 }
 
+static mq_status check_desc(const mq_layer_desc *d, const char *who) {
+  if (d->abi_version != MOE_QUANT_ABI_VERSION)
+    return fail(MQ_E_ABI, "%s: descriptor abi_version %u, library %u", who, d->abi_version,
+                MOE_QUANT_ABI_VERSION);
+  if (d->format != MQ_W_INT4_G128 && d->format != MQ_W_FP8_B128 && d->format != MQ_W_NVFP4_G16)
+    return fail(MQ_E_FORMAT, "%s: unknown weight format %d", who, d->format);
+  const int E = d->num_experts, H = d->hidden, I = d->intermediate, k = d->top_k;
+  if (E < 1 || E > mq::kMaxExperts)
+    return fail(MQ_E_SHAPE, "%s: num_experts %d outside [1, %d]", who, E, mq::kMaxExperts);
+  if (k < 1 || k > E || k > 64) return fail(MQ_E_SHAPE, "%s: top_k %d outside [1, min(E, 64)]", who, k);
+  if (H < 128 || I < 128 || H % 128 || I % 128)
+    return fail(MQ_E_SHAPE, "%s: hidden %d and intermediate %d must be positive multiples of 128 "
+                "(block sizes of INT4 g128 / FP8 128x128; this version's tiles for NVFP4)", who,
+                H, I);
+  if (!mq::decode_fits(H) || !mq::decode_fits(I))
+    return fail(MQ_E_SHAPE, "%s: hidden %d / intermediate %d above %d: the decode GEMM stages 16 whole "
+                "rows of the input dimension in LDS (160 KiB per workgroup)", who,
+                H, I, mq::kMaxGemmK);
+  if (!d->w13 || !d->w13_scale || !d->w2 || !d->w2_scale)
+    return fail(MQ_E_NULL, "%s: weight and scale pointers must be non-NULL", who);
+  if (d->format == MQ_W_NVFP4_G16 && (!d->w13_gscale || !d->w2_gscale))
+    return fail(MQ_E_NULL, "%s: NVFP4 needs w13_gscale and w2_gscale", who);
+  if (d->format != MQ_W_NVFP4_G16 && (d->w13_gscale || d->w2_gscale))
+    return fail(MQ_E_NULL, "%s: gscale pointers must be NULL for INT4 and FP8", who);
+  const void *al16[4] = {d->w13, d->w13_scale, d->w2, d->w2_scale};
+  for (const void *p : al16)
+    if (!aligned(p, 16)) return fail(MQ_E_ALIGN, "%s: weight/scale pointer %p not 16-byte aligned", who, p);
+  if ((d->w13_gscale && !aligned(d->w13_gscale, 4)) || (d->w2_gscale && !aligned(d->w2_gscale, 4)))
+    return fail(MQ_E_ALIGN, "%s: gscale pointers must be 4-byte aligned", who);
+  return MQ_OK;
+}
+
 mq_status moe_quant_init(const mq_layer_desc *d, mq_layer **out) {
   if (!d || !out) return fail(MQ_E_NULL, "init: desc and out must be non-NULL");
   *out = nullptr;
-  if (d->abi_version != MOE_QUANT_ABI_VERSION)
-    return fail(MQ_E_ABI, "init: descriptor abi_version %u, library %u", d->abi_version,
-                MOE_QUANT_ABI_VERSION);
-  if (d->format != MQ_W_INT4_G128 && d->format != MQ_W_FP8_B128 && d->format != MQ_W_NVFP4_G16)
-    return fail(MQ_E_FORMAT, "init: unknown weight format %d", d->format);
-  const int E = d->num_experts, H = d->hidden, I = d->intermediate, k = d->top_k;
-  if (E < 1 || E > mq::kMaxExperts)
-    return fail(MQ_E_SHAPE, "init: num_experts %d outside [1, %d]", E, mq::kMaxExperts);
-  if (k < 1 || k > E || k > 64) return fail(MQ_E_SHAPE, "init: top_k %d outside [1, min(E, 64)]", k);
-  if (H < 128 || I < 128 || H % 128 || I % 128)
-    return fail(MQ_E_SHAPE,
-                "init: hidden %d and intermediate %d must be positive multiples of 128 "
-                "(block sizes of INT4 g128 / FP8 128x128; this version's tiles for NVFP4)",
-                H, I);
-  if (!mq::decode_fits(H) || !mq::decode_fits(I))
-    return fail(MQ_E_SHAPE,
-                "init: hidden %d / intermediate %d above %d: the decode GEMM stages 16 whole "
-                "rows of the input dimension in LDS (160 KiB per workgroup)",
-                H, I, mq::kMaxGemmK);
-  if (!d->w13 || !d->w13_scale || !d->w2 || !d->w2_scale)
-    return fail(MQ_E_NULL, "init: weight and scale pointers must be non-NULL");
-  if (d->format == MQ_W_NVFP4_G16 && (!d->w13_gscale || !d->w2_gscale))
-    return fail(MQ_E_NULL, "init: NVFP4 needs w13_gscale and w2_gscale");
-  if (d->format != MQ_W_NVFP4_G16 && (d->w13_gscale || d->w2_gscale))
-    return fail(MQ_E_NULL, "init: gscale pointers must be NULL for INT4 and FP8");
-  const void *al16[4] = {d->w13, d->w13_scale, d->w2, d->w2_scale};
-  for (const void *p : al16)
-    if (!aligned(p, 16)) return fail(MQ_E_ALIGN, "init: weight/scale pointer %p not 16-byte aligned", p);
-  if ((d->w13_gscale && !aligned(d->w13_gscale, 4)) || (d->w2_gscale && !aligned(d->w2_gscale, 4)))
-    return fail(MQ_E_ALIGN, "init: gscale pointers must be 4-byte aligned");
+  const mq_status st = check_desc(d, "init");
+  if (st != MQ_OK) return st;
   mq_layer *L = new (std::nothrow) mq_layer;
   if (!L) return fail(MQ_E_NULL, "init: host allocation failed");
   L->d = *d;
@@ -279,6 +283,37 @@ mq_status moe_quant_forward_with_router(const mq_layer *L, const uint16_t *hidde
   return mq::forward_impl(L, nullptr, MQ_F32, hidden_bf16, residual_bf16, num_tokens, out_bf16,
                           workspace, workspace_bytes, probe, nullptr, (hipStream_t)stream,
                           router_bf16, logits_out);
+}
+
+mq_status moe_quant_import_expert(const mq_layer_desc *dst, int32_t expert, const mq_src_proj *gate,
+                                  const mq_src_proj *up, const mq_src_proj *down,
+                                  int32_t gptq_zero_offset, uint32_t *bad_zero_points,
+                                  struct ihipStream_t *stream) {
+  if (!dst || !gate || !up || !down) return fail(MQ_E_NULL, "import: NULL argument");
+  const mq_status st = check_desc(dst, "import");
+  if (st != MQ_OK) return st;
+  if (expert < 0 || expert >= dst->num_experts)
+    return fail(MQ_E_SHAPE, "import: expert %d outside [0, %d)", expert, dst->num_experts);
+  const bool int4 = dst->format == MQ_W_INT4_G128;
+  for (const mq_src_proj *p : {gate, up, down}) {
+    if (!p->weight || !p->scale || (int4 && !p->qzeros))
+      return fail(MQ_E_NULL, "import: a source tensor is NULL");
+    const size_t scale_align = dst->format == MQ_W_FP8_B128 ? 4 : int4 ? 2 : 1;
+    if (!aligned(p->weight, 16) || !aligned(p->scale, scale_align) || (int4 && !aligned(p->qzeros, 4)))
+      return fail(MQ_E_ALIGN, "import: source weights must be 16-byte aligned, scales and zeros aligned to their type");
+  }
+  if (bad_zero_points && !aligned(bad_zero_points, 4))
+    return fail(MQ_E_ALIGN, "import: bad_zero_points must be 4-byte aligned");
+  if (dst->format == MQ_W_NVFP4_G16 && gate->global_scale != up->global_scale)
+    return fail(MQ_E_FORMAT, "import: NVFP4 gate and up global scales differ (%g, %g); W13 holds one",
+                (double)gate->global_scale, (double)up->global_scale);
+  mq_layer tmp;
+  tmp.d = *dst;
+  const hipError_t e = mq::launch_import_expert(dims_of(&tmp), expert, *gate, *up, *down,
+                                                gptq_zero_offset, bad_zero_points, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(MQ_E_HIP, "import: %s", hipGetErrorString(e));
+  g_err[0] = 0;
+  return MQ_OK;
 }
 
 mq_status moe_quant_check(const mq_layer *L, const void *workspace, struct ihipStream_t *stream) {
