@@ -13,8 +13,9 @@ a real model's consecutive layers would.
 The headline line is the largest batch: NVFP4 weights, 16384 tokens with
 Zipf-skewed routing (the prefill regime, bound by the matrix units).  Beside it:
 
-* ``regimes``: the decode layer (INT4, 1 / 8 / 64 tokens, bound by HBM) and
-  the FP8 prefill layer (4096 tokens), each with the median, p10 and p90 of
+* ``regimes``: the decode layer (INT4, 1 / 8 / 64 tokens, bound by HBM), the
+  FP8 prefill layer (4096 tokens), and the same FP8 layer with dynamic 1x128
+  FP8 activations on the FP8 matrix units (W8A8), each with the median, p10 and p90 of
   per-step times with the weights cycled through the sets, with one set
   repeated (warm caches) and after a 1 GiB flush (cold caches), plus the
   decode batches replayed from a captured HIP graph;
@@ -48,6 +49,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 PEAK_FP16_TFLOPS = 2500.0    # MI355X dense FP16/BF16 MFMA
+PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 MFMA
 STAGES = ("route", "permute", "gate_up", "down", "combine")
 EVERY = 4  # bracket the dominant kernel with events in one step of every EVERY
 CSRC = os.path.join(ROOT, "weight_quantized_moe_amd", "csrc")
@@ -117,11 +119,11 @@ class LayerBench:
     """One workload's layer: several weight sets (cycled so they stream from
     HBM), its synthetic batch, workspace and output."""
 
-    def __init__(self, wl, T, dev, min_bytes=1.5 * 2 ** 30, seed0=1000, share=None):
+    def __init__(self, wl, T, dev, min_bytes=1.5 * 2 ** 30, seed0=1000, share=None, w8a8=False):
         import numpy as np
         import torch
         from weight_quantized_moe_amd import Layer, synth
-        self.wl, self.T, self.dev = wl, T, dev
+        self.wl, self.T, self.dev, self.w8a8 = wl, T, dev, w8a8
         E, H, I, k, fmt = wl.experts, wl.hidden, wl.inter, wl.top_k, wl.fmt
         layer_bytes = E * (packed_bytes(fmt, 2 * I, H) + packed_bytes(fmt, H, I))
         self.n_sets = max(2, math.ceil(min_bytes / layer_bytes))
@@ -149,8 +151,9 @@ class LayerBench:
         self.work = kernel_work(fmt, E, H, I, k, T, self.touched)
 
     def fwd(self, i, events=None):
-        self.layers[i % self.n_sets].forward(self.logits, self.x, out=self.out, workspace=self.ws,
-                                             events=events)
+        lay = self.layers[i % self.n_sets]
+        f = lay.forward_w8a8 if self.w8a8 else lay.forward
+        f(self.logits, self.x, out=self.out, workspace=self.ws, events=events)
 
     def stages(self, n):
         """Average per-stage time (ms) over n steps (its own run: ten event
@@ -243,9 +246,14 @@ def roofline(lb, dom, dom_ms, decode):
     else:
         algo = lb.work["flops"][dom]
         achieved = algo / secs / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4)}
-    roof["traffic"] = counter_traffic(f"{dom}_{wl.fmt}_T{lb.T}")
+        peak = PEAK_FP8_TFLOPS if lb.w8a8 else PEAK_FP16_TFLOPS
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4)}
+        if lb.w8a8:
+            roof["mfma_dtype"] = "fp8 (e4m3 x e4m3)"
+            roof["frac_of_fp16_peak"] = round(achieved / PEAK_FP16_TFLOPS, 4)
+    tag = f"{dom}_{wl.fmt}{'_w8a8' if lb.w8a8 else ''}_T{lb.T}"
+    roof["traffic"] = counter_traffic(tag)
     roof["kernel"] = dom
     roof["kernel_us"] = round(dom_ms * 1e3, 2)
     roof["algorithmic_bytes" if decode else "algorithmic_flops"] = algo
@@ -261,7 +269,8 @@ def regime_line(lb, iters, flush, graph):
     stage_ms = lb.stages(min(iters, 30))
     dom = max(("gate_up", "down"), key=lambda s: stage_ms[s])
     t = lb.timed(iters, 5, dom)
-    out = {"workload": lb.wl.name, "format": lb.wl.fmt, "tokens": lb.T, "touched_experts": lb.touched,
+    out = {"workload": lb.wl.name + ("_w8a8" if lb.w8a8 else ""), "format": lb.wl.fmt, "tokens": lb.T,
+           "touched_experts": lb.touched,
            "tokens_per_s": round(lb.T / (t["ms"] * 1e-3), 1), "us_per_step": round(t["ms"] * 1e3, 2)}
     for mode in ("cycled", "warm", "cold"):
         v = lb.per_step(iters, mode, flush)
@@ -616,7 +625,12 @@ def main():
             if T2 in (64, 4096):
                 res.setdefault("with_router", []).append(router_line(other, args.iters))
             prev = other
-        del prev, other
+        # W8A8 block FP8: the FP8 prefill layer with dynamic FP8 activations
+        w8 = LayerBench(synth.WORKLOADS["prefill_fp8"], 4096, dev, share=prev, w8a8=True)
+        line = regime_line(w8, args.iters, flush, graph=False)
+        res["regimes"].append(line)
+        print(f"# prefill_fp8 W8A8 T=4096: {line['us_per_step']} us/step", file=sys.stderr, flush=True)
+        del prev, other, w8
     res["import"] = import_bench(dev)
     print("# import done", file=sys.stderr, flush=True)
     if not args.no_stack:

@@ -198,6 +198,39 @@ mq_status moe_quant_forward(const mq_layer *L, const void *router_logits, int32_
                             struct ihipStream_t *stream);
 
 /*
+ * W8A8 block FP8: moe_quant_forward for an MQ_W_FP8_B128 layer with its
+ * activations quantized to FP8 as the "clef-omni-fp8" card (table "What was
+ * quantized") runs them in engines, "dynamic FP8 per 1x128 group": for each
+ * token (gate/up input) and each grouped row (down input) and each 128
+ * consecutive input features, s = amax / 448 (FP32) and code =
+ * RNE-to-E4M3(x / s) saturated to +-448; the SwiGLU intermediate is quantized
+ * from its FP32 value.  Both GEMMs run on the FP8 matrix units, the
+ * activation and weight scales multiplying each 128-wide k block's FP32
+ * partial sum.  Same arguments, workspace size and routing as
+ * moe_quant_forward (the kernels are the many-rows-per-expert ones at every
+ * batch size).  The probe's h buffer (T*k*I*2 bytes) receives h as kept
+ * here: the E4M3 codes uint8 [T*k, I] in grouped row order, followed by their
+ * FP32 scales [T*k, I/128].  Errors: as moe_quant_forward, plus MQ_E_FORMAT
+ * for another weight format.
+ */
+mq_status moe_quant_forward_w8a8(const mq_layer *L, const void *router_logits, int32_t logits_dtype,
+                                 const uint16_t *hidden_bf16, const uint16_t *residual_bf16,
+                                 int64_t num_tokens, uint16_t *out_bf16, void *workspace,
+                                 size_t workspace_bytes, const mq_probe *probe,
+                                 struct ihipStream_t *stream);
+
+/*
+ * Test entry: the dynamic 1x128 FP8 activation quantizer of the W8A8 path on
+ * FP32 rows x [rows, K] (device), writing codes uint8 [rows, K] (E4M3FN bits)
+ * and scales float [rows, K/128] (device, caller-owned), with the same group
+ * arithmetic the W8A8 kernels apply to hidden rows and to the SwiGLU
+ * intermediate.  K a positive multiple of 128 (at most 65536).
+ * Errors: MQ_E_SHAPE, MQ_E_NULL, MQ_E_ALIGN, MQ_E_HIP.
+ */
+mq_status moe_quant_quantize_act(const float *x, int64_t rows, int32_t K, uint8_t *codes, float *scales,
+                                 struct ihipStream_t *stream);
+
+/*
  * moe_quant_forward with the router in the library: the logits of the BF16
  * gate that stays unquantized on every card ("clef-omni-int4" card, section
  * "Recipe": ignore_layers=mlp.gate; "clef-omni-NVFP4" card, section "How it

@@ -69,6 +69,44 @@ def expert_w8a8(xq: np.ndarray, w13: np.ndarray, w2: np.ndarray,
     return dequantize_act(hc, hs) @ w2.T, h32
 
 
+def down_from_codes(layer: moe.Layer, logits: np.ndarray, hcodes: np.ndarray,
+                    hscales: np.ndarray, residual_bf16_bits: Optional[np.ndarray] = None):
+    """The layer output from given quantized intermediates (teacher forcing):
+    ``hcodes`` uint8 [T*k, I] and ``hscales`` float32 [T*k, I/128] in grouped
+    row order (experts ascending, tokens ascending inside one), the down
+    projection over their dequantized values and the slot-ordered combine."""
+    ids, w = moe.route(logits, layer.top_k)
+    perm = moe.permute(ids, layer.num_experts)
+    hq = dequantize_act(hcodes, hscales)
+    expert_out = np.empty((len(ids) * layer.top_k, layer.hidden), dtype=np.float64)
+    for e in range(layer.num_experts):
+        lo, hi = perm.offsets[e], perm.offsets[e + 1]
+        if hi > lo:
+            expert_out[lo:hi] = hq[lo:hi] @ formats.dequantize_expert(layer.w2, e).T
+    y = moe.combine(perm, w, expert_out)
+    if residual_bf16_bits is not None:
+        y = y + moe.bf16_bits_to_f64(residual_bf16_bits)
+    return y
+
+
+def intermediate_w8a8(layer: moe.Layer, logits: np.ndarray, x_bf16_bits: np.ndarray):
+    """The SwiGLU intermediate in FP32 [T*k, I], grouped row order, before its
+    quantization (for comparing the quantized codes)."""
+    ids, _ = moe.route(logits, layer.top_k)
+    perm = moe.permute(ids, layer.num_experts)
+    x = moe.bf16_bits_to_f64(x_bf16_bits)
+    xc, xs = quantize_act(x)
+    xq = dequantize_act(xc, xs)
+    i = layer.intermediate
+    h32 = np.empty((len(ids) * layer.top_k, i), dtype=np.float32)
+    for e in range(layer.num_experts):
+        lo, hi = perm.offsets[e], perm.offsets[e + 1]
+        if hi > lo:
+            gu = xq[perm.sorted_token_ids[lo:hi]] @ formats.dequantize_expert(layer.w13, e).T
+            h32[lo:hi] = (moe.silu(gu[:, :i]) * gu[:, i:]).astype(np.float32)
+    return h32
+
+
 def moe_forward_w8a8(layer: moe.Layer, logits: np.ndarray, x_bf16_bits: np.ndarray,
                      residual_bf16_bits: Optional[np.ndarray] = None):
     """Float64 W8A8 layer output y [T, H] (plus the residual if given), with

@@ -220,6 +220,27 @@ def test_import_expert_rejects_before_any_launch(lib):
     assert f(ctypes.byref(d), 0, ctypes.byref(g1), ctypes.byref(g2), ctypes.byref(g1), 1, None, None) == MQ_E_FORMAT
 
 
+def test_forward_w8a8_and_quantize_act_reject_before_any_launch(lib):
+    P = 0x100000
+    st, h = _init(lib, _desc(1))               # INT4: W8A8 needs the FP8 format
+    assert st == MQ_OK
+    f = lib.moe_quant_forward_w8a8
+    assert f(h, P, 0, P, None, 4, P, P, 1 << 20, None, None) == 4          # MQ_E_FORMAT
+    lib.moe_quant_destroy(h)
+    st, h = _init(lib, _desc(2))
+    assert f(h, P, 0, P, None, 4, P, P, 16, None, None) == MQ_E_WORKSPACE
+    pr = Probe()
+    pr.h = P
+    assert f(h, P, 0, P, None, 4, P, P, 1 << 20, ctypes.byref(pr), None) == 4
+    lib.moe_quant_destroy(h)
+    q = lib.moe_quant_quantize_act
+    assert q(P, 4, 200, P, P, None) == MQ_E_SHAPE
+    assert q(P, -1, 256, P, P, None) == MQ_E_SHAPE
+    assert q(None, 0, 256, None, None, None) == MQ_OK
+    assert q(None, 4, 256, P, P, None) == MQ_E_NULL
+    assert q(P + 4, 4, 256, P, P, None) == MQ_E_ALIGN
+
+
 def test_dequantize_rejects(lib):
     st, h = _init(lib, _desc(2))
     assert st == MQ_OK

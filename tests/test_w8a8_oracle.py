@@ -104,6 +104,21 @@ def test_forward_matches_brute_force():
     assert np.linalg.norm(y - y16) / np.linalg.norm(y16) > 1e-3
 
 
+def test_teacher_forced_down_reproduces_the_forward():
+    """Quantizing the oracle's own intermediate and running down_from_codes on
+    those codes gives moe_forward_w8a8's output (the pieces the GPU test
+    composes are the forward's own)."""
+    E, H, I, k, T = 4, 256, 256, 2, 9
+    p13, p2 = quantized_layer(formats.FP8, 73, 0, E, H, I)
+    layer = moe.Layer(p13, p2, k)
+    from weight_quantized_moe_amd import synth
+    lg = synth.router_logits(73, 0, T, E)
+    x = synth.hidden_bf16(73, 0, T, H)
+    y, _, _ = w8a8.moe_forward_w8a8(layer, lg, x)
+    hc, hs = w8a8.quantize_act(w8a8.intermediate_w8a8(layer, lg, x))
+    np.testing.assert_array_equal(w8a8.down_from_codes(layer, lg, hc, hs), y)
+
+
 def test_rejects_other_formats():
     p13, p2 = quantized_layer(formats.INT4, 72, 0, 2, 256, 128)
     with pytest.raises(ValueError):

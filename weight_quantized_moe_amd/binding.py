@@ -23,6 +23,8 @@ EXPORTED = (
     "moe_quant_forward",
     "moe_quant_forward_noalloc",
     "moe_quant_forward_with_router",
+    "moe_quant_forward_w8a8",
+    "moe_quant_quantize_act",
     "moe_quant_import_expert",
     "moe_quant_check",
     "moe_quant_dequantize",
@@ -110,6 +112,10 @@ def load_library():
     lib.moe_quant_import_expert.argtypes = [ctypes.POINTER(LayerDesc), i32, ctypes.POINTER(SrcProj),
                                             ctypes.POINTER(SrcProj), ctypes.POINTER(SrcProj), i32, vp, vp]
     lib.moe_quant_import_expert.restype = i32
+    lib.moe_quant_forward_w8a8.argtypes = [vp, vp, i32, vp, vp, i64, vp, vp, sz, ctypes.POINTER(Probe), vp]
+    lib.moe_quant_forward_w8a8.restype = i32
+    lib.moe_quant_quantize_act.argtypes = [vp, i64, i32, vp, vp, vp]
+    lib.moe_quant_quantize_act.restype = i32
     lib.moe_quant_check.argtypes = [vp, vp, vp]
     lib.moe_quant_check.restype = i32
     lib.moe_quant_dequantize.argtypes = [vp, i32, i32, vp, vp]
@@ -248,6 +254,27 @@ def import_expert(fmt: str, dst, expert: int, gate, up, down, gptq_zero_offset: 
                                             _stream(stream)))
 
 
+def quantize_act(x, codes=None, scales=None, stream=None):
+    """Dynamic 1x128 FP8 quantization of float32 rows x [rows, K] on the GPU
+    (moe_quant_quantize_act): returns (codes uint8 [rows, K], scales float32
+    [rows, K/128])."""
+    import torch
+    lib = load_library()
+    if x.dim() != 2:
+        raise ValueError("x must be [rows, K]")
+    r, k = x.shape
+    _need(x, "x", (r, k), (torch.float32,))
+    if codes is None:
+        codes = torch.empty((r, k), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((r, k // 128), dtype=torch.float32, device=x.device)
+    _need(codes, "codes", (r, k), (torch.uint8,))
+    _need(scales, "scales", (r, k // 128), (torch.float32,))
+    _on_gpu(None, x=x, codes=codes, scales=scales)
+    _check(lib, lib.moe_quant_quantize_act(_ptr(x), r, k, _ptr(codes), _ptr(scales), _stream(stream)))
+    return codes, scales
+
+
 class Layer:
     """One MoE expert layer over packed weights resident on the GPU.
 
@@ -320,6 +347,13 @@ class Layer:
         return self._forward(logits, None, hidden, residual, out, workspace, probe, events,
                              stream, None)
 
+    def forward_w8a8(self, logits, hidden, residual=None, out=None, workspace=None,
+                     probe: Optional[Dict] = None, events=None, stream=None):
+        """W8A8 forward of an FP8 layer (moe_quant_forward_w8a8): dynamic 1x128
+        FP8 activations on the FP8 matrix units."""
+        return self._forward(logits, None, hidden, residual, out, workspace, probe, events,
+                             stream, None, w8a8=True)
+
     def forward_with_router(self, router_w, hidden, residual=None, out=None, workspace=None,
                             logits_out=None, probe: Optional[Dict] = None, events=None,
                             stream=None):
@@ -330,7 +364,7 @@ class Layer:
                              stream, logits_out)
 
     def _forward(self, logits, router_w, hidden, residual, out, workspace, probe, events, stream,
-                 logits_out):
+                 logits_out, w8a8=False):
         import torch
         if hidden.dim() != 2:
             raise ValueError("hidden must be [T, H]")
@@ -381,7 +415,8 @@ class Layer:
         prp = ctypes.byref(pr) if pr is not None else None
         if router_w is None:
             ldt = MQ_F32 if logits.dtype == torch.float32 else MQ_BF16
-            st = self._lib.moe_quant_forward(
+            fn = self._lib.moe_quant_forward_w8a8 if w8a8 else self._lib.moe_quant_forward
+            st = fn(
                 self._h, _ptr(logits), ldt, _ptr(hidden), _ptr(residual), t, _ptr(out),
                 _ptr(workspace), _nbytes(workspace), prp, _stream(stream))
         else:

@@ -112,6 +112,23 @@ __device__ __forceinline__ h8 unpack_nvfp4(uint32_t w, _Float16 s) {
   return as_h8(r);
 }
 
+// ---------------------------------------------------------------- FP8 activations
+// Dynamic 1x128 FP8 activation quantization (the W8A8 variant of the FP8
+// layer: the "clef-omni-fp8" card, table "What was quantized", runs its
+// activations as dynamic FP8 per 1x128 group in engines).  For a group of 128
+// values with maximum magnitude m: s = m / 448 (one IEEE FP32 division; m = 0
+// gives s = 1 and zero codes) and code = RNE-to-E4M3(v / s), the quotient
+// clamped to +-448 first (one IEEE FP32 division per value).  gfx950's
+// v_cvt_pk_fp8_f32 encodes OCP E4M3FN with round-to-nearest-even.
+__device__ __forceinline__ float fp8_group_scale(float amax) { return amax > 0.f ? amax / 448.f : 1.f; }
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d, float s) {
+  const float qa = fminf(fmaxf(a / s, -448.f), 448.f), qb = fminf(fmaxf(b / s, -448.f), 448.f);
+  const float qc = fminf(fmaxf(c / s, -448.f), 448.f), qd = fminf(fmaxf(d / s, -448.f), 448.f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(qa, qb, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(qc, qd, w, true);
+  return (uint32_t)w;
+}
+
 // ---------------------------------------------------------------- misc
 // silu(z) = z / (1 + e^-z); the reciprocal is the hardware one (1 ulp), which
 // is far below the FP16 rounding of the SwiGLU intermediate it feeds.

@@ -972,7 +972,7 @@ static int num_cus() {
 }
 
 // Allow up to 160 KiB of dynamic LDS for kernel f on the current device (once).
-static void raise_lds_limit(const void *f) {
+void raise_lds_limit(const void *f) {
   const int dev = current_device();
   std::lock_guard<std::mutex> lk(g_launch_mu);
   if (g_lds_raised.insert({f, dev}).second)

@@ -88,6 +88,7 @@ struct FwdPtrs {
   int logits_bf16;
   const uint16_t *gate_w;  // BF16 router weight [E, H]: logits computed in-library (else null)
   float *p_logits;         // probe: the in-library logits [T, E] (may be null)
+  int w8a8;                // FP8 layer with dynamic 1x128 FP8 activations
   const uint16_t *hidden;
   const uint16_t *residual;
   uint16_t *out;
@@ -120,6 +121,15 @@ hipError_t launch_dequantize(const LayerDims &L, int which, int expert, float *o
 hipError_t launch_import_expert(const LayerDims &L, int e, const mq_src_proj &gate,
                                 const mq_src_proj &up, const mq_src_proj &down, int gptq_offset,
                                 uint32_t *bad, hipStream_t st);
+// Allow up to 160 KiB of dynamic LDS for kernel f on the current device (once
+// per device; thread safe).
+void raise_lds_limit(const void *f);
+hipError_t launch_quant_act(const float *x, int64_t rows, int K, uint8_t *codes, float *scales,
+                            hipStream_t s);
+hipError_t launch_w8a8_gate_up(const LayerDims &L, const FwdPtrs &P, const Workspace &W,
+                               const GemmLaunch &s);
+hipError_t launch_w8a8_down(const LayerDims &L, const FwdPtrs &P, const Workspace &W,
+                            const GemmLaunch &s);
 hipError_t launch_router_logits(const uint16_t *x, const uint16_t *w, float *out, int64_t T, int H,
                                 int E, hipStream_t s);
 
@@ -131,7 +141,7 @@ mq_status forward_impl(const mq_layer *L, const void *router_logits, int32_t log
                        int64_t num_tokens, uint16_t *out_bf16, void *workspace,
                        size_t workspace_bytes, const mq_probe *probe, uint32_t *flags,
                        hipStream_t stream, const uint16_t *gate_w = nullptr,
-                       float *logits_out = nullptr);
+                       float *logits_out = nullptr, int w8a8 = 0);
 // Record a status and its one-line explanation for moe_quant_last_error().
 mq_status fail(mq_status s, const char *fmt, ...);
 void clear_error();

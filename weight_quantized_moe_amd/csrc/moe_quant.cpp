@@ -177,7 +177,8 @@ mq_status mq::forward_impl(const mq_layer *L, const void *router_logits, int32_t
                            const uint16_t *hidden_bf16, const uint16_t *residual_bf16,
                            int64_t num_tokens, uint16_t *out_bf16, void *workspace,
                            size_t workspace_bytes, const mq_probe *probe, uint32_t *flags,
-                           hipStream_t stream, const uint16_t *gate_w, float *logits_out) {
+                           hipStream_t stream, const uint16_t *gate_w, float *logits_out,
+                           int w8a8) {
   if (!L) return fail(MQ_E_NULL, "forward: NULL layer handle");
   if (num_tokens < 0 || num_tokens > kMaxTokens)
     return fail(MQ_E_SHAPE, "forward: num_tokens %lld outside [0, %lld]", (long long)num_tokens,
@@ -215,6 +216,7 @@ mq_status mq::forward_impl(const mq_layer *L, const void *router_logits, int32_t
   P.logits_bf16 = logits_dtype == MQ_BF16;
   P.gate_w = gate_w;
   P.p_logits = logits_out;
+  P.w8a8 = w8a8;
   P.hidden = hidden_bf16;
   P.residual = residual_bf16;
   P.out = out_bf16;
@@ -254,15 +256,17 @@ mq_status mq::forward_impl(const mq_layer *L, const void *router_logits, int32_t
     }
     return g;
   };
-  if ((e = mq::launch_gate_up(D, P, W, decode, kev(MQ_STAGE_GATE_UP))) != hipSuccess)
-    return fail(MQ_E_HIP, "forward: gate_up launch: %s", hipGetErrorString(e));
+  e = w8a8 ? mq::launch_w8a8_gate_up(D, P, W, kev(MQ_STAGE_GATE_UP))
+           : mq::launch_gate_up(D, P, W, decode, kev(MQ_STAGE_GATE_UP));
+  if (e != hipSuccess) return fail(MQ_E_HIP, "forward: gate_up launch: %s", hipGetErrorString(e));
   if (P.p_h) {
     e = hipMemcpyAsync(P.p_h, P.ws + W.h, (size_t)num_tokens * D.k * D.I * 2,
                        hipMemcpyDeviceToDevice, s);
     if (e != hipSuccess) return fail(MQ_E_HIP, "forward: probe copy: %s", hipGetErrorString(e));
   }
-  if ((e = mq::launch_down(D, P, W, decode, kev(MQ_STAGE_DOWN))) != hipSuccess)
-    return fail(MQ_E_HIP, "forward: down launch: %s", hipGetErrorString(e));
+  e = w8a8 ? mq::launch_w8a8_down(D, P, W, kev(MQ_STAGE_DOWN))
+           : mq::launch_down(D, P, W, decode, kev(MQ_STAGE_DOWN));
+  if (e != hipSuccess) return fail(MQ_E_HIP, "forward: down launch: %s", hipGetErrorString(e));
   ev(MQ_STAGE_COMBINE, 0);
   if ((e = mq::launch_combine(D, P, W, s)) != hipSuccess)
     return fail(MQ_E_HIP, "forward: combine launch: %s", hipGetErrorString(e));
@@ -272,6 +276,37 @@ mq_status mq::forward_impl(const mq_layer *L, const void *router_logits, int32_t
 }
 
 extern "C" {
+
+mq_status moe_quant_forward_w8a8(const mq_layer *L, const void *router_logits, int32_t logits_dtype,
+                                 const uint16_t *hidden_bf16, const uint16_t *residual_bf16,
+                                 int64_t num_tokens, uint16_t *out_bf16, void *workspace,
+                                 size_t workspace_bytes, const mq_probe *probe,
+                                 struct ihipStream_t *stream) {
+  if (!L) return fail(MQ_E_NULL, "forward_w8a8: NULL layer handle");
+  if (L->d.format != MQ_W_FP8_B128)
+    return fail(MQ_E_FORMAT, "forward_w8a8: W8A8 applies to MQ_W_FP8_B128 layers (format %d)", L->d.format);
+  return mq::forward_impl(L, router_logits, logits_dtype, hidden_bf16, residual_bf16, num_tokens,
+                          out_bf16, workspace, workspace_bytes, probe, nullptr, (hipStream_t)stream,
+                          nullptr, nullptr, 1);
+}
+
+mq_status moe_quant_quantize_act(const float *x, int64_t rows, int32_t K, uint8_t *codes, float *scales,
+                                 struct ihipStream_t *stream) {
+  if (rows < 0 || rows > ((int64_t)1 << 30) || K <= 0 || K % 128 || K > 65536)
+    return fail(MQ_E_SHAPE, "quantize_act: rows %lld and K %d (K a positive multiple of 128, at most 65536)",
+                (long long)rows, K);
+  if (rows == 0) {
+    g_err[0] = 0;
+    return MQ_OK;
+  }
+  if (!x || !codes || !scales) return fail(MQ_E_NULL, "quantize_act: NULL argument");
+  if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(scales, 4))
+    return fail(MQ_E_ALIGN, "quantize_act: x 16-byte, codes 8-byte, scales 4-byte aligned");
+  const hipError_t e = mq::launch_quant_act(x, rows, K, codes, scales, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(MQ_E_HIP, "quantize_act: %s", hipGetErrorString(e));
+  g_err[0] = 0;
+  return MQ_OK;
+}
 
 mq_status moe_quant_forward_with_router(const mq_layer *L, const uint16_t *hidden_bf16,
                                         const uint16_t *router_bf16,

@@ -201,6 +201,77 @@ __device__ __forceinline__ void rows_to_f16(const uint16_t *__restrict__ hidden,
   }
 }
 
+// W8A8: the wave's 4 hidden rows as dynamic 1x128 FP8 activations, codes
+// [T, H] and FP32 scales [T, H/128].  Each pass covers 512 columns of a row:
+// lane l holds columns 8 l + [0, 8), so the 16 lanes of a DPP row hold one
+// 128-wide group, whose maximum is a 4-step DPP max.
+__device__ __forceinline__ void rows_to_fp8(const uint16_t *__restrict__ hidden, int t0, int T,
+                                            int H, int lane, uint8_t *__restrict__ xq,
+                                            float *__restrict__ xs) {
+  const int G = H / 128;
+  for (int r = 0; r < 4; ++r) {
+    const int t = t0 + r;
+    if (t >= T) break;  // wave-uniform
+    for (int c0 = 0; c0 < H; c0 += 512) {
+      const int c = c0 + lane * 8;
+      const bool ok = c < H;  // whole 16-lane groups (H is a multiple of 128)
+      const u4 v = ok ? *(const u4 *)(hidden + (size_t)t * H + c) : u4{0u, 0u, 0u, 0u};
+      float f[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f[2 * i] = bf16_to_f32(v[i] & 0xFFFFu);
+        f[2 * i + 1] = bf16_to_f32(v[i] >> 16);
+      }
+      float m = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
+      m = max16f(m);
+      const float s = fp8_group_scale(m);
+      if (ok) {
+        typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+        *(u2 *)(xq + (size_t)t * H + c) = u2{e4m3x4(f[0], f[1], f[2], f[3], s), e4m3x4(f[4], f[5], f[6], f[7], s)};
+        if ((lane & 15) == 0) xs[(size_t)t * G + c / 128] = s;
+      }
+    }
+  }
+}
+
+// Test entry: FP32 rows [rows, K] -> dynamic 1x128 FP8 codes and scales, with
+// the same group arithmetic as rows_to_fp8 and the W8A8 GEMM epilogue.  One
+// wave per (row, 512-column pass).
+__global__ __launch_bounds__(256) void quant_act_kernel(const float *__restrict__ x, int64_t rows, int K,
+                                                        uint8_t *__restrict__ codes,
+                                                        float *__restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int passes = (K + 511) / 512;
+  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wid >= rows * passes) return;  // wave-uniform
+  const int64_t row = wid / passes;
+  const int c = (int)(wid % passes) * 512 + lane * 8;
+  const bool ok = c < K;
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = ok ? x[row * K + c + i] : 0.f;
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
+  m = max16f(m);
+  const float s = fp8_group_scale(m);
+  if (ok) {
+    typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+    *(u2 *)(codes + row * K + c) = u2{e4m3x4(f[0], f[1], f[2], f[3], s), e4m3x4(f[4], f[5], f[6], f[7], s)};
+    if ((lane & 15) == 0) scales[row * (K / 128) + c / 128] = s;
+  }
+}
+
+hipError_t launch_quant_act(const float *x, int64_t rows, int K, uint8_t *codes, float *scales,
+                            hipStream_t s) {
+  const int64_t waves = rows * ((K + 511) / 512);
+  hipLaunchKernelGGL(quant_act_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, x, rows, K,
+                     codes, scales);
+  return hipGetLastError();
+}
+
 // Decode: only the power of two of each hidden row (rowscale[t] = 2^s), for
 // the wave's 4 tokens (rows of H <= kRowRegsMaxH, read once into registers).  The
 // decode gate/up GEMM scales the rows into FP16 itself while staging them.
@@ -244,6 +315,11 @@ __global__ __launch_bounds__(256) void route_kernel(const void *__restrict__ log
   if (blockIdx.x == 0 && threadIdx.x == 0) flags[0] = 0u;
   if (t0 >= T) return;
   static_assert(kRowRegsMaxH == 4 * 64 * 8, "4 x 16 bytes per lane cover one row");
+  if (stage_rows == 3) {  // W8A8: FP8 codes and scales of the hidden rows
+    if (t < T) topk16<kPer, kBf16Logits>(logits, t, E, k, li, ids, wts, p_ids, p_w);
+    rows_to_fp8(hidden, t0, T, H, lane, (uint8_t *)x16, (float *)((uint8_t *)x16 + (size_t)T * H));
+    return;
+  }
   if (stage_rows != 0 && H <= kRowRegsMaxH) {
     // rows of up to 2048 values: the rows' loads and the logits' loads in
     // flight together, each row read once (decode keeps only its scale,
@@ -636,7 +712,7 @@ hipError_t launch_route(const LayerDims &L, const FwdPtrs &P, const Workspace &W
   // prefill: FP16 rows and their scales (1); decode with H <= 2048: the
   // scales only (2), the decode gate/up GEMM converts the rows it stages;
   // larger decode rows: the GEMM finds the scales too (0)
-  const int stage_rows = !decode ? 1 : L.H <= kRowRegsMaxH ? 2 : 0;
+  const int stage_rows = P.w8a8 ? 3 : !decode ? 1 : L.H <= kRowRegsMaxH ? 2 : 0;
   if (P.gate_w && P.T >= kGateFusedMinT)  // router GEMM fused with the top-k
     return L.fmt == FMT_INT4 ? gate_route_dispatch<true>(L, P, W, stage_rows, s)
                              : gate_route_dispatch<false>(L, P, W, stage_rows, s);
