@@ -84,5 +84,27 @@ def build(verbose: bool = False, extra_flags=(), out: str = LIB) -> str:
     return out
 
 
+ASAN_LIB = os.path.join(OBJ_DIR, "libmoe_quant_asan.so")
+ASAN_FLAGS = ("-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer",
+              "-Xarch_host", "-shared-libasan")
+
+
+def asan_runtime() -> str:
+    """The clang AddressSanitizer runtime to preload for the host-ASan build."""
+    cands = sorted(glob.glob(os.path.join(os.path.dirname(hipcc()), "..", "lib", "llvm", "lib", "clang",
+                                          "*", "lib", "linux", "libclang_rt.asan-x86_64.so")))
+    if not cands:
+        cands = sorted(glob.glob("/opt/rocm/lib/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not cands:
+        raise RuntimeError("clang AddressSanitizer runtime not found")
+    return os.path.realpath(cands[-1])
+
+
+def build_asan(verbose: bool = False) -> str:
+    """The library with AddressSanitizer on its host code only (the device code
+    is built as usual), for running the host-side ABI tests under ASan."""
+    return build(verbose, extra_flags=ASAN_FLAGS, out=ASAN_LIB)
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

@@ -3,7 +3,9 @@
 //
 // Every unpack path is exact: INT4 codes (c - 8), E4M3 values and E2M1 x E4M3
 // block-scale products are all representable in FP16, so the contraction runs
-// on FP16 MFMA with FP32 accumulation and only the FP32 scales round.
+// on FP16 MFMA with FP32 accumulation.  Where the INT4 / FP8 scales enter
+// (on the FP32 partial sums in the decode GEMM, folded into the FP16 weight
+// operand in the prefill GEMM) is described with the GEMMs.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>

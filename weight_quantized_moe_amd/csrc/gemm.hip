@@ -6,9 +6,16 @@
 // grouped matmul" ("clef-omni-fp8" card, section "How this checkpoint runs";
 // "clef-omni-int4" card, section "How this checkpoint runs"; "clef-omni-NVFP4"
 // card, section "How it was made").  Here the dequantization never leaves the
-// chip: packed codes are unpacked exactly into FP16 MFMA operands, INT4 group
-// scales and FP8 block scales multiply the FP32 partial sum of each 128-wide k
-// block, and the NVFP4 global scale multiplies the finished sum.
+// chip: packed codes are unpacked exactly into FP16 MFMA operands, and the
+// NVFP4 global scale multiplies the finished FP32 sum.  The INT4 group scales
+// and FP8 block scales are applied differently by the two paths:
+//  - decode: they multiply the FP32 partial sum of each 128-wide k block (one
+//    FP32 rounding per block);
+//  - prefill: each is folded into the FP16 weight operand together with a
+//    power of two per weight column (the FP32 scale rounded to FP16, then the
+//    product code * scale rounded to FP16: at most about 2^-11 relative per
+//    weight beside the FP16 scale's own 2^-11), and the column's accumulator
+//    is multiplied back by the power of two at the end.
 //
 // Operand roles (both kernels): the MFMA A operand is activations (rows =
 // grouped tokens), the B operand is weights (columns = output features).  A
