@@ -64,9 +64,12 @@ def packed_bytes(fmt, n, k):
     return n * k // 2 + n * (k // 16) + 4
 
 
-def source_hash() -> str:
+def source_hash(files=None) -> str:
+    """Hash of the kernel sources (all of csrc/, or the named files in it and
+    the headers they include)."""
+    names = sorted(os.listdir(CSRC)) if files is None else sorted(set(files) | {"device.h", "internal.h"})
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
+    for name in names:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -74,14 +77,16 @@ def source_hash() -> str:
 
 def counter_traffic(kernel_tag: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None if there is none or the kernels changed since it was taken."""
+    None if there is none or the kernel's source changed since it was taken
+    (the summary names the source file and its hash)."""
     path = os.path.join(ROOT, "profiles", f"{kernel_tag}_counters.txt")
     if not os.path.exists(path):
         return None
     text = open(path).read()
+    f = re.search(r"source_file\s*=\s*([\w.]+)", text)
     m = re.search(r"source_hash\s*=\s*(\w+)", text)
     b = re.search(r"hbm_bytes_per_launch\s*=\s*([0-9.eE+]+)", text)
-    if not m or not b or m.group(1) != source_hash():
+    if not f or not m or not b or m.group(1) != source_hash([f.group(1)]):
         return None
     return float(b.group(1))
 
