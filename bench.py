@@ -15,7 +15,8 @@ Zipf-skewed routing (the prefill regime, bound by the matrix units).  Beside it:
 
 * ``regimes``: the decode layer (INT4, 1 / 8 / 64 tokens, bound by HBM), the
   FP8 prefill layer (4096 tokens), and the same FP8 layer with dynamic 1x128
-  FP8 activations on the FP8 matrix units (W8A8), each with the median, p10 and p90 of
+  FP8 activations on the FP8 matrix units (W8A8), the NVFP4 layer with 4-bit
+  activations (W4A4, 16384 tokens), each with the median, p10 and p90 of
   per-step times with the weights cycled through the sets, with one set
   repeated (warm caches) and after a 1 GiB flush (cold caches), plus the
   decode batches replayed from a captured HIP graph;
@@ -124,11 +125,12 @@ class LayerBench:
     """One workload's layer: several weight sets (cycled so they stream from
     HBM), its synthetic batch, workspace and output."""
 
-    def __init__(self, wl, T, dev, min_bytes=1.5 * 2 ** 30, seed0=1000, share=None, w8a8=False):
+    def __init__(self, wl, T, dev, min_bytes=1.5 * 2 ** 30, seed0=1000, share=None, w8a8=False,
+                 w4a4=False):
         import numpy as np
         import torch
         from weight_quantized_moe_amd import Layer, synth
-        self.wl, self.T, self.dev, self.w8a8 = wl, T, dev, w8a8
+        self.wl, self.T, self.dev, self.w8a8, self.w4a4 = wl, T, dev, w8a8, w4a4
         E, H, I, k, fmt = wl.experts, wl.hidden, wl.inter, wl.top_k, wl.fmt
         layer_bytes = E * (packed_bytes(fmt, 2 * I, H) + packed_bytes(fmt, H, I))
         self.n_sets = max(2, math.ceil(min_bytes / layer_bytes))
@@ -154,9 +156,21 @@ class LayerBench:
         torch.cuda.synchronize()
         self.touched = int((torch.diff(offs) > 0).sum().item())
         self.work = kernel_work(fmt, E, H, I, k, T, self.touched)
+        if w4a4:
+            # calibrated activation global scales (448 * 6 over the largest
+            # value): the hidden rows, and the intermediate of a 16-bit pass
+            h = torch.empty((T * k, I), dtype=torch.float16, device=dev)
+            self.layers[0].forward(self.logits, self.x, out=self.out, workspace=self.ws, probe={"h": h})
+            self.gx = 448 * 6 / float(self.x.float().abs().max())
+            self.gh = 448 * 6 / float(h.float().abs().max())
+            del h
 
     def fwd(self, i, events=None):
         lay = self.layers[i % self.n_sets]
+        if self.w4a4:
+            lay.forward_w4a4(self.logits, self.x, self.gx, self.gh, out=self.out, workspace=self.ws,
+                             events=events)
+            return
         f = lay.forward_w8a8 if self.w8a8 else lay.forward
         f(self.logits, self.x, out=self.out, workspace=self.ws, events=events)
 
@@ -257,7 +271,7 @@ def roofline(lb, dom, dom_ms, decode):
         if lb.w8a8:
             roof["mfma_dtype"] = "fp8 (e4m3 x e4m3)"
             roof["frac_of_fp16_peak"] = round(achieved / PEAK_FP16_TFLOPS, 4)
-    tag = f"{dom}_{wl.fmt}{'_w8a8' if lb.w8a8 else ''}_T{lb.T}"
+    tag = f"{dom}_{wl.fmt}{'_w8a8' if lb.w8a8 else ''}{'_w4a4' if lb.w4a4 else ''}_T{lb.T}"
     roof["traffic"] = counter_traffic(tag)
     roof["kernel"] = dom
     roof["kernel_us"] = round(dom_ms * 1e3, 2)
@@ -274,7 +288,8 @@ def regime_line(lb, iters, flush, graph):
     stage_ms = lb.stages(min(iters, 30))
     dom = max(("gate_up", "down"), key=lambda s: stage_ms[s])
     t = lb.timed(iters, 5, dom)
-    out = {"workload": lb.wl.name + ("_w8a8" if lb.w8a8 else ""), "format": lb.wl.fmt, "tokens": lb.T,
+    out = {"workload": lb.wl.name + ("_w8a8" if lb.w8a8 else "") + ("_w4a4" if lb.w4a4 else ""),
+           "format": lb.wl.fmt, "tokens": lb.T,
            "touched_experts": lb.touched,
            "tokens_per_s": round(lb.T / (t["ms"] * 1e-3), 1), "us_per_step": round(t["ms"] * 1e3, 2)}
     for mode in ("cycled", "warm", "cold"):
@@ -636,6 +651,14 @@ def main():
         res["regimes"].append(line)
         print(f"# prefill_fp8 W8A8 T=4096: {line['us_per_step']} us/step", file=sys.stderr, flush=True)
         del prev, other, w8
+        # NVFP4 W4A4: the NVFP4 layer with 4-bit activations (calibrated global scales)
+        nv = synth.WORKLOADS["nvfp4_zipf"]
+        same = lb.wl.name == nv.name and lb.T == 16384
+        w4 = LayerBench(nv, 16384, dev, share=lb if same else None, w4a4=True)
+        line = regime_line(w4, args.iters, flush, graph=False)
+        res["regimes"].append(line)
+        print(f"# nvfp4_zipf W4A4 T=16384: {line['us_per_step']} us/step", file=sys.stderr, flush=True)
+        del w4
     res["import"] = import_bench(dev)
     print("# import done", file=sys.stderr, flush=True)
     if not args.no_stack:

@@ -231,6 +231,48 @@ mq_status moe_quant_quantize_act(const float *x, int64_t rows, int32_t K, uint8_
                                  struct ihipStream_t *stream);
 
 /*
+ * NVFP4 W4A4: moe_quant_forward for an MQ_W_NVFP4_G16 layer with its
+ * activations quantized to NVFP4 as well, the format the
+ * "clef-flash-NVFP4-Hybrid" card (section "Quantization details") gives its
+ * W4A4 layers and the "clef-omni-fp8" card (table "Which Clef-Omni quant
+ * should I use?") lists for the W4A4 build: E2M1 values, one E4M3 scale per
+ * 16 consecutive values, one FP32 global scale per tensor, the activation
+ * global scales calibrated.  act_gscale13 is the global scale g of the
+ * gate/up input (the hidden rows), act_gscale2 that of the down input (the
+ * SwiGLU intermediate), one per layer, shared by its experts.  For each
+ * token (gate/up) or grouped row (down) and each 16 consecutive features
+ * with maximum magnitude m, in FP32:
+ *   s = RNE-to-E4M3(min((m * g) / 6, 448)),
+ *   code = RNE-to-E2M1((x * g) / s) saturated to +-6 (0 where s = 0),
+ * and the projection sees e2m1(code) * s / g; the intermediate is quantized
+ * from its FP32 value.  The GEMMs multiply the exact products e2m1 * s on the
+ * FP16 matrix units and apply 1 / g to their FP32 sums.  Same arguments,
+ * workspace size and routing as moe_quant_forward (the kernels are the
+ * many-rows-per-expert ones at every batch size).  The probe's h buffer
+ * receives the down input as kept here: FP16 values e2m1(code) * s [T*k, I]
+ * in grouped row order.  Errors: as moe_quant_forward, plus MQ_E_FORMAT for
+ * another weight format and MQ_E_SHAPE for a global scale that is not
+ * finite and positive.
+ */
+mq_status moe_quant_forward_w4a4(const mq_layer *L, const void *router_logits, int32_t logits_dtype,
+                                 const uint16_t *hidden_bf16, const uint16_t *residual_bf16,
+                                 int64_t num_tokens, uint16_t *out_bf16, void *workspace,
+                                 size_t workspace_bytes, float act_gscale13, float act_gscale2,
+                                 const mq_probe *probe, struct ihipStream_t *stream);
+
+/*
+ * Test entry: the NVFP4 activation quantizer of the W4A4 path on FP32 rows
+ * x [rows, K] (device) with global scale gscale, writing the E2M1 codes
+ * packed two per byte, even k in the low nibble, uint8 [rows, K/2], and the
+ * E4M3FN block scales uint8 [rows, K/16] (device, caller-owned): the NVFP4
+ * layout of MQ_W_NVFP4_G16 weights.  K a positive multiple of 16 (at most
+ * 65536); gscale finite and positive.
+ * Errors: MQ_E_SHAPE, MQ_E_NULL, MQ_E_ALIGN (x 16-byte, codes 4-byte), MQ_E_HIP.
+ */
+mq_status moe_quant_quantize_act_nvfp4(const float *x, int64_t rows, int32_t K, float gscale,
+                                       uint8_t *codes, uint8_t *scales, struct ihipStream_t *stream);
+
+/*
  * moe_quant_forward with the router in the library: the logits of the BF16
  * gate that stays unquantized on every card ("clef-omni-int4" card, section
  * "Recipe": ignore_layers=mlp.gate; "clef-omni-NVFP4" card, section "How it

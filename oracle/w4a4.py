@@ -77,9 +77,22 @@ def dequantize_act(codes: np.ndarray, s_codes: np.ndarray, g: float) -> np.ndarr
     return block_values(codes, s_codes) / np.float64(np.float32(g))
 
 
-def _fake_quant(x: np.ndarray, g: float) -> np.ndarray:
+def quantize_dequantize(x: np.ndarray, g: float) -> np.ndarray:
+    """Float64 values of rows ``x`` after NVFP4 quantization with global
+    scale ``g``."""
     c, s = quantize_act(x, g)
     return dequantize_act(c, s, g)
+
+
+def expert_w4a4(xq: np.ndarray, w13: np.ndarray, w2: np.ndarray, g_h: float):
+    """One SwiGLU expert on quantized activation rows ``xq`` [n, H] (their
+    float64 values): h is rounded to FP32, quantized with global scale
+    ``g_h``, and multiplied by the down projection.  Returns (expert output
+    [n, H], h in FP32 [n, I])."""
+    i = w13.shape[0] // 2
+    gu = xq @ w13.T
+    h32 = (moe.silu(gu[:, :i]) * gu[:, i:]).astype(np.float32)
+    return quantize_dequantize(h32, g_h) @ w2.T, h32
 
 
 def intermediate_w4a4(layer: moe.Layer, logits: np.ndarray, x_bf16_bits: np.ndarray, g_x: float):
@@ -87,7 +100,7 @@ def intermediate_w4a4(layer: moe.Layer, logits: np.ndarray, x_bf16_bits: np.ndar
     ascending, tokens ascending inside one), before its quantization."""
     ids, _ = moe.route(logits, layer.top_k)
     perm = moe.permute(ids, layer.num_experts)
-    xq = _fake_quant(moe.bf16_bits_to_f64(x_bf16_bits), g_x)
+    xq = quantize_dequantize(moe.bf16_bits_to_f64(x_bf16_bits), g_x)
     i = layer.intermediate
     h32 = np.empty((len(ids) * layer.top_k, i), dtype=np.float32)
     for e in range(layer.num_experts):
@@ -124,6 +137,17 @@ def moe_forward_w4a4(layer: moe.Layer, logits: np.ndarray, x_bf16_bits: np.ndarr
     if layer.w13.fmt != formats.NVFP4:
         raise ValueError("W4A4 applies to the NVFP4 format")
     ids, w = moe.route(logits, layer.top_k)
-    h32 = intermediate_w4a4(layer, logits, x_bf16_bits, g_x)
-    y = down_from_values(layer, logits, _fake_quant(h32, g_h), residual_bf16_bits)
+    perm = moe.permute(ids, layer.num_experts)
+    xq = quantize_dequantize(moe.bf16_bits_to_f64(x_bf16_bits), g_x)
+    expert_out = np.empty((len(ids) * layer.top_k, layer.hidden), dtype=np.float64)
+    for e in range(layer.num_experts):
+        lo, hi = perm.offsets[e], perm.offsets[e + 1]
+        if hi == lo:
+            continue
+        expert_out[lo:hi], _ = expert_w4a4(xq[perm.sorted_token_ids[lo:hi]],
+                                           formats.dequantize_expert(layer.w13, e),
+                                           formats.dequantize_expert(layer.w2, e), g_h)
+    y = moe.combine(perm, w, expert_out)
+    if residual_bf16_bits is not None:
+        y = y + moe.bf16_bits_to_f64(residual_bf16_bits)
     return y, ids, w

@@ -98,6 +98,53 @@ def oracle_forward_pool(pool, p13, p2, top_k, logits, x_bits):
     return moe.combine(perm, w, expert_out), ids, w
 
 
+def w4a4_expert_job(args):
+    """Worker job: the W4A4 oracle's expert step (oracle.w4a4.expert_w4a4) on
+    one expert's quantized rows, plus the down projection of given
+    intermediate values (teacher forcing).  Returns (expert output, h in
+    FP32, forced output)."""
+    from oracle import w4a4
+    H, I, q, xq, g_h, h_forced = args
+    (w13, s13, g13), (w2, s2, g2) = q
+    p13 = formats.Packed(formats.NVFP4, np.asarray(w13)[None], np.asarray(s13)[None], np.asarray(g13)[None], 2 * I, H)
+    p2 = formats.Packed(formats.NVFP4, np.asarray(w2)[None], np.asarray(s2)[None], np.asarray(g2)[None], H, I)
+    d13 = formats.dequantize_expert(p13, 0)
+    d2 = formats.dequantize_expert(p2, 0)
+    y, h32 = w4a4.expert_w4a4(xq, d13, d2, g_h)
+    return y, h32, (None if h_forced is None else h_forced @ d2.T)
+
+
+def oracle_w4a4_pool(pool, p13, p2, top_k, logits, x_bits, g_x, g_h, h_forced=None):
+    """oracle.w4a4.moe_forward_w4a4 for every token with the per-expert step
+    farmed to ``pool`` (route, permute, activation quantization and combine
+    are the oracle's own functions, in its order), plus, if ``h_forced``
+    (float64 [T*k, I], grouped order) is given, the teacher-forced output
+    oracle.w4a4.down_from_values would give.  Returns (y, y_forced, h32)."""
+    from oracle import w4a4
+    H, I, E = p13.k, p13.n // 2, p13.num_experts
+    ids, w = moe.route(logits, top_k)
+    perm = moe.permute(ids, E)
+    xq = w4a4.quantize_dequantize(moe.bf16_bits_to_f64(x_bits), g_x)
+    futs = {}
+    for e in range(E):
+        lo, hi = perm.offsets[e], perm.offsets[e + 1]
+        if hi > lo:
+            q = ((p13.w[e], p13.scale[e], p13.gscale[e]), (p2.w[e], p2.scale[e], p2.gscale[e]))
+            futs[e] = pool.submit(w4a4_expert_job, (H, I, q, xq[perm.sorted_token_ids[lo:hi]], g_h,
+                                                    None if h_forced is None else h_forced[lo:hi]))
+    R = len(ids) * top_k
+    out = np.empty((R, H))
+    forced = np.empty((R, H)) if h_forced is not None else None
+    h32 = np.empty((R, I), np.float32)
+    for e, f in futs.items():
+        lo, hi = perm.offsets[e], perm.offsets[e + 1]
+        y, h, yf = f.result()
+        out[lo:hi], h32[lo:hi] = y, h
+        if forced is not None:
+            forced[lo:hi] = yf
+    return (moe.combine(perm, w, out), None if forced is None else moe.combine(perm, w, forced), h32)
+
+
 def _single_threaded_blas():
     """Pool initializer: one BLAS thread per worker (the pool supplies the
     parallelism; nested BLAS threads would oversubscribe the cores)."""

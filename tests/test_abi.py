@@ -238,6 +238,30 @@ def test_forward_w8a8_and_quantize_act_reject_before_any_launch(lib):
     assert q(P + 4, 4, 256, P, P, None) == MQ_E_ALIGN
 
 
+def test_forward_w4a4_and_quantize_act_nvfp4_reject_before_any_launch(lib):
+    P = 0x100000
+    st, h = _init(lib, _desc(2))               # FP8: W4A4 needs the NVFP4 format
+    assert st == MQ_OK
+    f = lib.moe_quant_forward_w4a4
+    assert f(h, P, 0, P, None, 4, P, P, 1 << 20, 1.0, 1.0, None, None) == MQ_E_FORMAT
+    lib.moe_quant_destroy(h)
+    st, h = _init(lib, _desc(3))
+    assert st == MQ_OK
+    for g13, g2 in ((0.0, 1.0), (1.0, -2.0), (float("inf"), 1.0), (1.0, float("nan"))):
+        assert f(h, P, 0, P, None, 4, P, P, 1 << 20, g13, g2, None, None) == MQ_E_SHAPE
+    assert f(h, P, 0, P, None, 4, P, P, 16, 1.0, 1.0, None, None) == MQ_E_WORKSPACE
+    assert f(h, P, 0, P, None, 0, P, P, 0, 1.0, 1.0, None, None) == MQ_OK   # T = 0 enqueues nothing
+    lib.moe_quant_destroy(h)
+    q = lib.moe_quant_quantize_act_nvfp4
+    assert q(P, 4, 200, 1.0, P, P, None) == MQ_E_SHAPE        # K not a multiple of 16
+    assert q(P, -1, 256, 1.0, P, P, None) == MQ_E_SHAPE
+    assert q(P, 4, 256, 0.0, P, P, None) == MQ_E_SHAPE
+    assert q(None, 0, 256, 1.0, None, None, None) == MQ_OK
+    assert q(None, 4, 256, 1.0, P, P, None) == MQ_E_NULL
+    assert q(P + 4, 4, 256, 1.0, P, P, None) == MQ_E_ALIGN
+    assert q(P, 4, 256, 1.0, P + 2, P, None) == MQ_E_ALIGN
+
+
 def test_dequantize_rejects(lib):
     st, h = _init(lib, _desc(2))
     assert st == MQ_OK

@@ -23,3 +23,24 @@ def test_pooled_forward_matches_moe_forward():
         assert np.array_equal(ids, ids2) and np.array_equal(w, w2)
         np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-15)
         assert np.array_equal(q[0][0], p13.w[3]) and np.array_equal(q[1][1], p2.scale[3])
+
+
+def test_pooled_w4a4_matches_the_w4a4_oracle():
+    """oracle_w4a4_pool gives moe_forward_w4a4's output, the intermediate of
+    intermediate_w4a4, and down_from_values' teacher-forced output."""
+    from oracle import w4a4
+    from gpu_helpers import oracle_w4a4_pool
+    E, H, I, k, T = 8, 256, 128, 2, 40
+    p13, p2 = quantized_layer(formats.NVFP4, 2, 0, E, H, I)
+    layer = moe.Layer(p13, p2, k)
+    lg = synth.router_logits(2, 0, T, E)
+    x = synth.hidden_bf16(2, 0, T, H)
+    gx, gh = 500.0, 30000.0
+    ref, _, _ = w4a4.moe_forward_w4a4(layer, lg, x, gx, gh)
+    h_ref = w4a4.intermediate_w4a4(layer, lg, x, gx)
+    hf = np.random.default_rng(0).standard_normal((T * k, I))
+    with spawn_pool(2) as pool:
+        got, forced, h32 = oracle_w4a4_pool(pool, p13, p2, k, lg, x, gx, gh, hf)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-15)
+    assert np.array_equal(h32, h_ref)
+    np.testing.assert_allclose(forced, w4a4.down_from_values(layer, lg, hf), rtol=1e-12, atol=1e-15)

@@ -24,7 +24,9 @@ EXPORTED = (
     "moe_quant_forward_noalloc",
     "moe_quant_forward_with_router",
     "moe_quant_forward_w8a8",
+    "moe_quant_forward_w4a4",
     "moe_quant_quantize_act",
+    "moe_quant_quantize_act_nvfp4",
     "moe_quant_import_expert",
     "moe_quant_check",
     "moe_quant_dequantize",
@@ -116,6 +118,12 @@ def load_library():
     lib.moe_quant_forward_w8a8.restype = i32
     lib.moe_quant_quantize_act.argtypes = [vp, i64, i32, vp, vp, vp]
     lib.moe_quant_quantize_act.restype = i32
+    f32 = ctypes.c_float
+    lib.moe_quant_forward_w4a4.argtypes = [vp, vp, i32, vp, vp, i64, vp, vp, sz, f32, f32,
+                                           ctypes.POINTER(Probe), vp]
+    lib.moe_quant_forward_w4a4.restype = i32
+    lib.moe_quant_quantize_act_nvfp4.argtypes = [vp, i64, i32, f32, vp, vp, vp]
+    lib.moe_quant_quantize_act_nvfp4.restype = i32
     lib.moe_quant_check.argtypes = [vp, vp, vp]
     lib.moe_quant_check.restype = i32
     lib.moe_quant_dequantize.argtypes = [vp, i32, i32, vp, vp]
@@ -275,6 +283,29 @@ def quantize_act(x, codes=None, scales=None, stream=None):
     return codes, scales
 
 
+def quantize_act_nvfp4(x, gscale: float, codes=None, scales=None, stream=None):
+    """NVFP4 quantization of float32 rows x [rows, K] with global scale
+    ``gscale`` on the GPU (moe_quant_quantize_act_nvfp4): returns (codes uint8
+    [rows, K/2], two E2M1 codes per byte, even k in the low nibble; E4M3 block
+    scales uint8 [rows, K/16])."""
+    import torch
+    lib = load_library()
+    if x.dim() != 2:
+        raise ValueError("x must be [rows, K]")
+    r, k = x.shape
+    _need(x, "x", (r, k), (torch.float32,))
+    if codes is None:
+        codes = torch.empty((r, k // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((r, k // 16), dtype=torch.uint8, device=x.device)
+    _need(codes, "codes", (r, k // 2), (torch.uint8,))
+    _need(scales, "scales", (r, k // 16), (torch.uint8,))
+    _on_gpu(None, x=x, codes=codes, scales=scales)
+    _check(lib, lib.moe_quant_quantize_act_nvfp4(_ptr(x), r, k, float(gscale), _ptr(codes), _ptr(scales),
+                                                 _stream(stream)))
+    return codes, scales
+
+
 class Layer:
     """One MoE expert layer over packed weights resident on the GPU.
 
@@ -354,6 +385,16 @@ class Layer:
         return self._forward(logits, None, hidden, residual, out, workspace, probe, events,
                              stream, None, w8a8=True)
 
+    def forward_w4a4(self, logits, hidden, act_gscale13: float, act_gscale2: float, residual=None,
+                     out=None, workspace=None, probe: Optional[Dict] = None, events=None,
+                     stream=None):
+        """W4A4 forward of an NVFP4 layer (moe_quant_forward_w4a4): hidden rows
+        and the SwiGLU intermediate quantized to NVFP4 with the calibrated
+        global scales ``act_gscale13`` (gate/up input) and ``act_gscale2``
+        (down input)."""
+        return self._forward(logits, None, hidden, residual, out, workspace, probe, events,
+                             stream, None, w4a4=(float(act_gscale13), float(act_gscale2)))
+
     def forward_with_router(self, router_w, hidden, residual=None, out=None, workspace=None,
                             logits_out=None, probe: Optional[Dict] = None, events=None,
                             stream=None):
@@ -364,7 +405,7 @@ class Layer:
                              stream, logits_out)
 
     def _forward(self, logits, router_w, hidden, residual, out, workspace, probe, events, stream,
-                 logits_out, w8a8=False):
+                 logits_out, w8a8=False, w4a4=None):
         import torch
         if hidden.dim() != 2:
             raise ValueError("hidden must be [T, H]")
@@ -415,10 +456,15 @@ class Layer:
         prp = ctypes.byref(pr) if pr is not None else None
         if router_w is None:
             ldt = MQ_F32 if logits.dtype == torch.float32 else MQ_BF16
-            fn = self._lib.moe_quant_forward_w8a8 if w8a8 else self._lib.moe_quant_forward
-            st = fn(
-                self._h, _ptr(logits), ldt, _ptr(hidden), _ptr(residual), t, _ptr(out),
-                _ptr(workspace), _nbytes(workspace), prp, _stream(stream))
+            if w4a4 is not None:
+                st = self._lib.moe_quant_forward_w4a4(
+                    self._h, _ptr(logits), ldt, _ptr(hidden), _ptr(residual), t, _ptr(out),
+                    _ptr(workspace), _nbytes(workspace), w4a4[0], w4a4[1], prp, _stream(stream))
+            else:
+                fn = self._lib.moe_quant_forward_w8a8 if w8a8 else self._lib.moe_quant_forward
+                st = fn(
+                    self._h, _ptr(logits), ldt, _ptr(hidden), _ptr(residual), t, _ptr(out),
+                    _ptr(workspace), _nbytes(workspace), prp, _stream(stream))
         else:
             st = self._lib.moe_quant_forward_with_router(
                 self._h, _ptr(hidden), _ptr(router_w), _ptr(residual), t, _ptr(out),

@@ -131,6 +131,46 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d, f
   return (uint32_t)w;
 }
 
+// ---------------------------------------------------------------- NVFP4 activations
+// The W4A4 variant of the NVFP4 layer quantizes activations the way the
+// weights are quantized: E2M1 values, one E4M3 scale per 16 consecutive
+// values, and one FP32 global scale g per projection input, a calibrated
+// constant ("clef-flash-NVFP4-Hybrid" card, section "Quantization details").
+// For a group with maximum magnitude m:
+//   s    = RNE-to-E4M3(min((m * g) / 6, 448))  (FP32 multiply, IEEE division)
+//   code = RNE-to-E2M1((x * g) / s)            (FP32 multiply, IEEE division,
+//                                               saturated to +-6; s = 0: 0)
+// The GEMMs multiply e2m1(code) * s, an exact FP16 number (at most 2 + 4
+// significant bits, magnitude within [2^-10, 6 * 448]), and apply 1 / g to
+// their FP32 sums.
+struct Nvfp4Scale {
+  uint32_t code;  // E4M3FN bits
+  float s;        // its value
+};
+__device__ __forceinline__ Nvfp4Scale nvfp4_act_scale(float amax, float g) {
+  const float u = fminf((amax * g) / 6.f, 448.f);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(u, 0.f, 0, false) & 0xFFu;
+  return {c, (float)e4m3_to_f16(c)};
+}
+// E2M1 code of (x * g) / s: the magnitude is the count of rounding boundaries
+// below |q| (the midpoints of the grid 0, 0.5, 1, 1.5, 2, 3, 4, 6), each tie
+// going to the even code; the sign is q's sign bit.
+__device__ __forceinline__ uint32_t e2m1_code(float x, float g, float s) {
+  if (s == 0.f) return 0u;
+  const float q = (x * g) / s;
+  const float a = fminf(fabsf(q), 6.f);
+  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                     (uint32_t)(a > 5.f);
+  return c | ((__float_as_uint(q) >> 28) & 8u);
+}
+// Value of an E2M1 code as FP32.
+__device__ __forceinline__ float e2m1_value(uint32_t c) {
+  const uint32_t m = c & 7u;
+  const float a = m < 4u ? 0.5f * (float)m : m < 6u ? (float)(m - 2u) : m == 6u ? 4.f : 6.f;
+  return (c & 8u) ? -a : a;
+}
+
 // ---------------------------------------------------------------- misc
 // silu(z) = z / (1 + e^-z); the reciprocal is the hardware one (1 ulp), which
 // is far below the FP16 rounding of the SwiGLU intermediate it feeds.

@@ -50,6 +50,8 @@ struct GemmArgs {
   _Float16 *partial;      // down output [R, H] indexed by slot (FP16, routing-weighted)
   uint32_t *flags;
   int tiles;              // decode: column tiles per expert; prefill: N tiles
+  float hq_g;             // W4A4 gate/up: global scale of the NVFP4 quantization of h
+  float a_inv;            // down: factor on the sums (W4A4: 1 / the global scale of h; else 1)
 };
 
 // Saturate to the FP16 range, remembering whether anything was clamped.
@@ -442,7 +444,8 @@ __device__ __forceinline__ float row_pow2(float m, float *inv) {
 //
 // gate/up (STAGE 0): wave w of column tile nt holds gate columns
 // 16 TN (WPB nt + w) + [0, 16 TN) in tiles [0, TN/2) and the matching up
-// columns in the others, so SwiGLU runs in registers.  down (STAGE 1): wave w
+// columns in the others, so SwiGLU runs in registers (STAGE 2: the same, with
+// h quantized to NVFP4 activations for the W4A4 layer).  down (STAGE 1): wave w
 // holds output columns 32 TN (WPB nt + w) + [0, 32 TN); its rows go to
 // scattered partial slots through an LDS transpose.  A wave whose columns lie
 // past the end (I or H not a multiple of the block width) stages activations
@@ -510,12 +513,12 @@ void gemm_prefill_wide(GemmArgs a) {
 
   // ---- the wave's columns: global weight row of this lane in each tile
   // gate/up: first gate (h) column of the wave; down: first output column
-  const int cb = STAGE == 0 ? nt * (BC / 2) + wave * (WC / 2) : nt * BC + wave * WC;
-  const bool wvalid = cb < (STAGE == 0 ? a.I : N);  // wave-uniform
+  const int cb = STAGE != 1 ? nt * (BC / 2) + wave * (WC / 2) : nt * BC + wave * WC;
+  const bool wvalid = cb < (STAGE != 1 ? a.I : N);  // wave-uniform
   int gr[TN];
 #pragma unroll
   for (int tn = 0; tn < TN; ++tn) {
-    const int c = STAGE == 0 ? (tn < TH ? cb : a.I + cb) + (tn % TH) * 32 + j : cb + tn * 32 + j;
+    const int c = STAGE != 1 ? (tn < TH ? cb : a.I + cb) + (tn % TH) * 32 + j : cb + tn * 32 + j;
     gr[tn] = wvalid ? c : j;  // a row that exists; never stored
   }
 
@@ -553,7 +556,7 @@ void gemm_prefill_wide(GemmArgs a) {
     const int rr = (tid >> 3) + 8 * WPB * p;
     const int r = rbeg + (rr < nrows ? rr : nrows - 1);
     // gate/up: the token's x16 row; down: the grouped h row
-    asrc[p] = a.a_src + (STAGE == 0 ? (size_t)a.rowinfo[r].y : (size_t)r) * K + (tid & 7) * 8;
+    asrc[p] = a.a_src + (STAGE != 1 ? (size_t)a.rowinfo[r].y : (size_t)r) * K + (tid & 7) * 8;
   }
   // ---- weight and scale streams of the lane's TN columns
   const uint8_t *wsrc[TN];
@@ -779,6 +782,47 @@ void gemm_prefill_wide(GemmArgs a) {
         }
       }
     }
+  } else if constexpr (STAGE == 2) {
+    // W4A4 (NVFP4 only): h quantized to NVFP4 with global scale a.hq_g, stored
+    // as the FP16 values e2m1(code) * s (exact, never saturating).  A 32-wide
+    // slice of h holds two groups of 16: columns [0, 16) in registers g4 = 0,
+    // 1 and [16, 32) in g4 = 2, 3 of lanes j and j + 32 (the same row, so both
+    // lanes skip or keep a row together).
+    static_assert(FMT == FMT_NVFP4, "W4A4 is the NVFP4 layer's variant");
+    if (wvalid) {
+#pragma unroll
+      for (int tm = 0; tm < 4; ++tm) {
+        const int row = tm * 32 + j;
+        if (row >= nrows) continue;
+        const int r = rbeg + row;
+        const float rsc = __builtin_bit_cast(float, a.rowinfo[r].z) * ginv;
+#pragma unroll
+        for (int tn = 0; tn < TH; ++tn) {
+          float hv[16];
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            hv[v] = silu(acc[tn][tm][v] * rsc) * (acc[tn + TH][tm][v] * rsc);
+          float m0 = 0.f, m1 = 0.f;
+#pragma unroll
+          for (int v = 0; v < 8; ++v) {
+            m0 = fmaxf(m0, fabsf(hv[v]));
+            m1 = fmaxf(m1, fabsf(hv[8 + v]));
+          }
+          m0 = fmaxf(m0, __shfl_xor(m0, 32, 64));
+          m1 = fmaxf(m1, __shfl_xor(m1, 32, 64));
+          const float s0 = nvfp4_act_scale(m0, a.hq_g).s, s1 = nvfp4_act_scale(m1, a.hq_g).s;
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const float sg = g4 < 2 ? s0 : s1;
+            h2 o[2];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              o[i >> 1][i & 1] = (_Float16)(e2m1_value(e2m1_code(hv[4 * g4 + i], a.hq_g, sg)) * sg);
+            *(u2 *)(a.h_out + (size_t)r * a.I + cb + tn * 32 + 8 * g4 + cl) = u2{as_u32(o[0]), as_u32(o[1])};
+          }
+        }
+      }
+    }
   } else {
     // down: the rows go to scattered slots of the partial buffer, so each
     // 32-row slice of the wave's tile is converted and transposed through LDS
@@ -796,7 +840,7 @@ void gemm_prefill_wide(GemmArgs a) {
         if (tm * 32 >= nrows) break;
         const int row = tm * 32 + j;
         float rsc = 0.f;  // rows past the expert's end: zeros, never stored
-        if (row < nrows) rsc = __builtin_bit_cast(float, a.rowinfo[rbeg + row].w) * ginv;
+        if (row < nrows) rsc = __builtin_bit_cast(float, a.rowinfo[rbeg + row].w) * ginv * a.a_inv;
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int c4 = 8 * g4 + cl;
@@ -949,6 +993,8 @@ static GemmArgs make_args(const LayerDims &L, const FwdPtrs &P, const Workspace 
   a.partial = (_Float16 *)(ws + W.partial);
   a.flags = P.flags;
   a.tiles = 0;
+  a.hq_g = P.act_g2;
+  a.a_inv = stage == 1 && P.act_g2 > 0.f ? 1.f / P.act_g2 : 1.f;
   return a;
 }
 
@@ -1076,7 +1122,7 @@ static hipError_t run_prefill_wide(GemmArgs a, int64_t R, const GemmLaunch &s) {
   using Shape = WideShape<TN, WPB>;
   constexpr int BC = Shape::BC;
   if (a.K % (Shape::SPB * kWK) != 0) return hipErrorInvalidValue;  // K fills whole LDS buffers
-  a.tiles = STAGE == 0 ? (a.I + BC / 2 - 1) / (BC / 2) : (a.H + BC - 1) / BC;
+  a.tiles = STAGE != 1 ? (a.I + BC / 2 - 1) / (BC / 2) : (a.H + BC - 1) / BC;
   const int64_t max_mt = R / kBM + a.E;  // >= sum_e ceil(n_e / kBM)
   const int64_t grid = 8 * ((max_mt * a.tiles + 7) / 8);
   constexpr size_t lds = Shape::LDS;  // above the default limit
@@ -1106,6 +1152,12 @@ static hipError_t dispatch(const LayerDims &L, const FwdPtrs &P, const Workspace
   // down (K = I = 768): 4 waves per block, two blocks per CU, whose prologue
   // and epilogue overlap each other (8 waves measured slower there).
   constexpr int WPB = STAGE == 0 ? 8 : 4;
+  if constexpr (STAGE == 0) {
+    if (P.act_g13 > 0.f) {  // W4A4: h quantized in the epilogue
+      if (L.fmt != FMT_NVFP4) return hipErrorInvalidValue;
+      return run_prefill_wide<FMT_NVFP4, 2, WPB, 2>(a, R, s);
+    }
+  }
   switch (L.fmt) {
     case FMT_INT4: return run_prefill_wide<FMT_INT4, 2, WPB, STAGE>(a, R, s);
     case FMT_FP8: return run_prefill_wide<FMT_FP8, 2, WPB, STAGE>(a, R, s);

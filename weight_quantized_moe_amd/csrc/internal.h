@@ -89,6 +89,7 @@ struct FwdPtrs {
   const uint16_t *gate_w;  // BF16 router weight [E, H]: logits computed in-library (else null)
   float *p_logits;         // probe: the in-library logits [T, E] (may be null)
   int w8a8;                // FP8 layer with dynamic 1x128 FP8 activations
+  float act_g13, act_g2;   // NVFP4 W4A4: global scales of the gate/up and down inputs (0: W4A16)
   const uint16_t *hidden;
   const uint16_t *residual;
   uint16_t *out;
@@ -126,6 +127,8 @@ hipError_t launch_import_expert(const LayerDims &L, int e, const mq_src_proj &ga
 void raise_lds_limit(const void *f);
 hipError_t launch_quant_act(const float *x, int64_t rows, int K, uint8_t *codes, float *scales,
                             hipStream_t s);
+hipError_t launch_quant_act_nvfp4(const float *x, int64_t rows, int K, float g, uint8_t *codes,
+                                  uint8_t *scales, hipStream_t s);
 hipError_t launch_w8a8_gate_up(const LayerDims &L, const FwdPtrs &P, const Workspace &W,
                                const GemmLaunch &s);
 hipError_t launch_w8a8_down(const LayerDims &L, const FwdPtrs &P, const Workspace &W,
@@ -141,7 +144,8 @@ mq_status forward_impl(const mq_layer *L, const void *router_logits, int32_t log
                        int64_t num_tokens, uint16_t *out_bf16, void *workspace,
                        size_t workspace_bytes, const mq_probe *probe, uint32_t *flags,
                        hipStream_t stream, const uint16_t *gate_w = nullptr,
-                       float *logits_out = nullptr, int w8a8 = 0);
+                       float *logits_out = nullptr, int w8a8 = 0, float act_g13 = 0.f,
+                       float act_g2 = 0.f);
 // Record a status and its one-line explanation for moe_quant_last_error().
 mq_status fail(mq_status s, const char *fmt, ...);
 void clear_error();

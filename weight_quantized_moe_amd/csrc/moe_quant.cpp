@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <new>
@@ -178,7 +179,7 @@ mq_status mq::forward_impl(const mq_layer *L, const void *router_logits, int32_t
                            int64_t num_tokens, uint16_t *out_bf16, void *workspace,
                            size_t workspace_bytes, const mq_probe *probe, uint32_t *flags,
                            hipStream_t stream, const uint16_t *gate_w, float *logits_out,
-                           int w8a8) {
+                           int w8a8, float act_g13, float act_g2) {
   if (!L) return fail(MQ_E_NULL, "forward: NULL layer handle");
   if (num_tokens < 0 || num_tokens > kMaxTokens)
     return fail(MQ_E_SHAPE, "forward: num_tokens %lld outside [0, %lld]", (long long)num_tokens,
@@ -217,6 +218,8 @@ mq_status mq::forward_impl(const mq_layer *L, const void *router_logits, int32_t
   P.gate_w = gate_w;
   P.p_logits = logits_out;
   P.w8a8 = w8a8;
+  P.act_g13 = act_g13;
+  P.act_g2 = act_g2;
   P.hidden = hidden_bf16;
   P.residual = residual_bf16;
   P.out = out_bf16;
@@ -232,7 +235,8 @@ mq_status mq::forward_impl(const mq_layer *L, const void *router_logits, int32_t
     P.p_h = probe->h;
   }
   hipStream_t s = stream;
-  const bool decode = mq::use_decode_path(num_tokens, D.E, D.k, D.H, D.I);
+  // the W4A4 variant runs the many-rows-per-expert kernels at every batch size
+  const bool decode = act_g13 == 0.f && mq::use_decode_path(num_tokens, D.E, D.k, D.H, D.I);
   auto ev = [&](int stage, int after) {
     if (probe && probe->events[2 * stage + after])
       (void)hipEventRecord((hipEvent_t)probe->events[2 * stage + after], s);
@@ -288,6 +292,44 @@ mq_status moe_quant_forward_w8a8(const mq_layer *L, const void *router_logits, i
   return mq::forward_impl(L, router_logits, logits_dtype, hidden_bf16, residual_bf16, num_tokens,
                           out_bf16, workspace, workspace_bytes, probe, nullptr, (hipStream_t)stream,
                           nullptr, nullptr, 1);
+}
+
+static bool valid_gscale(float g) { return std::isfinite(g) && g > 0.f; }
+
+mq_status moe_quant_forward_w4a4(const mq_layer *L, const void *router_logits, int32_t logits_dtype,
+                                 const uint16_t *hidden_bf16, const uint16_t *residual_bf16,
+                                 int64_t num_tokens, uint16_t *out_bf16, void *workspace,
+                                 size_t workspace_bytes, float act_gscale13, float act_gscale2,
+                                 const mq_probe *probe, struct ihipStream_t *stream) {
+  if (!L) return fail(MQ_E_NULL, "forward_w4a4: NULL layer handle");
+  if (L->d.format != MQ_W_NVFP4_G16)
+    return fail(MQ_E_FORMAT, "forward_w4a4: W4A4 applies to MQ_W_NVFP4_G16 layers (format %d)", L->d.format);
+  if (!valid_gscale(act_gscale13) || !valid_gscale(act_gscale2))
+    return fail(MQ_E_SHAPE, "forward_w4a4: activation global scales %g and %g must be finite and positive",
+                (double)act_gscale13, (double)act_gscale2);
+  return mq::forward_impl(L, router_logits, logits_dtype, hidden_bf16, residual_bf16, num_tokens,
+                          out_bf16, workspace, workspace_bytes, probe, nullptr, (hipStream_t)stream,
+                          nullptr, nullptr, 0, act_gscale13, act_gscale2);
+}
+
+mq_status moe_quant_quantize_act_nvfp4(const float *x, int64_t rows, int32_t K, float gscale,
+                                       uint8_t *codes, uint8_t *scales, struct ihipStream_t *stream) {
+  if (rows < 0 || rows > ((int64_t)1 << 30) || K <= 0 || K % 16 || K > 65536)
+    return fail(MQ_E_SHAPE, "quantize_act_nvfp4: rows %lld and K %d (K a positive multiple of 16, at most 65536)",
+                (long long)rows, K);
+  if (!valid_gscale(gscale))
+    return fail(MQ_E_SHAPE, "quantize_act_nvfp4: global scale %g must be finite and positive", (double)gscale);
+  if (rows == 0) {
+    g_err[0] = 0;
+    return MQ_OK;
+  }
+  if (!x || !codes || !scales) return fail(MQ_E_NULL, "quantize_act_nvfp4: NULL argument");
+  if (!aligned(x, 16) || !aligned(codes, 4))
+    return fail(MQ_E_ALIGN, "quantize_act_nvfp4: x 16-byte, codes 4-byte aligned");
+  const hipError_t e = mq::launch_quant_act_nvfp4(x, rows, K, gscale, codes, scales, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(MQ_E_HIP, "quantize_act_nvfp4: %s", hipGetErrorString(e));
+  g_err[0] = 0;
+  return MQ_OK;
 }
 
 mq_status moe_quant_quantize_act(const float *x, int64_t rows, int32_t K, uint8_t *codes, float *scales,

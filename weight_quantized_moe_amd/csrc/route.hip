@@ -236,6 +236,85 @@ __device__ __forceinline__ void rows_to_fp8(const uint16_t *__restrict__ hidden,
   }
 }
 
+// W4A4: the wave's 4 hidden rows as NVFP4 activations with global scale g
+// (see nvfp4_act_scale), written as the FP16 values e2m1(code) * s into x16
+// [T, H] (exact; natural k order, the NVFP4 GEMMs' operand order), with
+// rowscale[t] = 1 / g for the GEMM to apply to its sums.  Each pass covers
+// 512 columns of a row: lane l holds columns 8 l + [0, 8), so lanes 2i and
+// 2i + 1 hold one group of 16.
+__device__ __forceinline__ void rows_to_nvfp4(const uint16_t *__restrict__ hidden, int t0, int T,
+                                              int H, int lane, float g, _Float16 *__restrict__ x16,
+                                              float *__restrict__ rowscale) {
+  for (int r = 0; r < 4; ++r) {
+    const int t = t0 + r;
+    if (t >= T) break;  // wave-uniform
+    if (lane == 0) rowscale[t] = 1.f / g;
+    for (int c0 = 0; c0 < H; c0 += 512) {
+      const int c = c0 + lane * 8;
+      const bool ok = c < H;  // whole 2-lane groups (H is a multiple of 128)
+      const u4 v = ok ? *(const u4 *)(hidden + (size_t)t * H + c) : u4{0u, 0u, 0u, 0u};
+      float f[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f[2 * i] = bf16_to_f32(v[i] & 0xFFFFu);
+        f[2 * i + 1] = bf16_to_f32(v[i] >> 16);
+      }
+      float m = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
+      m = fmaxf(m, __shfl_xor(m, 1, 64));
+      const Nvfp4Scale sc = nvfp4_act_scale(m, g);
+      u4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const h2 pr = {(_Float16)(e2m1_value(e2m1_code(f[2 * i], g, sc.s)) * sc.s),
+                       (_Float16)(e2m1_value(e2m1_code(f[2 * i + 1], g, sc.s)) * sc.s)};
+        o[i] = as_u32(pr);
+      }
+      if (ok) *(u4 *)(x16 + (size_t)t * H + c) = o;
+    }
+  }
+}
+
+// Test entry: FP32 rows [rows, K] -> NVFP4 codes (packed two per byte, low
+// nibble first, [rows, K/2]) and E4M3 block scales [rows, K/16], with the
+// group arithmetic of rows_to_nvfp4 and the W4A4 gate/up epilogue.  One wave
+// per (row, 512-column pass).
+__global__ __launch_bounds__(256) void quant_act_nvfp4_kernel(const float *__restrict__ x, int64_t rows,
+                                                              int K, float g, uint8_t *__restrict__ codes,
+                                                              uint8_t *__restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int passes = (K + 511) / 512;
+  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wid >= rows * passes) return;  // wave-uniform
+  const int64_t row = wid / passes;
+  const int c = (int)(wid % passes) * 512 + lane * 8;
+  const bool ok = c < K;  // K a multiple of 16: lanes 2i and 2i + 1 agree
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = ok ? x[row * K + c + i] : 0.f;
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
+  m = fmaxf(m, __shfl_xor(m, 1, 64));
+  const Nvfp4Scale sc = nvfp4_act_scale(m, g);
+  uint32_t w = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w |= e2m1_code(f[i], g, sc.s) << (4 * i);
+  if (ok) {
+    *(uint32_t *)(codes + row * (K / 2) + c / 2) = w;
+    if ((lane & 1) == 0) scales[row * (K / 16) + c / 16] = (uint8_t)sc.code;
+  }
+}
+
+hipError_t launch_quant_act_nvfp4(const float *x, int64_t rows, int K, float g, uint8_t *codes,
+                                  uint8_t *scales, hipStream_t s) {
+  const int64_t waves = rows * ((K + 511) / 512);
+  hipLaunchKernelGGL(quant_act_nvfp4_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, x, rows,
+                     K, g, codes, scales);
+  return hipGetLastError();
+}
+
 // Test entry: FP32 rows [rows, K] -> dynamic 1x128 FP8 codes and scales, with
 // the same group arithmetic as rows_to_fp8 and the W8A8 GEMM epilogue.  One
 // wave per (row, 512-column pass).
@@ -307,7 +386,8 @@ __global__ __launch_bounds__(256) void route_kernel(const void *__restrict__ log
                                                     float *__restrict__ rowscale,
                                                     uint32_t *__restrict__ flags,
                                                     int32_t *__restrict__ p_ids,
-                                                    float *__restrict__ p_w, int stage_rows) {
+                                                    float *__restrict__ p_w, int stage_rows,
+                                                    float act_g) {
   const int lane = threadIdx.x & 63, li = lane & 15;
   const int tpb = blockDim.x >> 4;  // tokens per block: 16 lanes each
   const int t = blockIdx.x * tpb + (threadIdx.x >> 4);
@@ -318,6 +398,11 @@ __global__ __launch_bounds__(256) void route_kernel(const void *__restrict__ log
   if (stage_rows == 3) {  // W8A8: FP8 codes and scales of the hidden rows
     if (t < T) topk16<kPer, kBf16Logits>(logits, t, E, k, li, ids, wts, p_ids, p_w);
     rows_to_fp8(hidden, t0, T, H, lane, (uint8_t *)x16, (float *)((uint8_t *)x16 + (size_t)T * H));
+    return;
+  }
+  if (stage_rows == 4) {  // W4A4: the hidden rows as NVFP4 activations
+    if (t < T) topk16<kPer, kBf16Logits>(logits, t, E, k, li, ids, wts, p_ids, p_w);
+    rows_to_nvfp4(hidden, t0, T, H, lane, act_g, x16, rowscale);
     return;
   }
   if (stage_rows != 0 && H <= kRowRegsMaxH) {
@@ -663,7 +748,7 @@ static hipError_t route_dispatch(const LayerDims &L, const FwdPtrs &P, const Wor
   hipLaunchKernelGGL((route_kernel<kPer, kBf16, kPerm>), dim3((P.T + tpb - 1) / tpb), dim3(threads), 0, s,
                      P.logits, P.hidden, P.T, L.E, L.H, L.k, (int32_t *)(ws + W.topk_ids),
                      (float *)(ws + W.topk_w), (_Float16 *)(ws + W.x16), (float *)(ws + W.rowscale),
-                     P.flags, P.p_ids, P.p_w, stage_rows);
+                     P.flags, P.p_ids, P.p_w, stage_rows, P.act_g13);
   return hipGetLastError();
 }
 
@@ -711,8 +796,9 @@ hipError_t launch_route(const LayerDims &L, const FwdPtrs &P, const Workspace &W
                         hipStream_t s) {
   // prefill: FP16 rows and their scales (1); decode with H <= 2048: the
   // scales only (2), the decode gate/up GEMM converts the rows it stages;
-  // larger decode rows: the GEMM finds the scales too (0)
-  const int stage_rows = P.w8a8 ? 3 : !decode ? 1 : L.H <= kRowRegsMaxH ? 2 : 0;
+  // larger decode rows: the GEMM finds the scales too (0); W8A8: FP8 codes
+  // and scales (3); W4A4: NVFP4 values and 1 / g (4)
+  const int stage_rows = P.w8a8 ? 3 : P.act_g13 > 0.f ? 4 : !decode ? 1 : L.H <= kRowRegsMaxH ? 2 : 0;
   if (P.gate_w && P.T >= kGateFusedMinT)  // router GEMM fused with the top-k
     return L.fmt == FMT_INT4 ? gate_route_dispatch<true>(L, P, W, stage_rows, s)
                              : gate_route_dispatch<false>(L, P, W, stage_rows, s);
