@@ -454,13 +454,13 @@ __device__ __forceinline__ float row_pow2(float m, float *inv) {
 constexpr int kWK = 64;  // k step
 
 // Shape of a variant with TN 32-column tiles per wave and WPB waves per block:
-// k steps per activation buffer (one barrier each), LDS row stride in halves,
+// SPB k steps per activation buffer (one barrier each), LDS row stride in halves,
 // bytes of one buffer, weight columns per block, dynamic LDS per block, and
 // the activation staging passes (each thread stages 16 bytes of one row per
 // pass; a pass covers 8 WPB rows).
-template <int TN, int WPB>
+template <int TN, int WPB, int SPB_>
 struct WideShape {
-  static constexpr int SPB = TN == 4 ? 4 : 2;
+  static constexpr int SPB = SPB_;
   static constexpr int LD = SPB * kWK + 8;
   static constexpr size_t ABUF = (size_t)kBM * LD * 2;
   static constexpr int BC = WPB * 32 * TN;
@@ -479,10 +479,10 @@ __device__ __forceinline__ int wide_koff(int s, int hh) {
   return FMT == FMT_FP8 ? 16 * hh + 8 * (s & 1) + 32 * (s >> 1) : 32 * hh + 8 * s;
 }
 
-template <int FMT, int TN, int WPB, int STAGE>
+template <int FMT, int TN, int WPB, int STAGE, int SPB_>
 __global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(4 / TN, 4 / TN)))
 void gemm_prefill_wide(GemmArgs a) {
-  using Shape = WideShape<TN, WPB>;
+  using Shape = WideShape<TN, WPB, SPB_>;
   constexpr int SPB = Shape::SPB, LD = Shape::LD, BC = Shape::BC, AP = Shape::AP;
   constexpr int WC = 32 * TN, TH = TN / 2;  // columns per wave; gate (and up) tiles per wave
   constexpr size_t ABUF = Shape::ABUF;
@@ -1117,9 +1117,9 @@ static hipError_t run_decode_ks(GemmArgs a, int slots, const GemmLaunch &s) {
   }
 }
 
-template <int FMT, int TN, int WPB, int STAGE>
-static hipError_t run_prefill_wide(GemmArgs a, int64_t R, const GemmLaunch &s) {
-  using Shape = WideShape<TN, WPB>;
+template <int FMT, int TN, int WPB, int STAGE, int SPB>
+static hipError_t run_prefill_wide1(GemmArgs a, int64_t R, const GemmLaunch &s) {
+  using Shape = WideShape<TN, WPB, SPB>;
   constexpr int BC = Shape::BC;
   if (a.K % (Shape::SPB * kWK) != 0) return hipErrorInvalidValue;  // K fills whole LDS buffers
   a.tiles = STAGE != 1 ? (a.I + BC / 2 - 1) / (BC / 2) : (a.H + BC - 1) / BC;
@@ -1127,10 +1127,21 @@ static hipError_t run_prefill_wide(GemmArgs a, int64_t R, const GemmLaunch &s) {
   const int64_t grid = 8 * ((max_mt * a.tiles + 7) / 8);
   constexpr size_t lds = Shape::LDS;  // above the default limit
   static_assert(lds <= kMaxLdsBytes, "prefill tile fits in LDS");
-  raise_lds_limit((const void *)gemm_prefill_wide<FMT, TN, WPB, STAGE>);
-  hipExtLaunchKernelGGL((gemm_prefill_wide<FMT, TN, WPB, STAGE>), dim3((unsigned)grid), dim3(64 * WPB),
+  raise_lds_limit((const void *)gemm_prefill_wide<FMT, TN, WPB, STAGE, SPB>);
+  hipExtLaunchKernelGGL((gemm_prefill_wide<FMT, TN, WPB, STAGE, SPB>), dim3((unsigned)grid), dim3(64 * WPB),
                         (uint32_t)lds, s.stream, s.start, s.stop, 0u, a);
   return hipGetLastError();
+}
+
+// gate/up (one 8-wave block per CU, so its LDS is free to take): activation
+// buffers of four k steps, one barrier per four steps, where K allows;
+// otherwise, and for the down projection (two blocks per CU), two.
+template <int FMT, int TN, int WPB, int STAGE>
+static hipError_t run_prefill_wide(GemmArgs a, int64_t R, const GemmLaunch &s) {
+  if constexpr (STAGE != 1 && TN == 2 && WPB == 8) {
+    if (a.K % (4 * kWK) == 0) return run_prefill_wide1<FMT, TN, WPB, STAGE, 4>(a, R, s);
+  }
+  return run_prefill_wide1<FMT, TN, WPB, STAGE, TN == 4 ? 4 : 2>(a, R, s);
 }
 
 template <int STAGE>

@@ -52,24 +52,60 @@ struct W8Args {
 };
 
 constexpr int kW8BM = 128;   // grouped rows per M tile (= kPrefillBM: the mtile prefix)
+constexpr int kW8BN = 256;   // weight rows per block (gate/up: 128 gate + 128 up; down: 256 outputs)
 constexpr int kW8K = 128;    // k step = one scale block
-constexpr int kW8LD = 144;   // LDS row stride of the activation tile, bytes
-constexpr int kW8MaxG = kMaxGemmK / 128;
+constexpr int kW8Stages = 3; // k steps in flight through LDS
+// one stage: activation codes [128 rows][128 B], weight codes [256 rows][128 B],
+// activation scales [128]
+constexpr int kW8ABytes = kW8BM * kW8K;
+constexpr int kW8WBytes = kW8BN * kW8K;
+constexpr int kW8StageBytes = kW8ABytes + kW8WBytes + kW8BM * 4;
 static_assert(kW8BM == kPrefillBM, "tiles follow the grouping's M-tile prefix");
+constexpr int kW8MaxG = kMaxGemmK / kW8K;
+constexpr int kW8Lds = kW8Stages * kW8StageBytes + 4 * kW8BM * 4 + 2 * kW8MaxG * 4;
+static_assert(kW8Lds <= kMaxLdsBytes, "stages fit in LDS");
 
 __device__ __forceinline__ f16v mfma_fp8(const i8v &a, const i8v &b, const f16v &c) {
   // E8M0 scale 127 = 2^0 on both operands: the plain E4M3 x E4M3 product
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
+// LDS position (16-byte slot) of chunk c (16 bytes of k) of row r of a stage
+// array: rows of 8 slots, the chunk index XOR-swizzled by bits 1..3 of the row
+// so that 16 consecutive rows reading the same chunk hit distinct banks.
+__device__ __forceinline__ int w8_slot(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+// Asynchronous copy of 16 (or 4) bytes per lane from global memory into LDS
+// at lds + 16 (4) * lane; completion is tracked by the wave's vmcnt.
+__device__ __forceinline__ void dma16(const void *g, unsigned char *lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void *)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void *g, unsigned char *lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void *)lds, 4, 0, 0);
+}
+// s_waitcnt vmcnt(n), other counters left alone
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Main loop: k step t's operands (activation codes and scales, weight codes)
+// are copied into stage t % 3 by the block's waves, global memory straight
+// into LDS, two k steps ahead of their use; one barrier per k step, after
+// which every wave reads its MFMA operands from the stage.  Per k step a wave
+// issues 2 activation and 4 weight copies of 1 KB (waves 0 and 1 one more of
+// 256 B for the activation scales).
 template <int STAGE>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_w8a8(W8Args a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  uint8_t *abuf = smem;                                         // [2][128][kW8LD]
-  float *rsc = (float *)(smem + 2 * kW8BM * kW8LD);             // [128][G] activation scales of the tile rows
-  float *hmax = rsc + kW8BM * kW8MaxG;                          // [4][128] (gate/up)
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  float *hmax = (float *)(smem + kW8Stages * kW8StageBytes);   // [4][128] (gate/up)
+  float *sws = hmax + 4 * kW8BM;                                // [2][G]: the block's weight scales
+  // the wave index as a scalar, so that per-wave addresses and the weight
+  // scale loads stay in scalar registers
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int cg = wave & 3, rh = wave >> 2, j = lane & 31, hh = lane >> 5;
   // ---- tile of this block (dealt to the 8 XCDs in contiguous ranges)
   const int NT = a.tiles;
@@ -90,63 +126,78 @@ void gemm_w8a8(W8Args a) {
   const int nrows = min(kW8BM, a.offsets[e + 1] - rbeg);
   const int K = a.K, N = a.N, G = K / kW8K, nK = G;
 
-  // ---- the wave's weight rows
-  const int cb = STAGE == 0 ? nt * 128 + cg * 32 : nt * 256 + cg * 64;  // gate/up: first h column
-  const bool wvalid = cb < (STAGE == 0 ? a.I : N);                      // wave-uniform
-  int gr[2];
+  // ---- the wave's weight rows (stage-local 0..255) and their block scales
+  // gate/up: wave cg holds h columns cb + [0, 32): gate rows 32 cg + [0, 32),
+  // up rows 128 + 32 cg + [0, 32) of the stage; down: rows 64 cg + [0, 64)
+  const int cb = STAGE == 0 ? nt * 128 + cg * 32 : nt * 256 + cg * 64;
+  const bool wvalid = cb < (STAGE == 0 ? a.I : N);  // wave-uniform
+  int wrow[2], wblk[2];  // stage row of each tile; its 128-row weight block (0 or 1) of the block's two
 #pragma unroll
   for (int tn = 0; tn < 2; ++tn) {
-    const int c = STAGE == 0 ? (tn == 0 ? cb : a.I + cb) + j : cb + 32 * tn + j;
-    gr[tn] = wvalid ? c : j;  // a row that exists; never stored
+    wrow[tn] = STAGE == 0 ? 128 * tn + 32 * cg : 64 * cg + 32 * tn;
+    wblk[tn] = STAGE == 0 ? tn : cg >> 1;
   }
-  const uint8_t *wsrc[2];
-  const float *wsc[2];  // block scales of the tile's 128-row weight block (wave-uniform)
-#pragma unroll
-  for (int tn = 0; tn < 2; ++tn) {
-    wsrc[tn] = a.w + ((size_t)e * N + gr[tn]) * K + 32 * hh;
-    const int n0 = STAGE == 0 ? (tn == 0 ? cb : a.I + cb) : cb + 32 * tn;
-    wsc[tn] = a.wscale + ((size_t)e * (N / 128) + (wvalid ? n0 : 0) / 128) * G;
+  // the block's two weight blocks' scales [2][G] into LDS (gate/up: the gate
+  // block of h columns nt * 128 + [0, 128) and its up block; down: weight
+  // rows nt * 256 + [0, 128) and [128, 256)); blocks past the end read as 0
+  for (int idx = tid; idx < 2 * G; idx += 512) {
+    const int b = idx / G, g = idx - b * G;
+    const int n0 = STAGE == 0 ? (b == 0 ? nt * 128 : a.I + nt * 128) : nt * 256 + 128 * b;
+    const bool ok = STAGE == 0 ? nt * 128 < a.I : n0 < N;
+    sws[idx] = ok ? a.wscale[((size_t)e * (N / 128) + n0 / 128) * G + g] : 0.f;
   }
 
-  // ---- activation rows of the tile: row (tid >> 3) + 64 p, 16-byte chunk tid & 7
+  // ---- copy sources of this lane: activation copies q = 2 wave + [0, 2)
+  // and weight copies q = 4 wave + [0, 4) of each k step; copy q's lane i
+  // fills slot 64 q + i, i.e. row 8 q + i / 8 at swizzled chunk i % 8
+  const int csl = lane & 7;
   const uint8_t *asrc[2];
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
-    const int rr = (tid >> 3) + 64 * p;
-    const int r = rbeg + (rr < nrows ? rr : nrows - 1);
-    asrc[p] = a.a + (STAGE == 0 ? (size_t)a.rowinfo[r].y : (size_t)r) * K + (tid & 7) * 16;
+    const int r = 8 * (2 * wave + p) + (lane >> 3);
+    const int c = csl ^ ((r >> 1) & 7);
+    const int rr = rbeg + (r < nrows ? r : nrows - 1);
+    asrc[p] = a.a + (STAGE == 0 ? (size_t)a.rowinfo[rr].y : (size_t)rr) * K + 16 * c;
   }
-  // activation scales of the tile's rows into LDS
-  for (int idx = tid; idx < kW8BM * G; idx += 512) {
-    const int rr = idx / G, g = idx - rr * G;
-    const int r = rbeg + (rr < nrows ? rr : nrows - 1);
-    rsc[rr * G + g] = a.as[(STAGE == 0 ? (size_t)a.rowinfo[r].y : (size_t)r) * G + g];
+  const uint8_t *wsrc[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int r = 8 * (4 * wave + p) + (lane >> 3);  // stage weight row 0..255
+    const int c = csl ^ ((r >> 1) & 7);
+    int n;
+    if (STAGE == 0) {
+      const int hc = nt * 128 + (r & 127);            // h column of this gate or up row
+      n = hc < a.I ? (r < 128 ? hc : a.I + hc) : 0;   // rows past I: any row, never stored
+    } else {
+      n = nt * 256 + r;
+      n = n < N ? n : 0;
+    }
+    wsrc[p] = a.w + ((size_t)e * N + n) * K + 16 * c;
   }
-
-  auto load_a = [&](u4 (&ar)[2], int ks) {
+  // activation scales: waves 0 and 1 copy rows 64 wave + lane
+  const float *ssrc = a.as;
+  if (wave < 2) {
+    const int r = 64 * wave + lane;
+    const int rr = rbeg + (r < nrows ? r : nrows - 1);
+    ssrc = a.as + (STAGE == 0 ? (size_t)a.rowinfo[rr].y : (size_t)rr) * G;
+  }
+  auto issue = [&](int ks) {
+    unsigned char *st = smem + (ks % kW8Stages) * kW8StageBytes;
 #pragma unroll
-    for (int p = 0; p < 2; ++p) ar[p] = *(const u4 *)(asrc[p] + (size_t)ks * kW8K);
-  };
-  auto write_a = [&](const u4 (&ar)[2], int buf) {
+    for (int p = 0; p < 2; ++p) dma16(asrc[p] + (size_t)ks * kW8K, st + 1024 * (2 * wave + p));
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
-      *(u4 *)(abuf + (size_t)buf * kW8BM * kW8LD + ((tid >> 3) + 64 * p) * kW8LD + (tid & 7) * 16) = ar[p];
+    for (int p = 0; p < 4; ++p) dma16(wsrc[p] + (size_t)ks * kW8K, st + kW8ABytes + 1024 * (4 * wave + p));
+    if (wave < 2) dma4(ssrc + ks, st + kW8ABytes + kW8WBytes + 256 * wave);
   };
-  // weight codes of one k step: [tile][sub-step] x 32 bytes
-  struct WRegs {
-    i8v v[2][2];
+  // wait for this wave's copies of the k step before the newest `later` steps
+  auto wait_step = [&](int later) {
+    if (wave < 2) {
+      if (later) wait_vm<7>(); else wait_vm<0>();
+    } else {
+      if (later) wait_vm<6>(); else wait_vm<0>();
+    }
   };
-  auto load_w = [&](WRegs &R, int ks) {
-#pragma unroll
-    for (int tn = 0; tn < 2; ++tn)
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const u4 *p = (const u4 *)(wsrc[tn] + (size_t)ks * kW8K + 64 * s);
-        const u4 x0 = p[0], x1 = p[1];
-        R.v[tn][s] = i8v{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
-                         (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
-      }
-  };
+  static_assert(kW8Stages == 3, "wait_step counts one later k step in flight");
 
   f16v acc[2][2];
 #pragma unroll
@@ -158,26 +209,38 @@ void gemm_w8a8(W8Args a) {
   // 32-row subtiles of the wave that hold rows of the expert (wave-uniform)
   const int nsub = wvalid ? max(0, min(2, (nrows - 64 * rh + 31) / 32)) : 0;
 
-  // one k step from LDS buffer `buf`: the 2 x 2 tiles' eight MFMAs first
-  // (two per tile, 64 k each, into a per-step partial), then the scale FMAs,
-  // which overlap the later MFMAs; NS = 32-row subtiles with rows
-  auto compute = [&](auto ns_c, const WRegs &R, int buf, int ks) {
+  // one k step from its stage: the 2 x 2 tiles' eight MFMAs first (two per
+  // tile, 64 k each, into a per-step partial), then the scale FMAs, which
+  // overlap the later MFMAs; NS = 32-row subtiles with rows
+  auto compute = [&](auto ns_c, int ks) {
     constexpr int NS = decltype(ns_c)::value;
     if constexpr (NS > 0) {
-      const uint8_t *As = abuf + (size_t)buf * kW8BM * kW8LD + 32 * hh;
-      i8v b[NS][2];
+      const float s0 = sws[wblk[0] * G + ks], s1 = sws[wblk[1] * G + ks];
+      const unsigned char *st = smem + (ks % kW8Stages) * kW8StageBytes;
+      const unsigned char *Ws = st + kW8ABytes;
+      const float *Ss = (const float *)(st + kW8ABytes + kW8WBytes);
+      i8v w[2][2], b[NS][2];
 #pragma unroll
-      for (int tm = 0; tm < NS; ++tm)
+      for (int s = 0; s < 2; ++s) {
+        const int c0 = 4 * s + 2 * hh;
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const u4 *p = (const u4 *)(As + (64 * rh + 32 * tm + j) * kW8LD + 64 * s);
-          const u4 x0 = p[0], x1 = p[1];
+        for (int tn = 0; tn < 2; ++tn) {
+          const int r = wrow[tn] + j;
+          const u4 x0 = *(const u4 *)(Ws + 16 * w8_slot(r, c0));
+          const u4 x1 = *(const u4 *)(Ws + 16 * w8_slot(r, c0 + 1));
+          w[tn][s] = i8v{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+        }
+#pragma unroll
+        for (int tm = 0; tm < NS; ++tm) {
+          const int r = 64 * rh + 32 * tm + j;
+          const u4 x0 = *(const u4 *)(st + 16 * w8_slot(r, c0));
+          const u4 x1 = *(const u4 *)(st + 16 * w8_slot(r, c0 + 1));
           b[tm][s] = i8v{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
         }
+      }
       float sa[NS];
 #pragma unroll
-      for (int tm = 0; tm < NS; ++tm) sa[tm] = rsc[(64 * rh + 32 * tm + j) * G + ks];
-      const float s0 = wsc[0][ks], s1 = wsc[1][ks];
+      for (int tm = 0; tm < NS; ++tm) sa[tm] = Ss[64 * rh + 32 * tm + j];
       f16v z;
 #pragma unroll
       for (int i = 0; i < 16; ++i) z[i] = 0.f;
@@ -185,11 +248,11 @@ void gemm_w8a8(W8Args a) {
 #pragma unroll
       for (int tm = 0; tm < NS; ++tm)
 #pragma unroll
-        for (int tn = 0; tn < 2; ++tn) tmp[tn][tm] = mfma_fp8(R.v[tn][0], b[tm][0], z);
+        for (int tn = 0; tn < 2; ++tn) tmp[tn][tm] = mfma_fp8(w[tn][0], b[tm][0], z);
 #pragma unroll
       for (int tm = 0; tm < NS; ++tm)
 #pragma unroll
-        for (int tn = 0; tn < 2; ++tn) tmp[tn][tm] = mfma_fp8(R.v[tn][1], b[tm][1], tmp[tn][tm]);
+        for (int tn = 0; tn < 2; ++tn) tmp[tn][tm] = mfma_fp8(w[tn][1], b[tm][1], tmp[tn][tm]);
 #pragma unroll
       for (int tm = 0; tm < NS; ++tm) {
         const float f0 = sa[tm] * s0, f1 = sa[tm] * s1;
@@ -202,37 +265,21 @@ void gemm_w8a8(W8Args a) {
     }
   };
 
-  // ---- main loop: stage k step t + 1 while step t multiplies.  Unrolled by
-  // two so the two weight register sets keep fixed names (selected by a
-  // runtime index, the compiler would place them in scratch memory).
   auto main_loop = [&](auto ns_c) {
-    WRegs R0, R1;
-    u4 ar[2];
-    load_a(ar, 0);
-    load_w(R0, 0);
-    write_a(ar, 0);
-    if (nK > 1) load_a(ar, 1);
-    for (int t = 0; t < nK; t += 2) {
-      __syncthreads();  // buffer 0 holds step t; buffer 1 is free
-      if (t + 1 < nK) {
-        write_a(ar, 1);
-        if (t + 2 < nK) load_a(ar, t + 2);
-        load_w(R1, t + 1);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      compute(ns_c, R0, 0, t);
-      if (t + 1 < nK) {
-        __syncthreads();  // buffer 1 holds step t + 1; buffer 0 is free
-        if (t + 2 < nK) {
-          write_a(ar, 0);
-          if (t + 3 < nK) load_a(ar, t + 3);
-          load_w(R0, t + 2);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        compute(ns_c, R1, 1, t + 1);
-      }
+    for (int s = 0; s < kW8Stages - 1 && s < nK; ++s) issue(s);
+    for (int t = 0; t < nK; ++t) {
+      wait_step(t + 1 < nK);
+      // step t is in its stage; every wave is done with step t - 1's.  A bare
+      // barrier: __syncthreads' fence would also wait for the copies of step
+      // t + 1, which are meant to stay in flight
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (t + kW8Stages - 1 < nK) issue(t + kW8Stages - 1);
+      compute(ns_c, t);
     }
   };
+  __syncthreads();  // the weight scales
   switch (nsub) {
     case 2: main_loop(std::integral_constant<int, 2>{}); break;
     case 1: main_loop(std::integral_constant<int, 1>{}); break;
@@ -280,7 +327,7 @@ void gemm_w8a8(W8Args a) {
     // ---- down: routing-weighted FP16 partials, each 32-row slice of the
     // wave's tile transposed through LDS and stored 16 bytes per lane
     constexpr int TL = 64 + 8;  // LDS row stride, halves
-    static_assert(8 * 32 * TL * 2 <= 2 * kW8BM * kW8LD, "transpose buffers fit the activation buffers");
+    static_assert(8 * 32 * TL * 2 <= kW8Stages * kW8StageBytes, "transpose buffers fit the stages");
     _Float16 *tb = (_Float16 *)smem + wave * 32 * TL;
     float vmax = 0.f, vnan = 0.f;
     __syncthreads();  // every wave is done with the activation buffers
@@ -323,9 +370,7 @@ void gemm_w8a8(W8Args a) {
   if (__builtin_amdgcn_ballot_w64(sat != 0u) != 0ull && lane == 0) atomicOr(a.flags, 1u);
 }
 
-static size_t w8a8_lds(int) {
-  return (size_t)2 * kW8BM * kW8LD + (size_t)kW8BM * kW8MaxG * 4 + (size_t)4 * kW8BM * 4;
-}
+static size_t w8a8_lds(int) { return (size_t)kW8Lds; }
 
 template <int STAGE>
 static hipError_t run_w8a8(const LayerDims &L, const FwdPtrs &P, const Workspace &W, const GemmLaunch &s) {
@@ -354,7 +399,6 @@ static hipError_t run_w8a8(const LayerDims &L, const FwdPtrs &P, const Workspace
   const int64_t max_mt = R / kW8BM + L.E;  // >= sum_e ceil(n_e / 128)
   const int64_t grid = 8 * ((max_mt * a.tiles + 7) / 8);
   const size_t lds = w8a8_lds(a.K);
-  static_assert(2 * kW8BM * kW8LD + kW8BM * kW8MaxG * 4 + 4 * kW8BM * 4 <= kMaxLdsBytes, "LDS");
   raise_lds_limit((const void *)gemm_w8a8<STAGE>);
   hipExtLaunchKernelGGL((gemm_w8a8<STAGE>), dim3((unsigned)grid), dim3(512), (uint32_t)lds, s.stream, s.start,
                         s.stop, 0u, a);
