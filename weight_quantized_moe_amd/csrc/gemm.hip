@@ -17,10 +17,11 @@
 //    weight beside the FP16 scale's own 2^-11), and the column's accumulator
 //    is multiplied back by the power of two at the end.
 //
-// Operand roles (both kernels): the MFMA A operand is activations (rows =
-// grouped tokens), the B operand is weights (columns = output features).  A
-// lane therefore owns one output column, so a per-column scale is one scalar
-// per lane.
+// Operand roles: the decode MFMA takes activations as its A operand (rows =
+// grouped tokens) and weights as B (columns = output features), so a lane
+// owns one output column and a per-column scale is one scalar per lane; the
+// prefill MFMA takes them the other way round (C[n][m], weights as A), so a
+// lane ends with four consecutive output columns of one grouped row.
 #include <algorithm>
 #include <map>
 #include <mutex>
@@ -405,13 +406,15 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode(GemmArgs a) {
 
 // ===========================================================================
 // Prefill path (many rows per expert).  Tiles of 128 grouped rows of one
-// expert; weight codes are dequantized exactly into FP16 MFMA operands:
-// INT4 (c - 8) * s and FP8 e4m3 * s carry their group / block scale,
-// multiplied by a power of two 2^p per weight column chosen from the column's
-// largest scale so the values sit high in FP16 range; the product is rounded
-// once to FP16 (relative error <= 2^-11) and the accumulator of that column is
-// multiplied by 2^-p at the end.  NVFP4 e2m1 * e4m3 products are exact in
-// FP16; its global scale divides the finished sum.
+// expert; weight codes become FP16 MFMA operands that carry their group /
+// block scale, multiplied by a power of two 2^p per weight column chosen from
+// the column's largest scale so the values sit high in FP16 range, and the
+// accumulator of that column is multiplied by 2^-p at the end.  INT4: the FP16
+// group scale times 2^p is exact, so (c - 8) * s is rounded once to FP16
+// (relative error <= 2^-11).  FP8: the FP32 block scale times 2^p is rounded
+// to FP16 first, then the product e4m3 * s (two roundings, relative error
+// below 2^-10).  NVFP4 e2m1 * e4m3 products are exact in FP16; its global
+// scale divides the finished sum.
 //
 // Tiles are numbered (M-tile, N-tile) with N fastest and dealt to the 8 XCDs
 // in contiguous ranges (blocks are dispatched to XCDs round robin), so tiles
