@@ -143,6 +143,29 @@ def test_decode_after_chunked_grouping(fmt, T):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("T,k,E,H,I", [(16, 4, 8, 512, 256), (9, 8, 8, 256, 768),
+                                       (40, 4, 16, 768, 512), (64, 8, 32, 1024, 1280),
+                                       (100, 2, 16, 2048, 256), (200, 8, 128, 512, 384)])
+def test_streaming_decode(fmt, T, k, E, H, I):
+    """Decode batches with 8 to 16 rows per expert on average and H a multiple
+    of 256 (at most 2048) run the streaming gate/up GEMM: experts holding 0, 1
+    and up to 49 rows (several 16-row chunks, the hidden rows staged again
+    between units), 1 to 8 chunks per unit (odd counts alternate the ring
+    slots across units), I not a multiple of 256, and from one unit per busy
+    block to many."""
+    log(f"[stream] fmt={fmt} T={T} k={k} E={E} H={H} I={I}")
+    p13, p2 = quantized_layer(fmt, 23, T, E, H, I)
+    g = GpuLayer(p13, p2, k)
+    lg = synth.router_logits(23, T, T, E, "bias")
+    x = synth.hidden_bf16(23, T, T, H)
+    _, pr = _check_layer(g, lg, x, tag=f"{fmt} stream T={T} E={E} H={H} I={I}")
+    counts = np.bincount(moe.route(lg, k)[0].ravel(), minlength=E)
+    assert 8 * E <= T * k <= 16 * E
+    if T >= 40:
+        assert counts.max() > 16, counts   # some expert spans two row chunks
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("T", [20, 700])
 def test_hidden_not_multiple_of_256(fmt, T):
     """H = 384: the prefill down projection's last 256-column tile is half full."""

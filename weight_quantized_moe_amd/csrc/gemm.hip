@@ -405,6 +405,303 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode(GemmArgs a) {
 }
 
 // ===========================================================================
+// Streaming decode gate/up GEMM (8 to 16 rows per expert on average,
+// K = H <= 2048).  The work is a list of units (one 16-row chunk of an
+// expert's grouped rows x 128 gate columns and the matching 128 up columns),
+// dealt to one persistent block per CU in contiguous ranges, so that
+// consecutive units of a block mostly share their activation rows.  Each of
+// the 8 waves owns 16 gate and the 16 matching up rows of a unit (two 16-row
+// tiles) and streams them 128 bytes of k at a time (a 4 KB chunk) from global
+// memory straight into a private LDS ring, kDSDepth chunks ahead of their use
+// and across unit boundaries: no register ring, no block barrier for the
+// weights, and every copy instruction moves 8 rows x 128 contiguous bytes.  A
+// chunk is unpacked from LDS into the B operand of the 16x16x32 FP16 MFMA,
+// whose A operand is the unit's FP16 hidden rows (scaled by the routing
+// kernel), staged in LDS by the same copies whenever the row chunk changes.
+// INT4 / FP8 scales multiply each 128-wide k block's FP32 partial sum, as in
+// gemm_decode.  A chunk's scales travel the same way, by one more copy into a
+// per-wave LDS slot: the loop issues no load whose result lands in registers,
+// so nothing but the explicit waits holds a wave back (a register load in the
+// mix would make the compiler wait for every copy in flight).
+//   Lane l: MFMA column (weight row) l % 16 of a tile, k slice q = l / 16;
+//   result rows (activation rows) 4 q + [0, 4).  Ring chunk layout: local row
+//   lr (0..31) x 8 pieces of 16 bytes, piece pc of row lr at slot
+//   8 lr + (pc ^ ((lr >> 1) & 7)), so 16 rows reading one piece hit distinct
+//   banks.
+// ===========================================================================
+constexpr int kDSMaxK = 2048;         // activation rows staged whole in LDS
+constexpr int kDSDepth = 2;           // chunks in flight per wave
+constexpr int kDSChunk = 32 * 128;    // bytes: 32 weight rows x 128 bytes of k
+constexpr size_t kDSAsBytes = (size_t)16 * (kDSMaxK + 8) * 2;
+constexpr int kDSScB = 1024;          // bytes of scale slot per wave and chunk (NVFP4; others use 256)
+// dynamic LDS (every copy target): the weight rings, the scale slots, the
+// activation rows; the tables are static
+constexpr size_t kDSLds = (size_t)8 * kDSDepth * (kDSChunk + kDSScB) + kDSAsBytes;
+static_assert(kDSLds + (size_t)(kMaxExperts + 1) * 4 + (size_t)kMaxExperts * 16 + 16 * 16 <= kMaxLdsBytes,
+              "streaming decode GEMM fits in LDS");
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+__device__ __forceinline__ void copy16_lds(const void *g, unsigned char *lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t *)lds, 16, 0, 0);
+}
+// 4 bytes per lane: lane i's dword lands at lds + 4 i
+__device__ __forceinline__ void copy4_lds(const void *g, unsigned char *lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t *)lds, 4, 0, 0);
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int FMT>
+__global__ __launch_bounds__(512) void gemm_decode_stream(GemmArgs a) {
+  // Every copy target is in the dynamic LDS array, which the compiler does
+  // not match against the copies in flight (for copies into a static array it
+  // would wait for all of them before any read of that array): the explicit
+  // waits below are what orders each read after its copy.
+  extern __shared__ __align__(16) unsigned char ring[];                 // [8 waves][kDSDepth][4 KB]
+  constexpr int SCB = FMT == FMT_NVFP4 ? kDSScB : 256;
+  unsigned char *scs = ring + (size_t)8 * kDSDepth * kDSChunk;          // [8 waves][kDSDepth][SCB]
+  _Float16 *As = (_Float16 *)(scs + (size_t)8 * kDSDepth * SCB);        // [16][K + 8]
+  __shared__ int rcpre[kMaxExperts + 1];                                // [active + 1]
+  __shared__ int4 einf[kMaxExperts];                                    // [active]: the expert table
+  __shared__ int4 rinf[16];                                             // the unit's row records
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int col = lane & 15, q = lane >> 4;
+  const int K = a.K, N = a.N, lda = K + 8, G = K / 128;
+  const int RB = FMT == FMT_FP8 ? K : K / 2;  // bytes per weight row
+  const int CPU = RB / 128;                   // chunks per unit and wave
+  constexpr int NGC = FMT == FMT_FP8 ? 1 : 2; // 128-wide k groups per chunk
+
+  // ---- the expert table and the exclusive prefix of its 16-row chunks, in
+  // LDS (global loads consumed in the loop would make the wave wait for every
+  // copy in flight)
+  // (.w: the NVFP4 expert's 1 / global scale)
+  const int n_act = __builtin_amdgcn_readfirstlane(a.einfo[0].x);
+  for (int i = threadIdx.x; i < n_act; i += 512) {
+    int4 ei = a.einfo[1 + i];
+    if (FMT == FMT_NVFP4) ei.w = __builtin_bit_cast(int, 1.0f / a.gscale[ei.x]);
+    einf[i] = ei;
+  }
+  if (wave == 0) {
+    int run = 0;
+    for (int b = 0; b < n_act; b += 64) {
+      const int i = b + lane;
+      const int c = i < n_act ? (a.einfo[1 + i].z + 15) >> 4 : 0;
+      int sc = c;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int t = __shfl_up(sc, d, 64);
+        if (lane >= d) sc += t;
+      }
+      if (i < n_act) rcpre[i] = run + sc - c;
+      run += __shfl(sc, 63, 64);
+    }
+    if (lane == 0) rcpre[n_act] = run;
+  }
+  __syncthreads();
+  const int UPE = a.tiles;
+  const int64_t n_units = (int64_t)rcpre[n_act] * UPE;
+  const int u0 = (int)((int64_t)blockIdx.x * n_units / gridDim.x);
+  const int u1 = (int)((int64_t)(blockIdx.x + 1) * n_units / gridDim.x);
+  if (u0 >= u1) return;  // block-uniform
+
+  struct Unit {
+    int e, r0, nr, tile, rc;
+    float ginv;
+  };
+  auto unit_of = [&](int u) {
+    Unit x;
+    x.rc = u / UPE;
+    x.tile = u - x.rc * UPE;
+    int lo = 0, hi = n_act - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (rcpre[mid] <= x.rc) lo = mid; else hi = mid - 1;
+    }
+    const int4 ei = einf[lo];
+    const int mc = x.rc - rcpre[lo];
+    x.e = ei.x;
+    x.r0 = ei.y + 16 * mc;
+    x.nr = min(16, ei.z - 16 * mc);
+    x.ginv = FMT == FMT_NVFP4 ? __builtin_bit_cast(float, ei.w) : 1.0f;
+    return x;
+  };
+  // global weight row of local row lr (0..31) of this wave in unit x (gate
+  // rows, then the matching up rows); rows past the end read row 0 of the
+  // expert and are never stored
+  auto wrow = [&](const Unit &x, int lr) {
+    const int hc = x.tile * 128 + 16 * wave + (lr & 15);
+    return hc < a.I ? (lr < 16 ? hc : a.I + hc) : 0;
+  };
+  // scales of a chunk, one copy into the wave's scale slot: INT4 the two FP16
+  // group scales of row lane % 32 (dword 4 lr), NVFP4 its 16 E4M3 bytes
+  // (16 lr + 8 g + 2 q: the pair of k slice q in group g), FP8 the block scale
+  // of tile lane % 2 (dword 4 t); lanes 32..63 repeat lanes 0..31
+  auto issue_sc = [&](const Unit &x, int c, int sl) {
+    unsigned char *dst = scs + ((size_t)wave * kDSDepth + sl) * SCB;
+    if (FMT == FMT_INT4) {
+      const int n = wrow(x, lane & 31);
+      copy4_lds((const uint16_t *)a.scale + ((size_t)x.e * N + n) * G + 2 * c, dst);
+    } else if (FMT == FMT_NVFP4) {
+      const int n = wrow(x, lane & 31);
+      copy16_lds((const uint8_t *)a.scale + ((size_t)x.e * N + n) * (K / 16) + 16 * c, dst);
+    } else {
+      const int nb = wrow(x, 16 * (lane & 1));  // the tile's 16 rows share a block
+      copy4_lds((const float *)a.scale + ((size_t)x.e * (N / 128) + nb / 128) * G + c, dst);
+    }
+  };
+  auto issue_w = [&](const Unit &x, int c, int sl) {
+    unsigned char *dst = ring + ((size_t)wave * kDSDepth + sl) * kDSChunk;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int lr = 8 * q4 + (lane >> 3), pc = (lane & 7) ^ ((lr >> 1) & 7);
+      copy16_lds(a.w + ((size_t)x.e * N + wrow(x, lr)) * RB + 128 * c + 16 * pc, dst + 1024 * q4);
+    }
+  };
+  // the unit's row records into rinf, then its hidden rows (by token) into As
+  // (all waves), by copies of up to 1 KB
+  auto stage_rows = [&](const Unit &x) {
+    if (threadIdx.x < 16) rinf[threadIdx.x] = threadIdx.x < x.nr ? a.rowinfo[x.r0 + threadIdx.x] : int4{0, 0, 0, 0};
+    __syncthreads();
+    const int rowb = 2 * K, pieces = (rowb + 1023) >> 10;
+    for (int idx = wave; idx < x.nr * pieces; idx += 8) {
+      const int m = idx / pieces, pc = idx - m * pieces;
+      const int src_row = __builtin_amdgcn_readfirstlane(rinf[m].y);
+      const int off = pc * 1024 + 16 * lane;
+      if (off < rowb)
+        copy16_lds((const unsigned char *)a.a_src + (size_t)src_row * rowb + off,
+                   (unsigned char *)As + (size_t)m * lda * 2 + pc * 1024);
+    }
+  };
+
+  f4 acc[2];
+  acc[0] = acc[1] = f4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const Unit &x, int c, int sl) {
+    const unsigned char *wb = ring + ((size_t)wave * kDSDepth + sl) * kDSChunk;
+    const unsigned char *sb = scs + ((size_t)wave * kDSDepth + sl) * SCB;
+#pragma unroll
+    for (int gi = 0; gi < NGC; ++gi) {
+      const int gk = (NGC * c + gi) * 128;
+      h8 av[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) av[j] = *(const h8 *)(As + col * lda + gk + 32 * q + 8 * j);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int lr = 16 * t + col, sw = (lr >> 1) & 7;
+        uint32_t sv = 0u;
+        float sf = 0.f;
+        if (FMT == FMT_INT4)
+          sv = (*(const uint32_t *)(sb + 4 * lr) >> (16 * gi)) & 0xFFFFu;
+        else if (FMT == FMT_NVFP4)
+          sv = *(const uint16_t *)(sb + 16 * lr + 8 * gi + 2 * q);
+        else
+          sf = *(const float *)(sb + 4 * t);
+        u4 w0, w1;
+        if (FMT == FMT_FP8) {
+          w0 = *(const u4 *)(wb + 16 * (8 * lr + ((2 * q) ^ sw)));
+          w1 = *(const u4 *)(wb + 16 * (8 * lr + ((2 * q + 1) ^ sw)));
+        } else {
+          w0 = *(const u4 *)(wb + 16 * (8 * lr + ((4 * gi + q) ^ sw)));
+        }
+        f4 tmp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          h8 bv;
+          if (FMT == FMT_INT4)
+            bv = unpack_int4(w0[j]);
+          else if (FMT == FMT_FP8)
+            bv = j < 2 ? unpack_fp8(w0[2 * j], w0[2 * j + 1]) : unpack_fp8(w1[2 * j - 4], w1[2 * j - 3]);
+          else
+            bv = unpack_nvfp4(w0[j], e4m3_to_f16((sv >> (8 * (j >> 1))) & 0xFFu));
+          if (FMT == FMT_NVFP4)
+            acc[t] = mfma16(av[j], bv, acc[t]);
+          else
+            tmp = mfma16(av[j], bv, tmp);
+        }
+        if (FMT == FMT_INT4)
+          acc[t] += tmp * (float)__builtin_bit_cast(_Float16, (uint16_t)sv);
+        else if (FMT == FMT_FP8)
+          acc[t] += tmp * sf;
+      }
+    }
+  };
+  auto epilogue = [&](const Unit &x) {
+    const float ginv = x.ginv;
+    uint32_t sat = 0u;
+    const int hc = x.tile * 128 + 16 * wave + col;
+    if (x.tile * 128 + 16 * wave < a.I) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = 4 * q + v;
+        if (m < x.nr) {
+          const float rs = __builtin_bit_cast(float, rinf[m].z) * ginv;
+          a.h_out[(size_t)(x.r0 + m) * a.I + hc] = to_f16_sat(silu(acc[0][v] * rs) * (acc[1][v] * rs), sat);
+        }
+      }
+    }
+    flag_saturation(a, sat);
+    acc[0] = acc[1] = f4{0.f, 0.f, 0.f, 0.f};
+  };
+
+  // ---- the chunk sequence of this block: s -> unit u0 + s / CPU, chunk s % CPU
+  const int S = (u1 - u0) * CPU;
+  Unit iss = unit_of(u0);
+  int iss_u = u0, iss_c = 0, issued = 0;
+  auto issue_next = [&](int sl) {
+    issue_sc(iss, iss_c, sl);
+    issue_w(iss, iss_c, sl);
+    ++issued;
+    if (++iss_c == CPU && issued < S) {
+      iss_c = 0;
+      iss = unit_of(++iss_u);
+    }
+  };
+  static_assert(kDSDepth == 2, "the loop below alternates two ring slots");
+  issue_next(0);
+  if (issued < S) issue_next(1);
+  Unit cur = unit_of(u0);
+  int cur_u = u0, staged_rc = -1;
+  // wait for this wave's chunk s with `later` newer chunks in flight: each
+  // chunk is five copies (scales, then four of weights) and copies complete in
+  // issue order, so at most five outstanding means chunk s is in LDS (stores
+  // of a finished unit, also counted, only make the wait stricter)
+  auto wait_chunk = [&](int later) {
+    if (later) wait_vmcnt<5>(); else wait_vmcnt<0>();
+  };
+  auto step = [&](int s, int sl) {
+    const int c = s - (cur_u - u0) * CPU;
+    if (c == 0 && cur.rc != staged_rc) {
+      // every wave is done reading the previous rows and records (no wait
+      // for the weight copies in flight)
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      stage_rows(cur);
+      wait_vmcnt<0>();  // this wave's row copies (and every chunk it has in flight)
+      __syncthreads();
+      staged_rc = cur.rc;
+    }
+    wait_chunk(issued - s - 1);
+    compute(cur, c, sl);
+    // the slot's LDS reads are complete before its refill is issued
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    if (issued < S) issue_next(sl);
+    if (c == CPU - 1) {
+      epilogue(cur);
+      if (cur_u + 1 < u1) cur = unit_of(++cur_u);
+    }
+  };
+  for (int s = 0; s < S; s += 2) {
+    step(s, 0);
+    if (s + 1 < S) step(s + 1, 1);
+  }
+}
+
+// ===========================================================================
 // Prefill path (many rows per expert).  Tiles of 128 grouped rows of one
 // expert; weight codes become FP16 MFMA operands that carry their group /
 // block scale, multiplied by a power of two 2^p per weight column chosen from
@@ -1031,8 +1328,12 @@ static int num_cus() {
 void raise_lds_limit(const void *f) {
   const int dev = current_device();
   std::lock_guard<std::mutex> lk(g_launch_mu);
-  if (g_lds_raised.insert({f, dev}).second)
-    (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLdsBytes);
+  if (g_lds_raised.insert({f, dev}).second) {
+    // the dynamic limit is what the kernel's static LDS leaves of the CU's
+    hipFuncAttributes fa{};
+    const size_t stat = hipFuncGetAttributes(&fa, f) == hipSuccess ? fa.sharedSizeBytes : 0;
+    (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)(kMaxLdsBytes - stat));
+  }
 }
 
 // Workgroups of kernel f resident per CU at `threads` threads and `lds` bytes.
@@ -1147,12 +1448,31 @@ static hipError_t run_prefill_wide(GemmArgs a, int64_t R, const GemmLaunch &s) {
   return run_prefill_wide1<FMT, TN, WPB, STAGE, TN == 4 ? 4 : 2>(a, R, s);
 }
 
+template <int FMT>
+static hipError_t run_decode_stream(GemmArgs a, const GemmLaunch &s) {
+  if (a.K > kDSMaxK || a.K % 256) return hipErrorInvalidValue;
+  a.tiles = (a.I + 127) / 128;  // units per 16-row chunk
+  raise_lds_limit((const void *)gemm_decode_stream<FMT>);
+  hipExtLaunchKernelGGL((gemm_decode_stream<FMT>), dim3((unsigned)num_cus()), dim3(512),
+                        (uint32_t)kDSLds, s.stream, s.start, s.stop, 0u, a);
+  return hipGetLastError();
+}
+
 template <int STAGE>
 static hipError_t dispatch(const LayerDims &L, const FwdPtrs &P, const Workspace &W, bool decode,
                            const GemmLaunch &s) {
   GemmArgs a = make_args(L, P, W, STAGE);
   const int64_t R = (int64_t)P.T * L.k;
   const int slots = (int)(R < L.E ? R : L.E);
+  if constexpr (STAGE == 0) {
+    if (decode && use_decode_stream(L.H, L.E, L.k, P.T)) {
+      switch (L.fmt) {
+        case FMT_INT4: return run_decode_stream<FMT_INT4>(a, s);
+        case FMT_FP8: return run_decode_stream<FMT_FP8>(a, s);
+        default: return run_decode_stream<FMT_NVFP4>(a, s);
+      }
+    }
+  }
   if (decode) {
     switch (L.fmt) {
       case FMT_INT4: return run_decode_ks<FMT_INT4, STAGE>(a, slots, s);

@@ -742,9 +742,9 @@ template <int kPer, bool kBf16, bool kPerm>
 static hipError_t route_dispatch(const LayerDims &L, const FwdPtrs &P, const Workspace &W,
                                  int stage_rows, hipStream_t s) {
   char *ws = P.ws;
-  // decode row scales: one wave (4 tokens) per workgroup spreads the row
-  // reads over more CUs; otherwise 16 tokens per workgroup
-  const int threads = stage_rows == 2 ? 64 : 256, tpb = threads / 16;
+  // decode batches: one wave (4 tokens) per workgroup spreads the row reads
+  // over more CUs; otherwise 16 tokens per workgroup
+  const int threads = stage_rows == 2 || P.T <= 256 ? 64 : 256, tpb = threads / 16;
   hipLaunchKernelGGL((route_kernel<kPer, kBf16, kPerm>), dim3((P.T + tpb - 1) / tpb), dim3(threads), 0, s,
                      P.logits, P.hidden, P.T, L.E, L.H, L.k, (int32_t *)(ws + W.topk_ids),
                      (float *)(ws + W.topk_w), (_Float16 *)(ws + W.x16), (float *)(ws + W.rowscale),
@@ -798,7 +798,9 @@ hipError_t launch_route(const LayerDims &L, const FwdPtrs &P, const Workspace &W
   // scales only (2), the decode gate/up GEMM converts the rows it stages;
   // larger decode rows: the GEMM finds the scales too (0); W8A8: FP8 codes
   // and scales (3); W4A4: NVFP4 values and 1 / g (4)
-  const int stage_rows = P.w8a8 ? 3 : P.act_g13 > 0.f ? 4 : !decode ? 1 : L.H <= kRowRegsMaxH ? 2 : 0;
+  const int stage_rows = P.w8a8 ? 3 : P.act_g13 > 0.f ? 4
+                       : !decode || use_decode_stream(L.H, L.E, L.k, P.T) ? 1
+                       : L.H <= kRowRegsMaxH ? 2 : 0;
   if (P.gate_w && P.T >= kGateFusedMinT)  // router GEMM fused with the top-k
     return L.fmt == FMT_INT4 ? gate_route_dispatch<true>(L, P, W, stage_rows, s)
                              : gate_route_dispatch<false>(L, P, W, stage_rows, s);
