@@ -166,6 +166,24 @@ def test_streaming_decode(fmt, T, k, E, H, I):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("T,k,E,H,I", [(40, 4, 32, 512, 256), (48, 8, 64, 384, 384),
+                                       (64, 8, 128, 256, 256), (30, 2, 16, 768, 512)])
+def test_decode_skewed_experts(fmt, T, k, E, H, I):
+    """Zipf-skewed routing with under 8 rows per expert on average and
+    experts of up to 64 rows: the register-streaming decode GEMMs (gate/up and
+    down) then take one 16-row chunk of an expert per unit, so an expert's
+    chunks spread over blocks."""
+    log(f"[skew] fmt={fmt} T={T} k={k} E={E} H={H} I={I}")
+    p13, p2 = quantized_layer(fmt, 29, T, E, H, I)
+    g = GpuLayer(p13, p2, k)
+    lg = synth.router_logits(29, T, T, E, "zipf")
+    x = synth.hidden_bf16(29, T, T, H)
+    counts = np.bincount(moe.route(lg, k)[0].ravel(), minlength=E)
+    assert T * k < 8 * E and T > 16 and counts.max() > 16, counts
+    _check_layer(g, lg, x, tag=f"{fmt} skew T={T} E={E} H={H} I={I}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("T", [20, 700])
 def test_hidden_not_multiple_of_256(fmt, T):
     """H = 384: the prefill down projection's last 256-column tile is half full."""

@@ -42,7 +42,9 @@ struct GemmArgs {
   const float *gscale;
   int N, K;  // weight matrix [N, K] per expert
   int E, I, H, k;
-  const int4 *einfo;    // {count}, then {expert, first grouped row, rows, 0} per active expert
+  int T;                // tokens
+  const int4 *einfo;    // {count, 16-row chunks}, then {expert, first grouped row, rows, 0} per active expert
+  const int32_t *rcp;   // per active expert, prefix of the 16-row chunks; then the total
   const int4 *rowinfo;  // per grouped row: {slot, token, row scale bits, routing weight bits}
   const int32_t *offsets, *mtile;
   const _Float16 *a_src;  // prefill: x16 [T, H] (gate/up) or h [R, I] (down); decode: h
@@ -53,6 +55,8 @@ struct GemmArgs {
   int tiles;              // decode: column tiles per expert; prefill: N tiles
   float hq_g;             // W4A4 gate/up: global scale of the NVFP4 quantization of h
   float a_inv;            // down: factor on the sums (W4A4: 1 / the global scale of h; else 1)
+  int rc_off;             // decode: byte offset in dynamic LDS of the 16-row-chunk table
+                          // (units are 16-row chunks); 0: units are whole experts
 };
 
 // Saturate to the FP16 range, remembering whether anything was clamped.
@@ -88,7 +92,8 @@ __device__ __forceinline__ void flag_saturation(const GemmArgs &a, uint32_t sat)
 // A block has kDecodeWaves waves: CG column-tile pairs x KSPLIT k-splits.  Each
 // wave owns two 16-column tiles (gate + matching up columns, or two adjacent
 // down columns); KSPLIT waves reduce their partial sums through LDS.  The grid
-// is persistent: resident blocks loop over (expert, tile group) units.
+// is persistent: resident blocks loop over (16-row chunk of an expert's rows,
+// tile group) units, so an expert with many rows spreads over many blocks.
 // ===========================================================================
 constexpr int kDecodeWaves = 8;
 constexpr int kD = 4;  // weight groups in flight per wave (even; 6 and 8 measured slower)
@@ -125,7 +130,23 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode(GemmArgs a) {
   const size_t rowbytes = FMT == FMT_FP8 ? (size_t)K : (size_t)K / 2;
   const int gb = (kp * G) / KSPLIT;                               // groups [gb, gb + ng)
   const int ng = NGCT > 0 ? NGCT : ((kp + 1) * G) / KSPLIT - gb;
-  const int n_units = a.einfo[0].x * a.tiles;
+  // Units are whole experts, or, when some expert holds more than 16 rows
+  // (more 16-row chunks than active experts) and the launch has room for it,
+  // 16-row chunks, through a table in LDS: the grouping's prefix of the active
+  // experts' chunks [n_act + 1], then the active-expert records [n_act] (from
+  // offset 16 * ceil((E + 1) / 4)).
+  const int4 hdr = a.einfo[0];
+  const int n_act = hdr.x;
+  int *rcpre = a.rc_off && hdr.y > hdr.x ? (int *)(smem + a.rc_off) : nullptr;  // block-uniform
+  int4 *einf = (int4 *)(smem + a.rc_off + 16 * ((a.E + 4) / 4));
+  if (rcpre) {
+    for (int i = threadIdx.x; i <= n_act; i += 64 * kDecodeWaves) {
+      if (i < n_act) einf[i] = a.einfo[1 + i];
+      rcpre[i] = a.rcp[i];
+    }
+    __syncthreads();
+  }
+  const int n_units = (rcpre ? rcpre[n_act] : n_act) * a.tiles;
   // TPW > 1 (down projection with few k groups): each wave streams TPW tile
   // pairs of the unit in one ring, so a unit's ring fill and drain cover more
   // weight bytes
@@ -133,9 +154,21 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode(GemmArgs a) {
   constexpr int NGT = NGCT * TPW;  // groups of the wave's ring (unrolled case)
 
   for (int unit = blockIdx.x; unit < n_units; unit += gridDim.x) {
-    const int slot_idx = unit / a.tiles, tile = unit - slot_idx * a.tiles;
-    const int4 ei = a.einfo[1 + slot_idx];
-    const int e = ei.x, r0 = ei.y, ne = ei.z;
+    const int ui = unit / a.tiles, tile = unit - ui * a.tiles;
+    int slot_idx = ui, mcg = 0;
+    if (rcpre) {  // ui is a 16-row chunk: find the active expert that holds it
+      // (every expert has at least one chunk, so it is at or before slot ui;
+      // with up to 16 rows per expert it is slot ui itself)
+      int lo = min(ui, n_act - 1);
+      int pre = rcpre[lo];
+      while (pre > ui) pre = rcpre[--lo];
+      slot_idx = lo;
+      mcg = ui - pre;
+    }
+    const int4 ei = rcpre ? einf[slot_idx] : a.einfo[1 + slot_idx];
+    // the unit's rows: chunk mcg of the expert (the row loop below then runs
+    // once), or all of them
+    const int e = ei.x, r0 = ei.y + 16 * mcg, ne = rcpre ? min(16, ei.z - 16 * mcg) : ei.z;
     int row[TPW][2];
 #pragma unroll
     for (int p = 0; p < TPW; ++p) {
@@ -474,31 +507,18 @@ __global__ __launch_bounds__(512) void gemm_decode_stream(GemmArgs a) {
   const int CPU = RB / 128;                   // chunks per unit and wave
   constexpr int NGC = FMT == FMT_FP8 ? 1 : 2; // 128-wide k groups per chunk
 
-  // ---- the expert table and the exclusive prefix of its 16-row chunks, in
+  // ---- the expert table and the grouping's prefix of its 16-row chunks, in
   // LDS (global loads consumed in the loop would make the wave wait for every
-  // copy in flight)
+  // copy in flight); count, records and prefix in one round trip
   // (.w: the NVFP4 expert's 1 / global scale)
   const int n_act = __builtin_amdgcn_readfirstlane(a.einfo[0].x);
-  for (int i = threadIdx.x; i < n_act; i += 512) {
-    int4 ei = a.einfo[1 + i];
-    if (FMT == FMT_NVFP4) ei.w = __builtin_bit_cast(int, 1.0f / a.gscale[ei.x]);
-    einf[i] = ei;
-  }
-  if (wave == 0) {
-    int run = 0;
-    for (int b = 0; b < n_act; b += 64) {
-      const int i = b + lane;
-      const int c = i < n_act ? (a.einfo[1 + i].z + 15) >> 4 : 0;
-      int sc = c;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int t = __shfl_up(sc, d, 64);
-        if (lane >= d) sc += t;
-      }
-      if (i < n_act) rcpre[i] = run + sc - c;
-      run += __shfl(sc, 63, 64);
+  for (int i = threadIdx.x; i <= n_act; i += 512) {
+    if (i < n_act) {
+      int4 ei = a.einfo[1 + i];
+      if (FMT == FMT_NVFP4) ei.w = __builtin_bit_cast(int, 1.0f / a.gscale[ei.x]);
+      einf[i] = ei;
     }
-    if (lane == 0) rcpre[n_act] = run;
+    rcpre[i] = a.rcp[i];
   }
   __syncthreads();
   const int UPE = a.tiles;
@@ -1274,9 +1294,9 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict_
 // Launchers
 // ===========================================================================
 static GemmArgs make_args(const LayerDims &L, const FwdPtrs &P, const Workspace &W, int stage) {
-  GemmArgs a;
+  GemmArgs a{};
   char *ws = P.ws;
-  a.E = L.E; a.I = L.I; a.H = L.H; a.k = L.k;
+  a.E = L.E; a.I = L.I; a.H = L.H; a.k = L.k; a.T = P.T;
   if (stage == 0) {
     a.w = L.w13; a.scale = L.s13; a.gscale = L.g13; a.N = 2 * L.I; a.K = L.H;
     a.a_src = (const _Float16 *)(ws + W.x16);
@@ -1286,6 +1306,7 @@ static GemmArgs make_args(const LayerDims &L, const FwdPtrs &P, const Workspace 
   }
   a.hidden = P.hidden;
   a.einfo = (const int4 *)(ws + W.active);
+  a.rcp = (const int32_t *)(ws + W.rcpre);
   a.rowinfo = (const int4 *)(ws + W.rowinfo);
   a.offsets = (const int32_t *)(ws + W.offsets);
   a.mtile = (const int32_t *)(ws + W.mtile);
@@ -1358,9 +1379,20 @@ template <int FMT, int STAGE, int KSPLIT, int GCT, int TPW>
 static hipError_t run_decode_t(GemmArgs a, int slots, const GemmLaunch &s) {
   constexpr int CG = kDecodeWaves / KSPLIT;
   a.tiles = STAGE == 0 ? a.I / (16 * CG * TPW) : a.H / (32 * CG * TPW);
-  const size_t lds = decode_lds_bytes(a.K, KSPLIT);
+  size_t lds = decode_lds_bytes(a.K, KSPLIT);
   static_assert(CG == 8 / KSPLIT && kDecodeWaves == 8, "decode_lds_bytes assumes 8 waves");
   if (lds > kMaxLdsBytes) return hipErrorInvalidValue;  // init rejects such shapes
+  // units of 16 rows (an expert with many rows spreads over blocks) where the
+  // chunk prefix fits after the staging buffers
+  const size_t rc_off = (lds + 15) & ~(size_t)15;
+  a.rc_off = 0;
+  const size_t table = (size_t)16 * ((a.E + 4) / 4) + (size_t)16 * a.E;
+  // with at most 16 tokens no expert holds more than 16 rows (a token's k
+  // experts are distinct): whole experts are the same units, without the table
+  if (a.T > 16 && rc_off + table <= kMaxLdsBytes) {
+    a.rc_off = (int)rc_off;
+    lds = rc_off + table;
+  }
   // persistent grid: as many blocks as are resident at once (from the
   // kernel's registers and LDS), never more than the number of units
   const int per_cu = blocks_per_cu(gemm_decode<FMT, STAGE, KSPLIT, GCT, TPW>, 64 * kDecodeWaves, lds);

@@ -59,9 +59,10 @@ inline void permute_chunks(int64_t T, int *nc, int *chunk) {
 struct Workspace {
   size_t topk_ids, topk_w;     // int32 [R], float [R]            (R = T*k)
   size_t offsets;              // int32 [E+1]
-  size_t active;               // int4 [1 + E]: {count}, then {expert, first row, rows, 0} per active expert
+  size_t active;               // int4 [1 + E]: {count, 16-row chunks}, then {expert, first row, rows, 0} per active expert
   size_t rowinfo;              // int4 [R]: {slot, token, row scale bits, routing weight bits} per grouped row
   size_t mtile;                // int32 [E+1]: prefix of ceil(n_e / kPrefillBM)
+  size_t rcpre;                // int32 [E+1]: per active expert, prefix of its 16-row chunks ceil(n_e / 16)
   size_t sorted_slots;         // int32 [R]: slot t*k+j of each grouped row
   size_t inv_pos;              // int32 [R]
   size_t x16;                  // fp16 [T, H]: hidden rows scaled by 2^-s_t (INT4: k order of the unpack)

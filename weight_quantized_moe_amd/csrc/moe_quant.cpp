@@ -53,6 +53,7 @@ Workspace workspace_layout(int64_t T, int E, int H, int I, int k) {
   w.active = take((size_t)(E + 1) * 16);
   w.rowinfo = take(R * 16);
   w.mtile = take((size_t)(E + 1) * 4);
+  w.rcpre = take((size_t)(E + 1) * 4);
   w.sorted_slots = take(R * 4);
   w.inv_pos = take(R * 4);
   w.chunks = take((size_t)mq::kMaxChunks * E * 4);

@@ -532,17 +532,21 @@ __global__ __launch_bounds__(64 * kGateWaves) void gate_route_kernel(
 // ---------------------------------------------------------------------------
 // Exclusive scan of cnt[0..E) (E <= 512) by one wave; also the prefill
 // M-tile counts and the table of active experts.  Writes offsets[E+1],
-// mtile[E+1], einfo (the count of active experts, then one {expert, first
-// grouped row, rows, 0} entry per active expert in ascending expert order)
+// mtile[E+1], einfo ({count of active experts, their 16-row chunks}, then one
+// {expert, first grouped row, rows, 0} entry per active expert in ascending
+// expert order),
+// rcp (per active expert, the prefix of the 16-row chunks of the experts
+// before it, then the total: [count + 1] entries)
 // and, if given, p_offsets.  Lanes hold 8 consecutive experts.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void scan_experts_wave(const int32_t *cnt, int E, int lane,
                                                   int32_t *__restrict__ offsets,
                                                   int32_t *__restrict__ mtile,
                                                   int4 *__restrict__ einfo,
+                                                  int32_t *__restrict__ rcp,
                                                   int32_t *__restrict__ p_offsets,
                                                   int32_t *cursor) {
-  int c[8], s0 = 0, s1 = 0, s2 = 0;
+  int c[8], s0 = 0, s1 = 0, s2 = 0, s3 = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int e = lane * 8 + i;
@@ -550,14 +554,16 @@ __device__ __forceinline__ void scan_experts_wave(const int32_t *cnt, int E, int
     s0 += c[i];
     s1 += (c[i] + kPrefillBM - 1) / kPrefillBM;
     s2 += c[i] > 0;
+    s3 += (c[i] + 15) >> 4;
   }
-  int i0 = s0, i1 = s1, i2 = s2;  // inclusive wave scans
+  int i0 = s0, i1 = s1, i2 = s2, i3 = s3;  // inclusive wave scans
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
     const int a0 = __shfl_up(i0, d, 64), a1 = __shfl_up(i1, d, 64), a2 = __shfl_up(i2, d, 64);
-    if (lane >= d) { i0 += a0; i1 += a1; i2 += a2; }
+    const int a3 = __shfl_up(i3, d, 64);
+    if (lane >= d) { i0 += a0; i1 += a1; i2 += a2; i3 += a3; }
   }
-  int r0 = i0 - s0, r1 = i1 - s1, r2 = i2 - s2;
+  int r0 = i0 - s0, r1 = i1 - s1, r2 = i2 - s2, r3 = i3 - s3;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int e = lane * 8 + i;
@@ -566,17 +572,22 @@ __device__ __forceinline__ void scan_experts_wave(const int32_t *cnt, int E, int
       if (p_offsets) p_offsets[e] = r0;
       if (cursor) cursor[e] = r0;
       mtile[e] = r1;
-      if (c[i] > 0) einfo[1 + r2] = int4{e, r0, c[i], 0};
+      if (c[i] > 0) {
+        einfo[1 + r2] = int4{e, r0, c[i], 0};
+        rcp[r2] = r3;
+      }
     }
     r0 += c[i];
     r1 += (c[i] + kPrefillBM - 1) / kPrefillBM;
     r2 += c[i] > 0;
+    r3 += (c[i] + 15) >> 4;
   }
   if (lane == 63) {
     offsets[E] = i0;
     if (p_offsets) p_offsets[E] = i0;
     mtile[E] = i1;
-    einfo[0] = int4{i2, 0, 0, 0};
+    einfo[0] = int4{i2, i3, 0, 0};
+    rcp[i2] = i3;
   }
 }
 
@@ -590,7 +601,8 @@ __device__ __forceinline__ void scan_experts_wave(const int32_t *cnt, int E, int
 __global__ __launch_bounds__(1024) void group_small_kernel(
     const int32_t *__restrict__ ids, const float *__restrict__ wts, const float *__restrict__ rowscale,
     int T, int E, int k, int32_t *__restrict__ offsets, int32_t *__restrict__ mtile,
-    int4 *__restrict__ einfo, int32_t *__restrict__ sorted_slots, int4 *__restrict__ rowinfo,
+    int4 *__restrict__ einfo, int32_t *__restrict__ rcp, int32_t *__restrict__ sorted_slots,
+    int4 *__restrict__ rowinfo,
     int32_t *__restrict__ inv_pos, int32_t *__restrict__ p_offsets, int32_t *__restrict__ p_sorted_tok,
     int32_t *__restrict__ p_inv) {
   __shared__ int32_t sm_ids[64 * 64];
@@ -605,7 +617,7 @@ __global__ __launch_bounds__(1024) void group_small_kernel(
   __syncthreads();
   for (int e = tid; e < E; e += 1024) cnt[e] = __popcll(mask[e]);
   __syncthreads();
-  if (tid < 64) scan_experts_wave(cnt, E, lane, offsets, mtile, einfo, p_offsets, off);
+  if (tid < 64) scan_experts_wave(cnt, E, lane, offsets, mtile, einfo, rcp, p_offsets, off);
   __syncthreads();
   for (int i = tid; i < T * k; i += 1024) {
     const int tt = i / k, e = sm_ids[i];
@@ -650,6 +662,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t *__restrict__ cnt, i
                                                     int32_t *__restrict__ offsets,
                                                     int32_t *__restrict__ mtile,
                                                     int4 *__restrict__ einfo,
+                                                    int32_t *__restrict__ rcp,
                                                     int32_t *__restrict__ p_offsets) {
   __shared__ int32_t tot[kMaxExperts];
   __shared__ int32_t off[kMaxExperts];
@@ -674,7 +687,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t *__restrict__ cnt, i
     }
   }
   __syncthreads();
-  if (tid < 64) scan_experts_wave(tot, E, tid, offsets, mtile, einfo, p_offsets, off);
+  if (tid < 64) scan_experts_wave(tot, E, tid, offsets, mtile, einfo, rcp, p_offsets, off);
   __syncthreads();
   for (int e0 = 0; e0 < E; e0 += 128) {
     const int e = e0 + (tid >> 3);
@@ -827,7 +840,8 @@ hipError_t launch_permute(const LayerDims &L, const FwdPtrs &P, const Workspace 
     hipLaunchKernelGGL(group_small_kernel, dim3(1), dim3(1024), 0, s, (const int32_t *)(ws + W.topk_ids),
                        (const float *)(ws + W.topk_w), decode && L.H > kRowRegsMaxH ? (const float *)nullptr : (const float *)(ws + W.rowscale),
                        P.T, L.E, L.k, (int32_t *)(ws + W.offsets), (int32_t *)(ws + W.mtile),
-                       (int4 *)(ws + W.active), (int32_t *)(ws + W.sorted_slots), (int4 *)(ws + W.rowinfo),
+                       (int4 *)(ws + W.active), (int32_t *)(ws + W.rcpre), (int32_t *)(ws + W.sorted_slots),
+                       (int4 *)(ws + W.rowinfo),
                        (int32_t *)(ws + W.inv_pos), P.p_offsets, P.p_sorted_tok, P.p_inv);
     return hipGetLastError();
   }
@@ -838,7 +852,7 @@ hipError_t launch_permute(const LayerDims &L, const FwdPtrs &P, const Workspace 
                      (const int32_t *)(ws + W.topk_ids), P.T, L.E, L.k, chunk, cnt);
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, cnt, nc, L.E,
                      (int32_t *)(ws + W.offsets), (int32_t *)(ws + W.mtile),
-                     (int4 *)(ws + W.active), P.p_offsets);
+                     (int4 *)(ws + W.active), (int32_t *)(ws + W.rcpre), P.p_offsets);
   hipLaunchKernelGGL(scatter_kernel, dim3(nc), dim3(256), (size_t)L.E * (4 * 8 + 4 * 4 + 4), s,
                      (const int32_t *)(ws + W.topk_ids), (const float *)(ws + W.topk_w),
                      decode && L.H > kRowRegsMaxH ? nullptr : (const float *)(ws + W.rowscale), P.T, L.E, L.k, chunk,
