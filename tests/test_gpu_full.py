@@ -45,8 +45,8 @@ def _layer(name):
 
 @pytest.mark.parametrize("T", [1, 8, 64, 128, 256])
 def test_decode_int4(T):
-    """Decode batches of the INT4 layer; T = 128 and 256 (8 and 16 rows per
-    expert) run the streaming gate/up GEMM."""
+    """Decode batches of the INT4 layer; T = 64, 128 and 256 (4, 8 and 16 rows
+    per expert) run the streaming gate/up GEMM."""
     log(f"[decode_int4] T={T}")
     w = synth.WORKLOADS["decode_int4"]
     g = _layer("decode_int4")

@@ -145,14 +145,16 @@ def test_decode_after_chunked_grouping(fmt, T):
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("T,k,E,H,I", [(16, 4, 8, 512, 256), (9, 8, 8, 256, 768),
                                        (40, 4, 16, 768, 512), (64, 8, 32, 1024, 1280),
-                                       (100, 2, 16, 2048, 256), (200, 8, 128, 512, 384)])
+                                       (100, 2, 16, 2048, 256), (200, 8, 128, 512, 384),
+                                       (64, 8, 128, 2048, 768), (40, 2, 16, 256, 256)])
 def test_streaming_decode(fmt, T, k, E, H, I):
-    """Decode batches with 8 to 16 rows per expert on average and H a multiple
+    """Decode batches with 4 to 16 rows per expert on average and H a multiple
     of 256 (at most 2048) run the streaming gate/up GEMM: experts holding 0, 1
     and up to 49 rows (several 16-row chunks, the hidden rows staged again
     between units), 1 to 8 chunks per unit (odd counts alternate the ring
-    slots across units), I not a multiple of 256, and from one unit per busy
-    block to many."""
+    slots across units), I not a multiple of 256, from one unit per busy block
+    to many, and unit ranges aligned to row chunks (T=64, 128 experts: three
+    units per block, half a chunk)."""
     log(f"[stream] fmt={fmt} T={T} k={k} E={E} H={H} I={I}")
     p13, p2 = quantized_layer(fmt, 23, T, E, H, I)
     g = GpuLayer(p13, p2, k)
@@ -160,26 +162,27 @@ def test_streaming_decode(fmt, T, k, E, H, I):
     x = synth.hidden_bf16(23, T, T, H)
     _, pr = _check_layer(g, lg, x, tag=f"{fmt} stream T={T} E={E} H={H} I={I}")
     counts = np.bincount(moe.route(lg, k)[0].ravel(), minlength=E)
-    assert 8 * E <= T * k <= 16 * E
+    assert 4 * E <= T * k <= 16 * E
     if T >= 40:
         assert counts.max() > 16, counts   # some expert spans two row chunks
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("T,k,E,H,I", [(40, 4, 32, 512, 256), (48, 8, 64, 384, 384),
-                                       (64, 8, 128, 256, 256), (30, 2, 16, 768, 512)])
+@pytest.mark.parametrize("T,k,E,H,I", [(24, 4, 32, 512, 256), (48, 8, 128, 384, 384),
+                                       (40, 4, 64, 256, 256), (30, 2, 16, 768, 512),
+                                       (64, 8, 128, 384, 256)])
 def test_decode_skewed_experts(fmt, T, k, E, H, I):
-    """Zipf-skewed routing with under 8 rows per expert on average and
-    experts of up to 64 rows: the register-streaming decode GEMMs (gate/up and
-    down) then take one 16-row chunk of an expert per unit, so an expert's
-    chunks spread over blocks."""
+    """Zipf-skewed routing with experts of up to 50 rows: the register-streaming
+    decode GEMMs then take one 16-row chunk of an expert per unit, so an
+    expert's chunks spread over blocks (gate/up below 4 rows per expert on
+    average or with H not a multiple of 256, the down projection always)."""
     log(f"[skew] fmt={fmt} T={T} k={k} E={E} H={H} I={I}")
     p13, p2 = quantized_layer(fmt, 29, T, E, H, I)
     g = GpuLayer(p13, p2, k)
     lg = synth.router_logits(29, T, T, E, "zipf")
     x = synth.hidden_bf16(29, T, T, H)
     counts = np.bincount(moe.route(lg, k)[0].ravel(), minlength=E)
-    assert T * k < 8 * E and T > 16 and counts.max() > 16, counts
+    assert (T * k < 4 * E or H % 256) and T > 16 and counts.max() > 16, counts
     _check_layer(g, lg, x, tag=f"{fmt} skew T={T} E={E} H={H} I={I}")
 
 

@@ -449,8 +449,9 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode(GemmArgs a) {
 // and across unit boundaries: no register ring, no block barrier for the
 // weights, and every copy instruction moves 8 rows x 128 contiguous bytes.  A
 // chunk is unpacked from LDS into the B operand of the 16x16x32 FP16 MFMA,
-// whose A operand is the unit's FP16 hidden rows (scaled by the routing
-// kernel), staged in LDS by the same copies whenever the row chunk changes.
+// whose A operand is the unit's hidden rows, copied (BF16) into LDS by the
+// same copies whenever the row chunk changes and converted there to FP16 with
+// the power of two the routing kernel found for each row.
 // INT4 / FP8 scales multiply each 128-wide k block's FP32 partial sum, as in
 // gemm_decode.  A chunk's scales travel the same way, by one more copy into a
 // per-wave LDS slot: the loop issues no load whose result lands in registers,
@@ -522,9 +523,20 @@ __global__ __launch_bounds__(512) void gemm_decode_stream(GemmArgs a) {
   }
   __syncthreads();
   const int UPE = a.tiles;
+  // Contiguous unit ranges of L = ceil(units / blocks) units.  When L divides
+  // the units of one row chunk, ranges start at multiples of L, so no range
+  // crosses a chunk (one row staging per block); otherwise ranges are spread
+  // proportionally (at most one more unit than the fewest).
   const int64_t n_units = (int64_t)rcpre[n_act] * UPE;
-  const int u0 = (int)((int64_t)blockIdx.x * n_units / gridDim.x);
-  const int u1 = (int)((int64_t)(blockIdx.x + 1) * n_units / gridDim.x);
+  const int64_t L = (n_units + gridDim.x - 1) / gridDim.x;
+  int u0, u1;
+  if (L > 0 && UPE % L == 0) {
+    u0 = (int)min<int64_t>((int64_t)blockIdx.x * L, n_units);
+    u1 = (int)min<int64_t>(u0 + L, n_units);
+  } else {
+    u0 = (int)((int64_t)blockIdx.x * n_units / gridDim.x);
+    u1 = (int)((int64_t)(blockIdx.x + 1) * n_units / gridDim.x);
+  }
   if (u0 >= u1) return;  // block-uniform
 
   struct Unit {
@@ -580,8 +592,9 @@ __global__ __launch_bounds__(512) void gemm_decode_stream(GemmArgs a) {
       copy16_lds(a.w + ((size_t)x.e * N + wrow(x, lr)) * RB + 128 * c + 16 * pc, dst + 1024 * q4);
     }
   };
-  // the unit's row records into rinf, then its hidden rows (by token) into As
-  // (all waves), by copies of up to 1 KB
+  // the unit's row records into rinf, then its BF16 hidden rows (by token)
+  // into As (all waves), by copies of up to 1 KB; to_f16 then converts them in
+  // place, once the copies have landed
   auto stage_rows = [&](const Unit &x) {
     if (threadIdx.x < 16) rinf[threadIdx.x] = threadIdx.x < x.nr ? a.rowinfo[x.r0 + threadIdx.x] : int4{0, 0, 0, 0};
     __syncthreads();
@@ -591,8 +604,23 @@ __global__ __launch_bounds__(512) void gemm_decode_stream(GemmArgs a) {
       const int src_row = __builtin_amdgcn_readfirstlane(rinf[m].y);
       const int off = pc * 1024 + 16 * lane;
       if (off < rowb)
-        copy16_lds((const unsigned char *)a.a_src + (size_t)src_row * rowb + off,
+        copy16_lds((const unsigned char *)a.hidden + (size_t)src_row * rowb + off,
                    (unsigned char *)As + (size_t)m * lda * 2 + pc * 1024);
+    }
+  };
+  // BF16 rows -> FP16 scaled by the row's 2^-s (the routing kernel's power of
+  // two, whose 2^s is the record's row scale; exact reciprocal of a power of
+  // two), in the INT4 unpack's k order for INT4, as the routing kernel stages
+  // rows for the prefill GEMMs
+  auto to_f16 = [&](const Unit &x) {
+    const int cpr = K >> 3;
+    for (int idx = threadIdx.x; idx < x.nr * cpr; idx += 512) {
+      const int m = idx / cpr, c = idx - m * cpr;
+      _Float16 *p = As + m * lda + c * 8;
+      const float down = __builtin_bit_cast(float, (uint32_t)(254u << 23) - (uint32_t)rinf[m].z);
+      u4 v = bf16x8_to_f16x8(*(const u4 *)p, down);
+      if (FMT == FMT_INT4) v = perm_0415(v);
+      *(u4 *)p = v;
     }
   };
 
@@ -701,6 +729,8 @@ __global__ __launch_bounds__(512) void gemm_decode_stream(GemmArgs a) {
       asm volatile("" ::: "memory");
       stage_rows(cur);
       wait_vmcnt<0>();  // this wave's row copies (and every chunk it has in flight)
+      __syncthreads();
+      to_f16(cur);
       __syncthreads();
       staged_rc = cur.rc;
     }

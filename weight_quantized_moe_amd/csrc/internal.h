@@ -157,12 +157,11 @@ constexpr int64_t kMaxTokens = 1 << 22;
 // Rows per expert at or below which the decode (weight-streaming) GEMMs run.
 bool use_decode_path(int64_t T, int E, int k, int H, int I);
 // Decode batches whose gate/up projection runs the streaming decode GEMM: H
-// (its K) a multiple of 256 and at most 2048, and at least 8 rows per expert
-// on average (T = 128 at 128 experts, top-8; below that the register-streaming
-// decode GEMM is as fast or faster, and for the down projection at every
-// size).  The routing kernel then stages their FP16 hidden rows as for prefill.
+// (its K) a multiple of 256 and at most 2048, and at least 4 rows per expert
+// on average (T = 64 at 128 experts, top-8; below that the register-streaming
+// decode GEMM is faster, and for the down projection at every size).
 inline bool use_decode_stream(int H, int E, int k, int64_t T) {
-  return H <= 2048 && H % 256 == 0 && T * k >= (int64_t)8 * E;
+  return H <= 2048 && H % 256 == 0 && T * k >= (int64_t)4 * E;
 }
 
 }  // namespace mq

@@ -811,9 +811,7 @@ hipError_t launch_route(const LayerDims &L, const FwdPtrs &P, const Workspace &W
   // scales only (2), the decode gate/up GEMM converts the rows it stages;
   // larger decode rows: the GEMM finds the scales too (0); W8A8: FP8 codes
   // and scales (3); W4A4: NVFP4 values and 1 / g (4)
-  const int stage_rows = P.w8a8 ? 3 : P.act_g13 > 0.f ? 4
-                       : !decode || use_decode_stream(L.H, L.E, L.k, P.T) ? 1
-                       : L.H <= kRowRegsMaxH ? 2 : 0;
+  const int stage_rows = P.w8a8 ? 3 : P.act_g13 > 0.f ? 4 : !decode ? 1 : L.H <= kRowRegsMaxH ? 2 : 0;
   if (P.gate_w && P.T >= kGateFusedMinT)  // router GEMM fused with the top-k
     return L.fmt == FMT_INT4 ? gate_route_dispatch<true>(L, P, W, stage_rows, s)
                              : gate_route_dispatch<false>(L, P, W, stage_rows, s);
