@@ -593,8 +593,12 @@ __global__ __launch_bounds__(512) void gemm_decode_stream(GemmArgs a) {
     }
   };
   // the unit's row records into rinf, then its BF16 hidden rows (by token)
-  // into As (all waves), by copies of up to 1 KB; to_f16 then converts them in
-  // place, once the copies have landed
+  // into As (all waves), by copies of up to 1 KB; once its copies have landed
+  // each lane converts the 16 bytes it copied in place: FP16 scaled by the
+  // row's 2^-s (the routing kernel's power of two, whose 2^s is the record's
+  // row scale; exact reciprocal of a power of two), in the INT4 unpack's k
+  // order for INT4, as the routing kernel stages rows for the prefill GEMMs.
+  // Leaves every copy of the wave complete; the caller's barrier publishes As.
   auto stage_rows = [&](const Unit &x) {
     if (threadIdx.x < 16) rinf[threadIdx.x] = threadIdx.x < x.nr ? a.rowinfo[x.r0 + threadIdx.x] : int4{0, 0, 0, 0};
     __syncthreads();
@@ -607,20 +611,17 @@ __global__ __launch_bounds__(512) void gemm_decode_stream(GemmArgs a) {
         copy16_lds((const unsigned char *)a.hidden + (size_t)src_row * rowb + off,
                    (unsigned char *)As + (size_t)m * lda * 2 + pc * 1024);
     }
-  };
-  // BF16 rows -> FP16 scaled by the row's 2^-s (the routing kernel's power of
-  // two, whose 2^s is the record's row scale; exact reciprocal of a power of
-  // two), in the INT4 unpack's k order for INT4, as the routing kernel stages
-  // rows for the prefill GEMMs
-  auto to_f16 = [&](const Unit &x) {
-    const int cpr = K >> 3;
-    for (int idx = threadIdx.x; idx < x.nr * cpr; idx += 512) {
-      const int m = idx / cpr, c = idx - m * cpr;
-      _Float16 *p = As + m * lda + c * 8;
-      const float down = __builtin_bit_cast(float, (uint32_t)(254u << 23) - (uint32_t)rinf[m].z);
-      u4 v = bf16x8_to_f16x8(*(const u4 *)p, down);
-      if (FMT == FMT_INT4) v = perm_0415(v);
-      *(u4 *)p = v;
+    wait_vmcnt<0>();  // this wave's row copies (and every chunk it has in flight)
+    for (int idx = wave; idx < x.nr * pieces; idx += 8) {
+      const int m = idx / pieces, pc = idx - m * pieces;
+      const int off = pc * 1024 + 16 * lane;
+      if (off < rowb) {
+        u4 *p = (u4 *)((unsigned char *)As + (size_t)m * lda * 2 + off);
+        const float down = __builtin_bit_cast(float, (uint32_t)(254u << 23) - (uint32_t)rinf[m].z);
+        u4 v = bf16x8_to_f16x8(*p, down);
+        if (FMT == FMT_INT4) v = perm_0415(v);
+        *p = v;
+      }
     }
   };
 
@@ -728,9 +729,6 @@ __global__ __launch_bounds__(512) void gemm_decode_stream(GemmArgs a) {
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       stage_rows(cur);
-      wait_vmcnt<0>();  // this wave's row copies (and every chunk it has in flight)
-      __syncthreads();
-      to_f16(cur);
       __syncthreads();
       staged_rc = cur.rc;
     }
