@@ -438,7 +438,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void gemm_decode(GemmArgs a) {
 }
 
 // ===========================================================================
-// Streaming decode gate/up GEMM (8 to 16 rows per expert on average,
+// Streaming decode gate/up GEMM (4 to 16 rows per expert on average,
 // K = H <= 2048).  The work is a list of units (one 16-row chunk of an
 // expert's grouped rows x 128 gate columns and the matching 128 up columns),
 // dealt to one persistent block per CU in contiguous ranges, so that
@@ -510,16 +510,28 @@ __global__ __launch_bounds__(512) void gemm_decode_stream(GemmArgs a) {
 
   // ---- the expert table and the grouping's prefix of its 16-row chunks, in
   // LDS (global loads consumed in the loop would make the wave wait for every
-  // copy in flight); count, records and prefix in one round trip
+  // copy in flight); count, records and prefix in one round trip (the
+  // workspace holds E + 1 of each; entries past the count are not kept)
   // (.w: the NVFP4 expert's 1 / global scale)
+  constexpr int NU = (kMaxExperts + 512) / 512;
+  int4 ev[NU];
+  int pv[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int i = threadIdx.x + 512 * u;
+    if (i < a.E) ev[u] = a.einfo[1 + i];
+    if (i <= a.E) pv[u] = a.rcp[i];
+  }
   const int n_act = __builtin_amdgcn_readfirstlane(a.einfo[0].x);
-  for (int i = threadIdx.x; i <= n_act; i += 512) {
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int i = threadIdx.x + 512 * u;
     if (i < n_act) {
-      int4 ei = a.einfo[1 + i];
+      int4 ei = ev[u];
       if (FMT == FMT_NVFP4) ei.w = __builtin_bit_cast(int, 1.0f / a.gscale[ei.x]);
       einf[i] = ei;
     }
-    rcpre[i] = a.rcp[i];
+    if (i <= n_act) rcpre[i] = pv[u];
   }
   __syncthreads();
   const int UPE = a.tiles;
