@@ -824,7 +824,7 @@ struct WideShape {
   static constexpr int LD = SPB * kWK + 8;
   static constexpr size_t ABUF = (size_t)kBM * LD * 2;
   static constexpr int BC = WPB * 32 * TN;
-  static constexpr size_t LDS = 2 * ABUF + 2 * BC * sizeof(float);
+  static constexpr size_t LDS = 2 * ABUF + 2 * BC * sizeof(float) + kBM * 16;
   static constexpr int AP = kBM / (8 * WPB);
 };
 
@@ -847,8 +847,9 @@ void gemm_prefill_wide(GemmArgs a) {
   constexpr int WC = 32 * TN, TH = TN / 2;  // columns per wave; gate (and up) tiles per wave
   constexpr size_t ABUF = Shape::ABUF;
   extern __shared__ __align__(16) unsigned char smem[];
-  float *colinv = (float *)(smem + 2 * ABUF);  // [BC]: 2^-p of each weight column
+  float *colinv = (float *)(smem + 2 * ABUF);  // [BC]: 2^-p of each weight column (not NVFP4)
   float *rowfs = colinv + BC;                  // [BC]: 2^p
+  int4 *rmeta = (int4 *)(rowfs + BC);          // [kBM]: the tile's grouped-row records
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int j = lane & 31, hh = lane >> 5;
   // ---- tile of this block
@@ -904,10 +905,13 @@ void gemm_prefill_wide(GemmArgs a) {
       rowfs[wave * WC + tn * 32 + j] = row_pow2(m * (FMT == FMT_INT4 ? 8.f : 448.f), &inv);
       colinv[wave * WC + tn * 32 + j] = inv;
     }
-  } else if (hh == 0) {
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn) colinv[wave * WC + tn * 32 + j] = 1.f;
   }
+
+  // ---- the epilogue's per-row data (slot, scale, routing weight), read now
+  // so that the epilogue issues no global load (each would wait for every
+  // store before it)
+  if (tid < kBM) rmeta[tid] = tid < nrows ? a.rowinfo[rbeg + tid] : int4{0, 0, 0, 0};
+  const float ginv = FMT == FMT_NVFP4 ? 1.0f / a.gscale[e] : 1.0f;
 
   // ---- activation staging: row (tid >> 3) + 8 WPB p, 16-byte chunk tid & 7
   const _Float16 *asrc[AP];
@@ -1093,7 +1097,6 @@ void gemm_prefill_wide(GemmArgs a) {
 
   // ---- epilogue: lane l holds grouped row m = 32 tm + l % 32 and, in
   // register v of tile tn, column 8 (v / 4) + 4 (l / 32) + v % 4 of the tile
-  const float ginv = FMT == FMT_NVFP4 ? 1.0f / a.gscale[e] : 1.0f;
   const int cl = 4 * hh;
   const float *cinv = colinv + wave * WC;
   uint32_t sat = 0u;
@@ -1105,19 +1108,23 @@ void gemm_prefill_wide(GemmArgs a) {
         const int row = tm * 32 + j;
         if (row >= nrows) continue;
         const int r = rbeg + row;
-        const float rsc = __builtin_bit_cast(float, a.rowinfo[r].z) * ginv;
+        const float rsc = __builtin_bit_cast(float, rmeta[row].z) * ginv;
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int c4 = 8 * g4 + cl;
 #pragma unroll
           for (int tn = 0; tn < TH; ++tn) {
-            const f4 ig = *(const f4 *)(cinv + tn * 32 + c4);
-            const f4 iu = *(const f4 *)(cinv + (tn + TH) * 32 + c4);
+            // column inverses (NVFP4: all 1, not applied)
+            f4 ig = {1.f, 1.f, 1.f, 1.f}, iu = ig;
+            if (FMT != FMT_NVFP4) {
+              ig = *(const f4 *)(cinv + tn * 32 + c4);
+              iu = *(const f4 *)(cinv + (tn + TH) * 32 + c4);
+            }
             h2 o[2];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const float gv = acc[tn][tm][4 * g4 + i] * (rsc * ig[i]);
-              const float uv = acc[tn + TH][tm][4 * g4 + i] * (rsc * iu[i]);
+              const float gv = acc[tn][tm][4 * g4 + i] * (FMT == FMT_NVFP4 ? rsc : rsc * ig[i]);
+              const float uv = acc[tn + TH][tm][4 * g4 + i] * (FMT == FMT_NVFP4 ? rsc : rsc * iu[i]);
               const float hv = silu(gv) * uv;
               const float hc = fminf(fmaxf(hv, -65504.f), 65504.f);
               sat |= hc != hv;
@@ -1141,7 +1148,7 @@ void gemm_prefill_wide(GemmArgs a) {
         const int row = tm * 32 + j;
         if (row >= nrows) continue;
         const int r = rbeg + row;
-        const float rsc = __builtin_bit_cast(float, a.rowinfo[r].z) * ginv;
+        const float rsc = __builtin_bit_cast(float, rmeta[row].z) * ginv;
 #pragma unroll
         for (int tn = 0; tn < TH; ++tn) {
           float hv[16];
@@ -1178,29 +1185,41 @@ void gemm_prefill_wide(GemmArgs a) {
     constexpr int RPI = 64 / LPR;  // rows per store instruction
     static_assert(WPB * 32 * TL * 2 <= (int)(2 * ABUF), "transpose buffers fit the activation buffers");
     _Float16 *tb = (_Float16 *)smem + wave * 32 * TL;
-    float vmax = 0.f, vnan = 0.f;  // largest |value| before the FP16 clamp; NaN sentinel
-    __syncthreads();               // every wave is done with the activation buffers
+    float vmax = 0.f;   // largest |value| before the FP16 clamp
+    bool vnan = false;  // some value is NaN
+    // the lane's column inverses, read once (NVFP4: all 1, not applied);
+    // read inside the row loop they would be re-read after every transpose
+    // store, which the compiler cannot tell apart from them
+    f4 icr[TN][4];
+    if (FMT != FMT_NVFP4) {
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) icr[tn][g4] = *(const f4 *)(cinv + tn * 32 + 8 * g4 + cl);
+    }
+    __syncthreads();  // every wave is done with the activation buffers
     if (wvalid) {
 #pragma unroll
       for (int tm = 0; tm < 4; ++tm) {
         if (tm * 32 >= nrows) break;
         const int row = tm * 32 + j;
         float rsc = 0.f;  // rows past the expert's end: zeros, never stored
-        if (row < nrows) rsc = __builtin_bit_cast(float, a.rowinfo[rbeg + row].w) * ginv * a.a_inv;
+        if (row < nrows) rsc = __builtin_bit_cast(float, rmeta[row].w) * ginv * a.a_inv;
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int c4 = 8 * g4 + cl;
 #pragma unroll
           for (int tn = 0; tn < TN; ++tn) {
-            const f4 ic = *(const f4 *)(cinv + tn * 32 + c4);
+            float v[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              v[i] = acc[tn][tm][4 * g4 + i] * (FMT == FMT_NVFP4 ? rsc : rsc * icr[tn][g4][i]);
+            vmax = fmaxf(vmax, fmaxf(fabsf(v[0]), fabsf(v[1])));
+            vmax = fmaxf(vmax, fmaxf(fabsf(v[2]), fabsf(v[3])));
+            vnan |= __builtin_isunordered(v[0], v[1]) | __builtin_isunordered(v[2], v[3]);
             h2 o[2];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float v = acc[tn][tm][4 * g4 + i] * (rsc * ic[i]);
-              vmax = fmaxf(vmax, fabsf(v));
-              vnan = __builtin_fmaf(v, 0.f, vnan);  // stays 0 unless v is NaN or infinite
-              o[i >> 1][i & 1] = (_Float16)fminf(fmaxf(v, -65504.f), 65504.f);
-            }
+            for (int i = 0; i < 4; ++i) o[i >> 1][i & 1] = (_Float16)fminf(fmaxf(v[i], -65504.f), 65504.f);
             *(u2 *)(tb + j * TL + tn * 32 + c4) = u2{as_u32(o[0]), as_u32(o[1])};
           }
         }
@@ -1214,13 +1233,13 @@ void gemm_prefill_wide(GemmArgs a) {
           const int orow = tm * 32 + rr;
           const u4 v = *(const u4 *)(tb + rr * TL + ch * 8);
           if (orow < nrows)
-            *(u4 *)(a.partial + (size_t)a.rowinfo[rbeg + orow].x * a.H + cb + ch * 8) = v;
+            *(u4 *)(a.partial + (size_t)rmeta[orow].x * a.H + cb + ch * 8) = v;
         }
         __builtin_amdgcn_s_waitcnt(0xC07F);
         __builtin_amdgcn_wave_barrier();
       }
     }
-    sat |= !(vmax <= 65504.f) || vnan != 0.f;  // NaN counts as saturated
+    sat |= !(vmax <= 65504.f) || vnan;  // NaN counts as saturated
   }
   flag_saturation(a, sat);
 }
