@@ -62,7 +62,7 @@ constexpr int kW8WBytes = kW8BN * kW8K;
 constexpr int kW8StageBytes = kW8ABytes + kW8WBytes + kW8BM * 4;
 static_assert(kW8BM == kPrefillBM, "tiles follow the grouping's M-tile prefix");
 constexpr int kW8MaxG = kMaxGemmK / kW8K;
-constexpr int kW8Lds = kW8Stages * kW8StageBytes + 4 * kW8BM * 4 + 2 * kW8MaxG * 4;
+constexpr int kW8Lds = kW8Stages * kW8StageBytes + 4 * kW8BM * 4 + 2 * kW8MaxG * 4 + kW8BM * 16;
 static_assert(kW8Lds <= kMaxLdsBytes, "stages fit in LDS");
 
 __device__ __forceinline__ f16v mfma_fp8(const i8v &a, const i8v &b, const f16v &c) {
@@ -103,6 +103,7 @@ void gemm_w8a8(W8Args a) {
   extern __shared__ __align__(16) unsigned char smem[];
   float *hmax = (float *)(smem + kW8Stages * kW8StageBytes);   // [4][128] (gate/up)
   float *sws = hmax + 4 * kW8BM;                                // [2][G]: the block's weight scales
+  int4 *rmeta = (int4 *)(sws + 2 * kW8MaxG);                    // [128]: the tile's row records (down)
   // the wave index as a scalar, so that per-wave addresses and the weight
   // scale loads stay in scalar registers
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -146,6 +147,10 @@ void gemm_w8a8(W8Args a) {
     const bool ok = STAGE == 0 ? nt * 128 < a.I : n0 < N;
     sws[idx] = ok ? a.wscale[((size_t)e * (N / 128) + n0 / 128) * G + g] : 0.f;
   }
+
+  // the down epilogue's row records (slot, routing weight), read now so that
+  // the epilogue issues no global load between its stores
+  if (STAGE == 1 && tid < kW8BM) rmeta[tid] = tid < nrows ? a.rowinfo[rbeg + tid] : int4{0, 0, 0, 0};
 
   // ---- copy sources of this lane: activation copies q = 2 wave + [0, 2)
   // and weight copies q = 4 wave + [0, 4) of each k step; copy q's lane i
@@ -336,7 +341,7 @@ void gemm_w8a8(W8Args a) {
       for (int tm = 0; tm < 2; ++tm) {
         if (64 * rh + 32 * tm >= nrows) break;
         const int row = 64 * rh + 32 * tm + j;
-        const float wt = row < nrows ? __builtin_bit_cast(float, a.rowinfo[rbeg + row].w) : 0.f;
+        const float wt = row < nrows ? __builtin_bit_cast(float, rmeta[row].w) : 0.f;
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4)
 #pragma unroll
@@ -359,7 +364,7 @@ void gemm_w8a8(W8Args a) {
           const int rr = it * 8 + (lane >> 3);
           const int orow = 64 * rh + 32 * tm + rr;
           const u4 v = *(const u4 *)(tb + rr * TL + ch * 8);
-          if (orow < nrows) *(u4 *)(a.partial + (size_t)a.rowinfo[rbeg + orow].x * a.H + cb + ch * 8) = v;
+          if (orow < nrows) *(u4 *)(a.partial + (size_t)rmeta[orow].x * a.H + cb + ch * 8) = v;
         }
         __builtin_amdgcn_s_waitcnt(0xC07F);
         __builtin_amdgcn_wave_barrier();
