@@ -69,6 +69,8 @@ def test_dequantize_bit_exact(fmt):
 
 @pytest.mark.parametrize("logit_kind", ["f32", "bf16_ties"])
 @pytest.mark.parametrize("T,E,k", [(1, 128, 8), (37, 128, 8), (64, 128, 8), (65, 128, 8),
+                                   (128, 128, 8), (256, 128, 8), (130, 512, 31), (255, 16, 16),
+                                   (200, 128, 32), (257, 128, 8),
                                    (300, 128, 8), (2500, 128, 8), (37, 200, 20), (300, 200, 6),
                                    (50, 512, 64), (700, 512, 3)])
 def test_routing_and_grouping_bit_exact(T, E, k, logit_kind):
@@ -87,6 +89,34 @@ def test_routing_and_grouping_bit_exact(T, E, k, logit_kind):
         lgf = np.round(rng.standard_normal((T, E)) * 4) / 4
         bits = synth.to_bf16_bits(lgf.astype(np.float32))
         out, pr, _ = g.run(bits, x, probe=True, logits_bf16=True)
+        check_routing(pr, moe.bf16_bits_to_f64(bits), k, E)
+
+
+@pytest.mark.parametrize("logit_kind", ["f32", "bf16"])
+def test_signed_zero_logits_tie(logit_kind):
+    """-0 and +0 are equal logits: their order in the top-k falls to the expert
+    id, as for any other tie (rows whose k-th largest logit is a zero of either
+    sign, and rows of zeros only)."""
+    log(f"[routing] signed zeros, logits={logit_kind}")
+    T, E, k, H, I = 48, 16, 5, 256, 128
+    rng = np.random.default_rng(3)
+    lg = np.zeros((T, E), np.float32)
+    for t in range(T):
+        nz = rng.choice(E, size=int(rng.integers(0, 4)), replace=False)
+        lg[t, nz] = rng.choice([1.0, 2.0, -1.0], size=len(nz))
+        neg0 = rng.random(E) < 0.5
+        z = lg[t] == 0
+        lg[t, z & neg0] = -0.0
+    assert np.signbit(lg[lg == 0]).any() and (~np.signbit(lg[lg == 0])).any()
+    p13, p2 = random_layer(formats.INT4, 5, E, H, I)
+    g = GpuLayer(p13, p2, k)
+    x = synth.hidden_bf16(7, 0, T, H)
+    if logit_kind == "f32":
+        _, pr, _ = g.run(lg, x, probe=True)
+        check_routing(pr, lg, k, E)
+    else:
+        bits = synth.to_bf16_bits(lg)
+        _, pr, _ = g.run(bits, x, probe=True, logits_bf16=True)
         check_routing(pr, moe.bf16_bits_to_f64(bits), k, E)
 
 

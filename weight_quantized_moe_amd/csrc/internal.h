@@ -9,6 +9,9 @@
 namespace mq {
 
 constexpr int kMaxExperts = 512;
+// Grouping in one workgroup (token bit masks per expert) up to these sizes.
+constexpr int kSmallT = 256;      // tokens
+constexpr int kSmallRows = 4096;  // routed rows T k
 constexpr int kMaxGateExperts = 256;  // experts the fused router + top-k kernel holds in LDS
 // Batches of at least this many tokens route from the gate's weight with the
 // fused router + top-k kernel; smaller ones run the router-logits kernel into
@@ -16,7 +19,7 @@ constexpr int kMaxGateExperts = 256;  // experts the fused router + top-k kernel
 // kernel's block runs its GEMM, top-k and row staging back to back).
 constexpr int64_t kGateFusedMinT = 4096;
 constexpr int kPrefillBM = 128;  // token rows per prefill M-tile
-constexpr int kMaxChunks = 256;  // token chunks of the grouping for T > 64
+constexpr int kMaxChunks = 256;  // token chunks of the three-launch grouping
 // Hidden rows of at most this many values are read whole into the registers
 // of one wave by the routing kernel, which then also finds each row's power of
 // two (and, for prefill, writes the FP16 row); longer rows are scanned by the

@@ -17,9 +17,11 @@
 namespace mq {
 
 // Order-preserving map of an IEEE float to an unsigned integer (every bit
-// pattern, NaN included, gets a distinct position in a total order).
+// pattern, NaN included, gets a position in a total order).  -0 maps to the
+// key of +0: the two are equal logits, so their order falls to the expert id.
 __device__ __forceinline__ uint32_t ordered_key(float v) {
   uint32_t b = __builtin_bit_cast(uint32_t, v);
+  if ((b << 1) == 0u) b = 0u;
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 __device__ __forceinline__ float from_ordered_key(uint32_t o) {
@@ -592,11 +594,12 @@ __device__ __forceinline__ void scan_experts_wave(const int32_t *cnt, int E, int
 }
 
 // ---------------------------------------------------------------------------
-// T <= 64: grouping in one workgroup of 1024 threads, after route_kernel's
-// top-k (whose 16-lane-per-token selection is VALU work worth spreading over
-// several CUs).  One 64-bit token mask per expert gives the counts (popcount)
-// and the stable rank of every token inside its expert (popcount of the mask
-// bits below it).
+// T <= kSmallT (and T k <= kSmallRows): grouping in one workgroup of 1024
+// threads, after route_kernel's top-k (whose 16-lane-per-token selection is
+// VALU work worth spreading over several CUs).  A bit mask of tokens per
+// expert (one 64-bit word per 64 tokens) gives the counts (popcounts) and the
+// stable rank of every token inside its expert (popcount of the mask bits
+// below it).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void group_small_kernel(
     const int32_t *__restrict__ ids, const float *__restrict__ wts, const float *__restrict__ rowscale,
@@ -605,24 +608,33 @@ __global__ __launch_bounds__(1024) void group_small_kernel(
     int4 *__restrict__ rowinfo,
     int32_t *__restrict__ inv_pos, int32_t *__restrict__ p_offsets, int32_t *__restrict__ p_sorted_tok,
     int32_t *__restrict__ p_inv) {
-  __shared__ int32_t sm_ids[64 * 64];
-  __shared__ uint64_t mask[kMaxExperts];
+  __shared__ int32_t sm_ids[kSmallRows];
+  __shared__ uint64_t mask[kMaxExperts * (kSmallT / 64)];  // [E][NW]
   __shared__ int32_t cnt[kMaxExperts];
   __shared__ int32_t off[kMaxExperts];
   const int tid = threadIdx.x, lane = tid & 63;
-  for (int e = tid; e < E; e += 1024) mask[e] = 0ull;
+  const int NW = (T + 63) >> 6;  // mask words per expert
+  for (int i = tid; i < E * NW; i += 1024) mask[i] = 0ull;
   for (int i = tid; i < T * k; i += 1024) sm_ids[i] = ids[i];
   __syncthreads();
-  for (int i = tid; i < T * k; i += 1024) atomicOr(&mask[sm_ids[i]], 1ull << (i / k));
+  for (int i = tid; i < T * k; i += 1024) {
+    const int tt = i / k;
+    atomicOr(&mask[sm_ids[i] * NW + (tt >> 6)], 1ull << (tt & 63));
+  }
   __syncthreads();
-  for (int e = tid; e < E; e += 1024) cnt[e] = __popcll(mask[e]);
+  for (int e = tid; e < E; e += 1024) {
+    int c = 0;
+    for (int w = 0; w < NW; ++w) c += __popcll(mask[e * NW + w]);
+    cnt[e] = c;
+  }
   __syncthreads();
   if (tid < 64) scan_experts_wave(cnt, E, lane, offsets, mtile, einfo, rcp, p_offsets, off);
   __syncthreads();
   for (int i = tid; i < T * k; i += 1024) {
-    const int tt = i / k, e = sm_ids[i];
-    const uint64_t below = tt == 0 ? 0ull : (~0ull >> (64 - tt));
-    const int pos = off[e] + __popcll(mask[e] & below);
+    const int tt = i / k, e = sm_ids[i], tw = tt >> 6, tb = tt & 63;
+    const uint64_t below = tb == 0 ? 0ull : (~0ull >> (64 - tb));
+    int pos = off[e] + __popcll(mask[e * NW + tw] & below);
+    for (int w = 0; w < tw; ++w) pos += __popcll(mask[e * NW + w]);
     sorted_slots[pos] = i;
     const float rs = rowscale ? rowscale[tt] : 0.f;
     rowinfo[pos] = int4{i, tt, __builtin_bit_cast(int, rs), __builtin_bit_cast(int, wts[i])};
@@ -633,7 +645,7 @@ __global__ __launch_bounds__(1024) void group_small_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Stable grouping by expert for T > 64, in three launches over chunks of
+// Stable grouping by expert for larger batches, in three launches over chunks of
 // consecutive tokens (at most kMaxChunks chunks):
 //   1. hist_kernel:    per-chunk expert counts cnt[c][e];
 //   2. scan_kernel:    one workgroup turns them into the exclusive position of
@@ -834,7 +846,7 @@ hipError_t launch_route(const LayerDims &L, const FwdPtrs &P, const Workspace &W
 hipError_t launch_permute(const LayerDims &L, const FwdPtrs &P, const Workspace &W, bool decode,
                           hipStream_t s) {
   char *ws = P.ws;
-  if (P.T <= 64) {
+  if (P.T <= kSmallT && P.T * L.k <= kSmallRows) {
     hipLaunchKernelGGL(group_small_kernel, dim3(1), dim3(1024), 0, s, (const int32_t *)(ws + W.topk_ids),
                        (const float *)(ws + W.topk_w), decode && L.H > kRowRegsMaxH ? (const float *)nullptr : (const float *)(ws + W.rowscale),
                        P.T, L.E, L.k, (int32_t *)(ws + W.offsets), (int32_t *)(ws + W.mtile),
