@@ -217,6 +217,30 @@ def test_decode_skewed_experts(fmt, T, k, E, H, I):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("T,k,E,H,I", [(1, 8, 128, 2048, 768), (1, 3, 16, 256, 384),
+                                       (2, 12, 32, 512, 256), (2, 8, 64, 384, 1152),
+                                       (2, 1, 8, 256, 128), (3, 8, 64, 384, 1152)])
+@pytest.mark.parametrize("with_res", [False, True])
+def test_decode_down_fused_combine(fmt, T, k, E, H, I, with_res):
+    """One or two tokens: the decode down projection adds each token's slots
+    itself (slot values in FP32, slots in order, then the residual) and writes
+    the BF16 output; no combine launch.  Covers both column-block widths (8
+    columns at T = 1, 16 at T = 2), more slots than waves (k = 12), k parts
+    without a chunk (I = 128, 256, 384) and uneven ones (I = 1152), H not a
+    multiple of 256, and the first batch size past the limit (T = 3: the
+    expert-major GEMM and the combine)."""
+    log(f"[down-fused] fmt={fmt} T={T} k={k} E={E} H={H} I={I} res={with_res}")
+    p13, p2 = quantized_layer(fmt, 37, T, E, H, I)
+    g = GpuLayer(p13, p2, k)
+    lg = synth.router_logits(37, T, T, E)
+    x = synth.hidden_bf16(37, T, T, H)
+    res = synth.residual_bf16(37, T, T, H) if with_res else None
+    out1, _ = _check_layer(g, lg, x, res, tag=f"{fmt} fused down T={T} k={k} I={I}")
+    out2, _, _ = g.run(lg, x, res)
+    assert np.array_equal(out1, out2), "repeat runs differ"
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("T", [20, 700])
 def test_hidden_not_multiple_of_256(fmt, T):
     """H = 384: the prefill down projection's last 256-column tile is half full."""

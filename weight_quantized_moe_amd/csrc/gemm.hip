@@ -57,6 +57,12 @@ struct GemmArgs {
   float a_inv;            // down: factor on the sums (W4A4: 1 / the global scale of h; else 1)
   int rc_off;             // decode: byte offset in dynamic LDS of the 16-row-chunk table
                           // (units are 16-row chunks); 0: units are whole experts
+  // decode down projection with the combine fused in (a few tokens)
+  const int32_t *slot_ids;   // [T k]: expert of slot (t, j)
+  const int32_t *slot_pos;   // [T k]: grouped row of slot (t, j)
+  const float *slot_w;       // [T k]: routing weight of slot (t, j)
+  const uint16_t *residual;  // BF16 [T, H] or null
+  uint16_t *out;             // BF16 [T, H]
 };
 
 // Saturate to the FP16 range, remembering whether anything was clamped.
@@ -1245,6 +1251,117 @@ void gemm_prefill_wide(GemmArgs a) {
 }
 
 // ===========================================================================
+// Decode down projection with the combine fused in, for a few tokens
+// (T <= kTokDownMaxT, where the expert-major GEMM and the combine are two
+// short latency-bound launches).  One block per (token t, CB output columns);
+// wave j takes the token's slots j, j + 8, ...: expert ids[t k + j], its
+// grouped intermediate row inv_pos[t k + j] and routing weight.  Lane l is
+// column l % CB of the block and k part l / CB; a part takes every (64 / CB)-th
+// 64-wide k chunk (each inside one 128-wide scale group), converts the
+// column's codes of the chunk to exact FP16 values and takes FP32 dot products
+// with the h row (two products per instruction).  INT4 / FP8 scales multiply
+// each chunk's sum in FP32, as in gemm_decode; NVFP4 block scales each 16-wide
+// block's sum, 1/g the slot's total.  The parts are added across lanes, the
+// slot's CB values times its routing weight go to LDS, and CB threads add the
+// slots in order j = 0..k-1 (then the residual) into the BF16 output.  The
+// slot values stay FP32: no FP16 partials, no partial buffer, no combine.
+// A lane loads the codes and h of up to kTDBatch chunks before it multiplies.
+// ===========================================================================
+constexpr int kTokDownMaxT = 2;
+constexpr int kTDBatch = 3;
+
+template <int FMT, int CB>
+__global__ __launch_bounds__(512) void gemm_decode_down_tok(GemmArgs a) {
+  constexpr int QP = 64 / CB;                        // k parts per column
+  constexpr int WQ = FMT == FMT_FP8 ? 4 : 2;         // 16-byte code loads per chunk
+  __shared__ float red[64][CB];                      // [slot][column], k <= 64
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int c = lane % CB, qp = lane / CB;
+  const int t = blockIdx.y, n0 = blockIdx.x * CB, n = n0 + c;
+  const int K = a.K, N = a.N, G = K / 128, NCH = K / 64, k = a.k;
+  const size_t RB = FMT == FMT_FP8 ? (size_t)K : (size_t)K / 2;
+  for (int j = wave; j < k; j += 8) {
+    const int slot = t * k + j;
+    const int e = __builtin_amdgcn_readfirstlane(a.slot_ids[slot]);
+    const int r = __builtin_amdgcn_readfirstlane(a.slot_pos[slot]);
+    const float wt = a.slot_w[slot] * (FMT == FMT_NVFP4 ? 1.0f / a.gscale[e] : 1.0f);
+    const uint8_t *wrow = a.w + ((size_t)e * N + n) * RB;
+    const _Float16 *hrow = a.a_src + (size_t)r * K;
+    float acc = 0.f;
+    for (int cb = qp; cb < NCH; cb += kTDBatch * QP) {
+      u4 wv[kTDBatch][WQ], hv[kTDBatch][8];
+      uint32_t sv[kTDBatch];
+#pragma unroll
+      for (int b = 0; b < kTDBatch; ++b) {
+        const int ch = cb + b * QP;
+        if (ch < NCH) {
+#pragma unroll
+          for (int i = 0; i < WQ; ++i) wv[b][i] = *(const u4 *)(wrow + (size_t)ch * (16 * WQ) + 16 * i);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) hv[b][i] = *(const u4 *)(hrow + ch * 64 + 8 * i);
+          if (FMT == FMT_INT4)
+            sv[b] = ((const uint16_t *)a.scale)[((size_t)e * N + n) * G + ch / 2];
+          else if (FMT == FMT_FP8)
+            sv[b] = ((const uint32_t *)a.scale)[((size_t)e * (N / 128) + n / 128) * G + ch / 2];
+          else
+            sv[b] = *(const uint32_t *)((const uint8_t *)a.scale + ((size_t)e * N + n) * (K / 16) + ch * 4);
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < kTDBatch; ++b) {
+        if (cb + b * QP >= NCH) break;
+        float sum = 0.f;
+        if (FMT == FMT_NVFP4) {
+#pragma unroll
+          for (int sb = 0; sb < 4; ++sb) {  // 16-wide blocks: words 2 sb, 2 sb + 1
+            float bs = 0.f;
+#pragma unroll
+            for (int ww = 2 * sb; ww < 2 * sb + 2; ++ww) {
+              const uint32_t word = wv[b][ww >> 2][ww & 3];
+#pragma unroll
+              for (int bs8 = 0; bs8 < 4; ++bs8)
+                bs = __builtin_amdgcn_fdot2(e2m1x2_to_h2(word, bs8), as_h2(hv[b][ww][bs8]), bs, false);
+            }
+            sum += bs * (float)e4m3_to_f16((sv[b] >> (8 * sb)) & 0xFFu);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {  // k 8 i + [0, 8) of the chunk
+            h8 wf;
+            u4 hp = hv[b][i];
+            if (FMT == FMT_INT4) {
+              wf = unpack_int4(wv[b][i >> 2][i & 3]);
+              hp = perm_0415(hp);  // the unpack's k order 0, 4, 1, 5, ...
+            } else {
+              wf = unpack_fp8(wv[b][(2 * i) >> 2][(2 * i) & 3], wv[b][(2 * i + 1) >> 2][(2 * i + 1) & 3]);
+            }
+            const u4 wu = as_u4(wf);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) sum = __builtin_amdgcn_fdot2(as_h2(wu[q]), as_h2(hp[q]), sum, false);
+          }
+          sum *= FMT == FMT_INT4 ? (float)__builtin_bit_cast(_Float16, (uint16_t)sv[b])
+                                 : __builtin_bit_cast(float, sv[b]);
+        }
+        acc += sum;
+      }
+    }
+    // the k parts of a column, added in a fixed pattern (every lane ends
+    // with the same value)
+#pragma unroll
+    for (int d = CB; d < 64; d <<= 1) acc += __shfl_xor(acc, d, 64);
+    if (qp == 0) red[j][c] = acc * wt;
+  }
+  __syncthreads();
+  if (threadIdx.x < CB) {
+    float o = 0.f;
+    for (int j = 0; j < k; ++j) o += red[j][threadIdx.x];
+    const size_t oi = (size_t)t * a.H + n0 + threadIdx.x;
+    if (a.residual) o = bf16_to_f32(a.residual[oi]) + o;
+    a.out[oi] = f32_to_bf16_rne(o);
+  }
+}
+
+// ===========================================================================
 // Combine: out[t] = bf16(sum_j partial[t*k + j] (+ residual[t])), the FP16
 // partials widened to FP32 and added in order j = 0..k-1 so repeated runs are
 // bit-identical.  kStream: non-temporal partial loads, for a partial buffer
@@ -1361,6 +1478,11 @@ static GemmArgs make_args(const LayerDims &L, const FwdPtrs &P, const Workspace 
   a.tiles = 0;
   a.hq_g = P.act_g2;
   a.a_inv = stage == 1 && P.act_g2 > 0.f ? 1.f / P.act_g2 : 1.f;
+  a.slot_ids = (const int32_t *)(ws + W.topk_ids);
+  a.slot_pos = (const int32_t *)(ws + W.inv_pos);
+  a.slot_w = (const float *)(ws + W.topk_w);
+  a.residual = P.residual;
+  a.out = P.out;
   return a;
 }
 
@@ -1526,6 +1648,22 @@ static hipError_t run_prefill_wide(GemmArgs a, int64_t R, const GemmLaunch &s) {
 }
 
 template <int FMT>
+static hipError_t run_decode_down_tok(GemmArgs a, const GemmLaunch &s) {
+  // one token: 8 columns per block (H / 8 blocks); more: 16
+  if (a.T == 1)
+    hipExtLaunchKernelGGL((gemm_decode_down_tok<FMT, 8>), dim3((unsigned)(a.N / 8), 1u), dim3(512), 0u,
+                          s.stream, s.start, s.stop, 0u, a);
+  else
+    hipExtLaunchKernelGGL((gemm_decode_down_tok<FMT, 16>), dim3((unsigned)(a.N / 16), (unsigned)a.T), dim3(512),
+                          0u, s.stream, s.start, s.stop, 0u, a);
+  return hipGetLastError();
+}
+
+bool down_writes_output(const LayerDims &L, const FwdPtrs &P, bool decode) {
+  return decode && !P.w8a8 && P.act_g13 == 0.f && P.T <= kTokDownMaxT && L.H % 16 == 0 && L.I % 64 == 0;
+}
+
+template <int FMT>
 static hipError_t run_decode_stream(GemmArgs a, const GemmLaunch &s) {
   if (a.K > kDSMaxK || a.K % 256) return hipErrorInvalidValue;
   a.tiles = (a.I + 127) / 128;  // units per 16-row chunk
@@ -1547,6 +1685,15 @@ static hipError_t dispatch(const LayerDims &L, const FwdPtrs &P, const Workspace
         case FMT_INT4: return run_decode_stream<FMT_INT4>(a, s);
         case FMT_FP8: return run_decode_stream<FMT_FP8>(a, s);
         default: return run_decode_stream<FMT_NVFP4>(a, s);
+      }
+    }
+  }
+  if constexpr (STAGE == 1) {
+    if (down_writes_output(L, P, decode)) {
+      switch (L.fmt) {
+        case FMT_INT4: return run_decode_down_tok<FMT_INT4>(a, s);
+        case FMT_FP8: return run_decode_down_tok<FMT_FP8>(a, s);
+        default: return run_decode_down_tok<FMT_NVFP4>(a, s);
       }
     }
   }

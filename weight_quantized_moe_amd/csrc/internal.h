@@ -122,6 +122,9 @@ hipError_t launch_gate_up(const LayerDims &L, const FwdPtrs &P, const Workspace 
 hipError_t launch_down(const LayerDims &L, const FwdPtrs &P, const Workspace &W, bool decode,
                        const GemmLaunch &s);
 hipError_t launch_combine(const LayerDims &L, const FwdPtrs &P, const Workspace &W, hipStream_t s);
+// True when launch_down writes the layer output itself (the decode down
+// projection with the combine fused in, for a few tokens): no combine launch.
+bool down_writes_output(const LayerDims &L, const FwdPtrs &P, bool decode);
 hipError_t launch_dequantize(const LayerDims &L, int which, int expert, float *out, hipStream_t s);
 hipError_t launch_import_expert(const LayerDims &L, int e, const mq_src_proj &gate,
                                 const mq_src_proj &up, const mq_src_proj &down, int gptq_offset,

@@ -273,7 +273,7 @@ mq_status mq::forward_impl(const mq_layer *L, const void *router_logits, int32_t
            : mq::launch_down(D, P, W, decode, kev(MQ_STAGE_DOWN));
   if (e != hipSuccess) return fail(MQ_E_HIP, "forward: down launch: %s", hipGetErrorString(e));
   ev(MQ_STAGE_COMBINE, 0);
-  if ((e = mq::launch_combine(D, P, W, s)) != hipSuccess)
+  if (!mq::down_writes_output(D, P, decode) && (e = mq::launch_combine(D, P, W, s)) != hipSuccess)
     return fail(MQ_E_HIP, "forward: combine launch: %s", hipGetErrorString(e));
   ev(MQ_STAGE_COMBINE, 1);
   g_err[0] = 0;
