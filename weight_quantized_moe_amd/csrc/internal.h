@@ -12,6 +12,7 @@ constexpr int kMaxExperts = 512;
 // Grouping in one workgroup (token bit masks per expert) up to these sizes.
 constexpr int kSmallT = 256;      // tokens
 constexpr int kSmallRows = 4096;  // routed rows T k
+constexpr int kFusedT = 16;       // decode: routing and grouping in one launch up to this many tokens
 constexpr int kMaxGateExperts = 256;  // experts the fused router + top-k kernel holds in LDS
 // Batches of at least this many tokens route from the gate's weight with the
 // fused router + top-k kernel; smaller ones run the router-logits kernel into
@@ -125,6 +126,9 @@ hipError_t launch_combine(const LayerDims &L, const FwdPtrs &P, const Workspace 
 // True when launch_down writes the layer output itself (the decode down
 // projection with the combine fused in, for a few tokens): no combine launch.
 bool down_writes_output(const LayerDims &L, const FwdPtrs &P, bool decode);
+// True when launch_route also groups the rows (a few decode tokens): then
+// launch_permute launches nothing.
+bool route_groups(const LayerDims &L, const FwdPtrs &P, bool decode);
 hipError_t launch_dequantize(const LayerDims &L, int which, int expert, float *out, hipStream_t s);
 hipError_t launch_import_expert(const LayerDims &L, int e, const mq_src_proj &gate,
                                 const mq_src_proj &up, const mq_src_proj &down, int gptq_offset,

@@ -601,28 +601,30 @@ __device__ __forceinline__ void scan_experts_wave(const int32_t *cnt, int E, int
 // stable rank of every token inside its expert (popcount of the mask bits
 // below it).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void group_small_kernel(
-    const int32_t *__restrict__ ids, const float *__restrict__ wts, const float *__restrict__ rowscale,
-    int T, int E, int k, int32_t *__restrict__ offsets, int32_t *__restrict__ mtile,
-    int4 *__restrict__ einfo, int32_t *__restrict__ rcp, int32_t *__restrict__ sorted_slots,
-    int4 *__restrict__ rowinfo,
+// NTH threads of one workgroup group the T k (token, slot) pairs whose experts
+// are ids[] (ids, wts and rowscale may be in LDS or global memory).
+template <int NTH>
+__device__ __forceinline__ void group_small_body(
+    const int32_t *ids, const float *wts, const float *rowscale, int T, int E, int k,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ mtile, int4 *__restrict__ einfo,
+    int32_t *__restrict__ rcp, int32_t *__restrict__ sorted_slots, int4 *__restrict__ rowinfo,
     int32_t *__restrict__ inv_pos, int32_t *__restrict__ p_offsets, int32_t *__restrict__ p_sorted_tok,
-    int32_t *__restrict__ p_inv) {
-  __shared__ int32_t sm_ids[kSmallRows];
+    int32_t *__restrict__ p_inv, int32_t *sm_ids) {
   __shared__ uint64_t mask[kMaxExperts * (kSmallT / 64)];  // [E][NW]
   __shared__ int32_t cnt[kMaxExperts];
   __shared__ int32_t off[kMaxExperts];
   const int tid = threadIdx.x, lane = tid & 63;
   const int NW = (T + 63) >> 6;  // mask words per expert
-  for (int i = tid; i < E * NW; i += 1024) mask[i] = 0ull;
-  for (int i = tid; i < T * k; i += 1024) sm_ids[i] = ids[i];
+  for (int i = tid; i < E * NW; i += NTH) mask[i] = 0ull;
+  if (sm_ids != ids)
+    for (int i = tid; i < T * k; i += NTH) sm_ids[i] = ids[i];
   __syncthreads();
-  for (int i = tid; i < T * k; i += 1024) {
+  for (int i = tid; i < T * k; i += NTH) {
     const int tt = i / k;
     atomicOr(&mask[sm_ids[i] * NW + (tt >> 6)], 1ull << (tt & 63));
   }
   __syncthreads();
-  for (int e = tid; e < E; e += 1024) {
+  for (int e = tid; e < E; e += NTH) {
     int c = 0;
     for (int w = 0; w < NW; ++w) c += __popcll(mask[e * NW + w]);
     cnt[e] = c;
@@ -630,7 +632,7 @@ __global__ __launch_bounds__(1024) void group_small_kernel(
   __syncthreads();
   if (tid < 64) scan_experts_wave(cnt, E, lane, offsets, mtile, einfo, rcp, p_offsets, off);
   __syncthreads();
-  for (int i = tid; i < T * k; i += 1024) {
+  for (int i = tid; i < T * k; i += NTH) {
     const int tt = i / k, e = sm_ids[i], tw = tt >> 6, tb = tt & 63;
     const uint64_t below = tb == 0 ? 0ull : (~0ull >> (64 - tb));
     int pos = off[e] + __popcll(mask[e * NW + tw] & below);
@@ -642,6 +644,67 @@ __global__ __launch_bounds__(1024) void group_small_kernel(
     if (p_sorted_tok) p_sorted_tok[pos] = tt;
     if (p_inv) p_inv[i] = pos;
   }
+}
+
+__global__ __launch_bounds__(1024) void group_small_kernel(
+    const int32_t *__restrict__ ids, const float *__restrict__ wts, const float *__restrict__ rowscale,
+    int T, int E, int k, int32_t *__restrict__ offsets, int32_t *__restrict__ mtile,
+    int4 *__restrict__ einfo, int32_t *__restrict__ rcp, int32_t *__restrict__ sorted_slots,
+    int4 *__restrict__ rowinfo,
+    int32_t *__restrict__ inv_pos, int32_t *__restrict__ p_offsets, int32_t *__restrict__ p_sorted_tok,
+    int32_t *__restrict__ p_inv) {
+  __shared__ int32_t sm_ids[kSmallRows];
+  group_small_body<1024>(ids, wts, rowscale, T, E, k, offsets, mtile, einfo, rcp, sorted_slots, rowinfo,
+                         inv_pos, p_offsets, p_sorted_tok, p_inv, sm_ids);
+}
+
+// ---------------------------------------------------------------------------
+// Decode batches of up to kFusedT tokens: routing and grouping in one
+// workgroup of 4 waves (one launch less on the latency-bound smallest steps).
+// Each wave takes 4 tokens as route_kernel does (top-k on 16 lanes per token,
+// and with rows of at most kRowRegsMaxH values the rows' powers of two); the
+// ids, weights and powers of two stay in LDS for the grouping, and are also
+// written out for the kernels after it.
+// ---------------------------------------------------------------------------
+template <int kPer, bool kBf16Logits>
+__global__ __launch_bounds__(256) void route_group_kernel(
+    const void *__restrict__ logits, const uint16_t *__restrict__ hidden, int T, int E, int H, int k,
+    int32_t *__restrict__ ids, float *__restrict__ wts, float *__restrict__ rowscale,
+    uint32_t *__restrict__ flags, int32_t *__restrict__ p_ids, float *__restrict__ p_w, int with_scales,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ mtile, int4 *__restrict__ einfo,
+    int32_t *__restrict__ rcp, int32_t *__restrict__ sorted_slots, int4 *__restrict__ rowinfo,
+    int32_t *__restrict__ inv_pos, int32_t *__restrict__ p_offsets, int32_t *__restrict__ p_sorted_tok,
+    int32_t *__restrict__ p_inv) {
+  __shared__ int32_t s_ids[kFusedT * 64];
+  __shared__ float s_wts[kFusedT * 64];
+  __shared__ float s_rs[kFusedT];
+  const int lane = threadIdx.x & 63, li = lane & 15;
+  const int t = threadIdx.x >> 4, t0 = (threadIdx.x >> 6) * 4;
+  if (threadIdx.x == 0) flags[0] = 0u;
+  if (t0 < T) {
+    uint64_t key[kPer];
+    if (t < T) topk16_keys<kPer, kBf16Logits>(logits, t, E, li, key);
+    if (with_scales) {
+      u4 v[4][4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          v[r][u] = t0 + r < T && lane * 8 + 512 * u < H
+                        ? *(const u4 *)(hidden + (size_t)(t0 + r) * H + lane * 8 + 512 * u)
+                        : u4{0u, 0u, 0u, 0u};
+      row_scale_regs(v, t0, T, H, lane, s_rs);
+    }
+    if (t < T) topk16_select<kPer>(key, t, k, li, s_ids, s_wts, p_ids, p_w);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < T * k; i += 256) {
+    ids[i] = s_ids[i];
+    wts[i] = s_wts[i];
+  }
+  if (with_scales && threadIdx.x < T) rowscale[threadIdx.x] = s_rs[threadIdx.x];
+  group_small_body<256>(s_ids, s_wts, with_scales ? s_rs : nullptr, T, E, k, offsets, mtile, einfo, rcp,
+                        sorted_slots, rowinfo, inv_pos, p_offsets, p_sorted_tok, p_inv, s_ids);
 }
 
 // ---------------------------------------------------------------------------
@@ -788,6 +851,20 @@ static hipError_t route_dispatch2(const LayerDims &L, const FwdPtrs &P, const Wo
               : route_dispatch<kPer, false, false>(L, P, W, stage_rows, s);
 }
 
+template <int kPer>
+static hipError_t route_group_dispatch(const LayerDims &L, const FwdPtrs &P, const Workspace &W,
+                                       int stage_rows, hipStream_t s) {
+  char *ws = P.ws;
+  auto k = P.logits_bf16 ? route_group_kernel<kPer, true> : route_group_kernel<kPer, false>;
+  hipLaunchKernelGGL(k, dim3(1), dim3(256), 0, s, P.logits, P.hidden, P.T, L.E, L.H, L.k,
+                     (int32_t *)(ws + W.topk_ids), (float *)(ws + W.topk_w), (float *)(ws + W.rowscale),
+                     P.flags, P.p_ids, P.p_w, stage_rows == 2 ? 1 : 0, (int32_t *)(ws + W.offsets),
+                     (int32_t *)(ws + W.mtile), (int4 *)(ws + W.active), (int32_t *)(ws + W.rcpre),
+                     (int32_t *)(ws + W.sorted_slots), (int4 *)(ws + W.rowinfo), (int32_t *)(ws + W.inv_pos),
+                     P.p_offsets, P.p_sorted_tok, P.p_inv);
+  return hipGetLastError();
+}
+
 template <int EG, bool kPerm>
 static hipError_t gate_route_launch(const LayerDims &L, const FwdPtrs &P, const Workspace &W,
                                     int stage_rows, hipStream_t s) {
@@ -838,14 +915,25 @@ hipError_t launch_route(const LayerDims &L, const FwdPtrs &P, const Workspace &W
     Q.gate_w = nullptr;
     return launch_route(L, Q, W, decode, s);
   }
+  if (route_groups(L, P, decode)) {
+    if (L.E <= 128) return route_group_dispatch<8>(L, P, W, stage_rows, s);
+    if (L.E <= 256) return route_group_dispatch<16>(L, P, W, stage_rows, s);
+    return route_group_dispatch<32>(L, P, W, stage_rows, s);
+  }
   if (L.E <= 128) return route_dispatch2<8>(L, P, W, stage_rows, s);
   if (L.E <= 256) return route_dispatch2<16>(L, P, W, stage_rows, s);
   return route_dispatch2<32>(L, P, W, stage_rows, s);
 }
 
+bool route_groups(const LayerDims &L, const FwdPtrs &P, bool decode) {
+  (void)L;
+  return decode && !P.w8a8 && P.act_g13 == 0.f && P.T <= kFusedT;
+}
+
 hipError_t launch_permute(const LayerDims &L, const FwdPtrs &P, const Workspace &W, bool decode,
                           hipStream_t s) {
   char *ws = P.ws;
+  if (route_groups(L, P, decode)) return hipSuccess;  // the routing kernel grouped the rows
   if (P.T <= kSmallT && P.T * L.k <= kSmallRows) {
     hipLaunchKernelGGL(group_small_kernel, dim3(1), dim3(1024), 0, s, (const int32_t *)(ws + W.topk_ids),
                        (const float *)(ws + W.topk_w), decode && L.H > kRowRegsMaxH ? (const float *)nullptr : (const float *)(ws + W.rowscale),
