@@ -306,6 +306,8 @@ mq_status moe_quant_forward_with_router(const mq_layer *L, const uint16_t *hidde
  * `workspace` saturated one of its FP16 intermediates (the SwiGLU output h or a
  * routing-weighted per-slot expert output; values beyond +-65504 are clamped):
  * MQ_OK if not, MQ_E_OVERFLOW if it did.  workspace as passed to forward.
+ * Batches of one or two tokens keep the per-slot outputs in FP32 (the down
+ * projection adds them into the output itself), so there only h can saturate.
  */
 mq_status moe_quant_check(const mq_layer *L, const void *workspace, struct ihipStream_t *stream);
 
