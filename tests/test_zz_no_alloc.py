@@ -37,9 +37,10 @@ def test_noalloc_matches_workspace_forward(fmt):
     g = GpuLayer(*random_layer(fmt, 41, E, H, I), K)
     lay = g.layer
     flag = torch.full((1,), 7, dtype=torch.int32, device="cuda")
-    # 1300 tokens (prefill path, ~63 MiB of scratch), then 64 and 5 (decode
-    # path) reusing the scratch the larger call left behind
-    for i, T in enumerate((1300, 64, 5)):
+    # 1300 tokens (prefill path, ~63 MiB of scratch), then 64, 5 and 2 (decode
+    # path; at 2 tokens the down projection writes the output itself) reusing
+    # the scratch the larger call left behind
+    for i, T in enumerate((1300, 64, 5, 2)):
         log(f"[noalloc] fmt={fmt} call {i}: T={T}")
         lg, x, res = _inputs(T, E, H, 50 + i)
         ref = lay.forward(lg, x, residual=res)
