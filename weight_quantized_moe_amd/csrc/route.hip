@@ -36,16 +36,11 @@ __device__ __forceinline__ uint32_t dpp(uint32_t v) {
 }
 constexpr int kXor1 = 0xB1, kXor2 = 0x4E, kHalfMirror = 0x141, kMirror = 0x140;
 
-template <int kCtrl>
-__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
-  return ((uint64_t)dpp<kCtrl>((uint32_t)(v >> 32)) << 32) | dpp<kCtrl>((uint32_t)v);
-}
-__device__ __forceinline__ uint64_t max16_u64(uint64_t v) {
-  uint64_t o;
-  o = dpp64<kXor1>(v); v = o > v ? o : v;
-  o = dpp64<kXor2>(v); v = o > v ? o : v;
-  o = dpp64<kHalfMirror>(v); v = o > v ? o : v;
-  o = dpp64<kMirror>(v); v = o > v ? o : v;
+__device__ __forceinline__ uint32_t max16_u32(uint32_t v) {
+  v = max(v, dpp<kXor1>(v));
+  v = max(v, dpp<kXor2>(v));
+  v = max(v, dpp<kHalfMirror>(v));
+  v = max(v, dpp<kMirror>(v));
   return v;
 }
 template <int kCtrl>
@@ -96,16 +91,29 @@ __device__ __forceinline__ void topk16_select(uint64_t *key, int t, int k, int l
   float sv[4] = {0.f, 0.f, 0.f, 0.f};  // slot j = li + 16 s held by this lane
   int si[4] = {0, 0, 0, 0};
   float vmax = 0.f;
-  for (int j = 0; j < k; ++j) {
-    uint64_t best = key[0];
+  // The 64-bit maximum taken as two 32-bit ones: the largest ordered logit,
+  // then the largest id half among the keys that hold it (32-bit max
+  // instructions, no 64-bit compare and select chains).
+  uint32_t hi[kPer], lo[kPer];
 #pragma unroll
-    for (int i = 1; i < kPer; ++i) best = key[i] > best ? key[i] : best;
-    best = max16_u64(best);
-    const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
-    const float v = from_ordered_key((uint32_t)(best >> 32));
+  for (int i = 0; i < kPer; ++i) {
+    hi[i] = (uint32_t)(key[i] >> 32);
+    lo[i] = (uint32_t)key[i];
+  }
+  for (int j = 0; j < k; ++j) {
+    uint32_t hm = hi[0];
+#pragma unroll
+    for (int i = 1; i < kPer; ++i) hm = max(hm, hi[i]);
+    hm = max16_u32(hm);
+    uint32_t lm = 0u;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) lm = max(lm, hi[i] == hm ? lo[i] : 0u);
+    lm = max16_u32(lm);
+    const int e = (int)(0xFFFFFFFFu - lm);
+    const float v = from_ordered_key(hm);
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
-      if (li + 16 * i == e) key[i] = 0;
+      if (li + 16 * i == e) hi[i] = lo[i] = 0u;
     if (j == 0) vmax = v;
     if ((j & 15) == li) {
 #pragma unroll
