@@ -8,8 +8,10 @@
 // mlp.gate); its logits arrive as an input.
 //
 // Top-k runs on a group of 16 lanes per token (4 tokens per wave): every lane
-// holds E/16 keys, and each of the k rounds is a local maximum plus a 4-step
-// DPP all-reduce inside the 16-lane row.
+// holds E/16 keys, and each of the k rounds finds the largest key as two
+// 32-bit maxima (the logit half, then the id half among the keys that hold
+// it), each a local maximum plus a 4-step DPP all-reduce inside the 16-lane
+// row.
 #include "device.h"
 #include "gate.h"
 #include "internal.h"
