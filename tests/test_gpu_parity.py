@@ -68,7 +68,8 @@ def test_dequantize_bit_exact(fmt):
 # ------------------------------------------------------------ routing
 
 @pytest.mark.parametrize("logit_kind", ["f32", "bf16_ties"])
-@pytest.mark.parametrize("T,E,k", [(1, 128, 8), (16, 128, 8), (16, 512, 64), (11, 200, 20), (17, 128, 8),
+@pytest.mark.parametrize("T,E,k", [(1, 128, 8), (2, 16, 16), (3, 512, 64), (4, 200, 20), (4, 40, 7),
+                                   (16, 128, 8), (16, 512, 64), (11, 200, 20), (17, 128, 8),
                                    (37, 128, 8), (64, 128, 8), (65, 128, 8),
                                    (128, 128, 8), (256, 128, 8), (130, 512, 31), (255, 16, 16),
                                    (200, 128, 32), (257, 128, 8),

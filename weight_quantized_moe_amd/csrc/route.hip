@@ -151,6 +151,73 @@ __device__ __forceinline__ void topk16(const void *__restrict__ logits, int t, i
   topk16_select<kPer>(key, t, k, li, ids, wts, p_ids, p_w);
 }
 
+// Top-k + softmax of token t on all 64 lanes of one wave (batches of at most
+// 4 tokens, one per wave; every lane of the wave active).  Lane l holds the
+// keys of experts l + 64 i; a round takes the same two 32-bit maxima as
+// topk16_select, each a DPP maximum inside the 16-lane rows followed by the
+// maximum of the four row results read with v_readlane (wave-uniform).
+__device__ __forceinline__ uint32_t max64_u32(uint32_t v) {
+  v = max16_u32(v);  // every lane of a row holds the row maximum
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return max(max(a, b), max(c, d));
+}
+__device__ __forceinline__ float sum64f(float v) {
+  v = sum16(v);
+  const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return ((a + b) + c) + d;
+}
+template <int kPer64, bool kBf16Logits>
+__device__ __forceinline__ void topk64(const void *__restrict__ logits, int t, int E, int k, int lane,
+                                       int32_t *__restrict__ ids, float *__restrict__ wts,
+                                       int32_t *__restrict__ p_ids, float *__restrict__ p_w) {
+  uint32_t hi[kPer64], lo[kPer64];
+#pragma unroll
+  for (int i = 0; i < kPer64; ++i) {
+    const int e = lane + 64 * i;
+    hi[i] = lo[i] = 0u;
+    if (e < E) {
+      const float v = kBf16Logits ? bf16_to_f32(((const uint16_t *)logits)[(size_t)t * E + e])
+                                  : ((const float *)logits)[(size_t)t * E + e];
+      hi[i] = ordered_key(v);
+      lo[i] = 0xFFFFFFFFu - (uint32_t)e;
+    }
+  }
+  float sv = 0.f, vmax = 0.f;  // lane j < k keeps slot j
+  int si = 0;
+  for (int j = 0; j < k; ++j) {
+    uint32_t hm = hi[0];
+#pragma unroll
+    for (int i = 1; i < kPer64; ++i) hm = max(hm, hi[i]);
+    hm = max64_u32(hm);
+    uint32_t lm = 0u;
+#pragma unroll
+    for (int i = 0; i < kPer64; ++i) lm = max(lm, hi[i] == hm ? lo[i] : 0u);
+    lm = max64_u32(lm);
+    const int e = (int)(0xFFFFFFFFu - lm);
+    const float v = from_ordered_key(hm);
+#pragma unroll
+    for (int i = 0; i < kPer64; ++i)
+      if (lane + 64 * i == e) hi[i] = lo[i] = 0u;
+    if (j == 0) vmax = v;
+    if (j == lane) { sv = v; si = e; }
+  }
+  const float p = lane < k ? expf(sv - vmax) : 0.f;
+  const float sum = sum64f(p);
+  if (lane < k) {
+    const float w = p / sum;
+    ids[(size_t)t * k + lane] = si;
+    wts[(size_t)t * k + lane] = w;
+    if (p_ids) p_ids[(size_t)t * k + lane] = si;
+    if (p_w) p_w[(size_t)t * k + lane] = w;
+  }
+}
+
 // Hidden rows of the wave's 4 tokens -> FP16 scaled by a power of two each,
 // using all 64 lanes per row.  With max|x| mapped into [2^14, 2^15), every BF16
 // value of the row above max * 2^-31 converts to FP16 exactly (BF16 has 8
@@ -672,9 +739,11 @@ __global__ __launch_bounds__(1024) void group_small_kernel(
 // Decode batches of up to kFusedT tokens: routing and grouping in one
 // workgroup of 4 waves (one launch less on the latency-bound smallest steps).
 // Each wave takes 4 tokens as route_kernel does (top-k on 16 lanes per token,
-// and with rows of at most kRowRegsMaxH values the rows' powers of two); the
-// ids, weights and powers of two stay in LDS for the grouping, and are also
-// written out for the kernels after it.
+// and with rows of at most kRowRegsMaxH values the rows' powers of two); with
+// at most 4 tokens each wave takes one token on all its lanes (topk64) and
+// wave 0 finds the rows' powers of two.  The ids, weights and powers of two
+// stay in LDS for the grouping, and are also written out for the kernels
+// after it.
 // ---------------------------------------------------------------------------
 template <int kPer, bool kBf16Logits>
 __global__ __launch_bounds__(256) void route_group_kernel(
@@ -691,7 +760,21 @@ __global__ __launch_bounds__(256) void route_group_kernel(
   const int lane = threadIdx.x & 63, li = lane & 15;
   const int t = threadIdx.x >> 4, t0 = (threadIdx.x >> 6) * 4;
   if (threadIdx.x == 0) flags[0] = 0u;
-  if (t0 < T) {
+  if (T <= 4) {
+    // one token per wave on all its lanes (wave 0 also finds the rows' powers of two)
+    const int wave = threadIdx.x >> 6;
+    if (wave == 0 && with_scales) {
+      u4 v[4][4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          v[r][u] = r < T && lane * 8 + 512 * u < H ? *(const u4 *)(hidden + (size_t)r * H + lane * 8 + 512 * u)
+                                                     : u4{0u, 0u, 0u, 0u};
+      row_scale_regs(v, 0, T, H, lane, s_rs);
+    }
+    if (wave < T) topk64<kPer / 4, kBf16Logits>(logits, wave, E, k, lane, s_ids, s_wts, p_ids, p_w);
+  } else if (t0 < T) {
     uint64_t key[kPer];
     if (t < T) topk16_keys<kPer, kBf16Logits>(logits, t, E, li, key);
     if (with_scales) {
